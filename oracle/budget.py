@@ -1,0 +1,53 @@
+"""Per-layer recompute budget (oracle; test infrastructure only).
+
+Follows "Dynamic-dLLM" reading notes, Key design 1 (DCU), the budget equation
+B^{t,l} = (B_layer * LayerNum) * s^{t+1,l} / sum_k s^{t+1,k}: the total budget T = B_layer * L is
+split across layers in proportion to the previous step's layer means (the page's step t+1 is the
+previous step because its step index counts down).
+
+The page gives a real-valued share. Readings (listed in the design doc):
+* integer budgets by floor plus largest remainder, ties to the lower layer, in IEEE fp64 with the
+  fixed operation order below, so that sum_l b_l == T exactly;
+* with no previous step, or when every previous mean is 0, each layer gets B_layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def layer_budget_row(s_prev: np.ndarray | None, L: int, b_layer: int) -> np.ndarray:
+    T = b_layer * L
+    if s_prev is None:
+        return np.full(L, b_layer, np.int32)
+    s = [float(np.float32(v)) for v in np.asarray(s_prev, np.float32).reshape(L)]
+    S = 0.0
+    for v in s:  # ascending layer order
+        S += v
+    if S == 0.0:
+        return np.full(L, b_layer, np.int32)
+    q = [(float(T) * v) / S for v in s]
+    f = [float(np.floor(x)) for x in q]
+    r = [q[i] - f[i] for i in range(L)]
+    b = [int(x) for x in f]
+    R = T - sum(b)
+    if R >= 0:
+        # the R largest remainders get +1; ties to the lower layer
+        order = sorted(range(L), key=lambda i: (-r[i], i))
+        for i in order[:R]:
+            b[i] += 1
+    else:
+        # only fp rounding can make the floors overshoot: take 1 from the -R smallest remainders
+        # among layers with a positive floor; ties to the higher layer
+        cand = [i for i in range(L) if b[i] > 0]
+        order = sorted(cand, key=lambda i: (r[i], -i))
+        for i in order[:-R]:
+            b[i] -= 1
+    return np.asarray(b, np.int32)
+
+
+def layer_budget(s_prev: np.ndarray | None, B: int, L: int, b_layer: int) -> np.ndarray:
+    """[B, L] fp32 previous-step means (or None) -> [B, L] int32 budgets, each row summing to b_layer*L."""
+    if s_prev is None:
+        return np.full((B, L), b_layer, np.int32)
+    s_prev = np.asarray(s_prev, np.float32).reshape(B, L)
+    return np.stack([layer_budget_row(s_prev[b], L, b_layer) for b in range(B)])
