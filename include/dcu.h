@@ -1,0 +1,197 @@
+/*
+ * dcu.h -- C ABI of the selective token cache library for MI355X (gfx950).
+ *
+ * The library implements, as hand-written HIP kernels, one denoising step of Dynamic Cache
+ * Updating (DCU) for masked-diffusion LLMs and the Frechet-profile commit rule that ends the step:
+ *
+ *   dcu_budget           per-layer recompute budgets from the previous step's layer means
+ *   dcu_distance         per-token cosine distance between a layer's input now and its cached input
+ *                        from the previous step, plus the per-group mean (layer dynamics)
+ *   dcu_select           per-sequence top-B selection by distance, united with forced windows
+ *   dcu_selective_layer  QKV / attention / output projection / SwiGLU FFN on the selected rows only,
+ *                        with K/V and output rows scattered back into caller-owned caches
+ *   dllm_confidence      per-position softmax confidence and argmax over the vocabulary
+ *   frechet_commit       sort, prefix sum and the Frechet margin rule -> how many positions commit
+ *
+ * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
+ * Acceleration of Diffusion LLM" (reading notes), Key designs 1-2; "Fast-dLLM++: Frechet Profile
+ * Decoding for Faster Diffusion LLM Inference" (reading notes), Key designs 1-3.
+ *
+ * Conventions (every entry point):
+ *  - Every pointer is a DEVICE pointer to caller-owned memory, row-major and contiguous, aligned
+ *    to 16 bytes, unless stated otherwise. bf16 tensors are raw 16-bit patterns.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work and return;
+ *    outputs are valid once the stream reaches that point; inputs must stay alive until then.
+ *  - The library never allocates device memory, keeps no pointer past a call and has no mutable
+ *    global state: calls are reentrant and thread-safe. Outputs must not alias inputs except for
+ *    the documented in/out buffers.
+ *  - All argument checks happen on the host before any launch: a non-zero status means nothing
+ *    was enqueued, except DCU_EHIP, which reports a failed launch.
+ *  - NaN or Inf inputs are a caller error; the results are then unspecified.
+ */
+#ifndef DCU_H
+#define DCU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DCU_OK = 0,
+  DCU_EINVAL = 1,       /* null pointer, non-positive size, value out of range            */
+  DCU_EUNSUPPORTED = 2, /* a valid request outside what the kernels implement (see below) */
+  DCU_EWORKSPACE = 3,   /* workspace missing or smaller than the *_workspace query says   */
+  DCU_EHIP = 4          /* a kernel launch failed (hipGetLastError has the detail)        */
+};
+
+enum { DCU_F32 = 0, DCU_BF16 = 1 };
+
+/* Text for a status code (static storage; never NULL). */
+const char* dcu_status_string(int status);
+/* Library version, major*10000 + minor*100 + patch. */
+int dcu_version(void);
+
+/*
+ * dcu_budget -- per-layer budgets of one step.
+ * Dynamic-dLLM notes, Key design 1 (DCU), budget equation: the total T = b_layer * L of each
+ * sequence is split across the L layers in proportion to the previous step's layer means.
+ *
+ * s_prev  [B, L] fp32 layer means of the previous step, or NULL for "no previous step".
+ * budget  [B, L] int32 out. Each row sums to exactly T: floor of T*s/sum(s) plus one for the
+ *         largest remainders (ties to the lower layer), computed in IEEE fp64 in a fixed order.
+ *         A NULL s_prev, or a row whose means sum to 0, gives b_layer to every layer.
+ * Errors: EINVAL if budget is NULL, B <= 0, L <= 0, b_layer < 0 or b_layer*L overflows int32;
+ *         EUNSUPPORTED if L > 1024.
+ */
+int dcu_budget(const float* s_prev, int32_t B, int32_t L, int32_t b_layer, int32_t* budget,
+               void* stream);
+
+/*
+ * dcu_distance -- token cosine distance and group mean.
+ * Dynamic-dLLM notes, Key design 1 (DCU): d_i = 1 - <x_i^t, x_i^{t+1}> / (|x_i^t| |x_i^{t+1}|)
+ * between a token's layer input now (x_cur) and at the previous step (x_prev); the layer dynamics
+ * s = (1/N) sum_i d_i.
+ *
+ * x_cur, x_prev  [G, N, d] of dtype DCU_BF16 or DCU_F32 (G groups, e.g. sequences or layers).
+ * dist           [G, N] fp32 out. Accumulated in fp64; bitwise-identical rows give exactly 0,
+ *                two zero rows give 0, exactly one zero row gives 1; clamped to [0, 2].
+ * mean           [G] fp32 out, or NULL: (sum over the fp32 dist of the group, in fp64) / N.
+ * Errors: EINVAL on NULL x_cur/x_prev/dist or G, N, d <= 0 or a bad dtype;
+ *         EUNSUPPORTED if d is not a multiple of 8 (bf16) or 4 (fp32), or a pointer is not
+ *         16-byte aligned.
+ */
+int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype, int64_t G, int64_t N,
+                 int64_t d, float* dist, float* mean, void* stream);
+
+/*
+ * dcu_select -- recompute set of one layer for each sequence.
+ * Dynamic-dLLM notes, Key design 1 (top-B tokens by distance are recomputed, the rest reuse their
+ * cached values) and Key design 2 (forced update window around each key token unmasked at the
+ * previous step; the remaining budget is spent outside the window).
+ *
+ * dist      [B, N] fp32 distances of this layer (from dcu_distance).
+ * budgets   [B, L] int32; column `layer` is this layer's budget b (negative values count as 0).
+ * key_pos   [B, P] int32 positions unmasked at the previous step; values outside [0, N) are
+ *           ignored (-1 = unused). May be NULL when P == 0.
+ * b_window  window size: positions [p - b_window/2, p - b_window/2 + b_window - 1] clipped to
+ *           [0, N) are always selected (b_window/2 rounds down).
+ * sel_idx   [B, N] int32 out: ascending positions W u A, where A is the top-min(b, |C|) of the
+ *           candidates C = {i not in W : dist_i > 0} ranked by (dist desc, position asc).
+ *           Entries past sel_count[b] are set to -1.
+ * sel_count [B] int32 out.
+ * Errors: EINVAL on NULL pointers, B, N, L <= 0, P < 0, b_window < 0, layer outside [0, L);
+ *         EUNSUPPORTED if N > 8192.
+ */
+int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t layer,
+               const int32_t* key_pos, int32_t P, int32_t B, int32_t N, int32_t b_window,
+               int32_t* sel_idx, int32_t* sel_count, void* stream);
+
+/*
+ * One pre-norm transformer layer (bf16 weights, [out, in] row-major):
+ *   xn = RMSNorm(x; g_attn), [q|k|v] = xn W_qkv^T, o = softmax(q K^T / sqrt(head_dim)) V per head
+ *   over all N cached rows (no mask), a = x + o W_o^T, an = RMSNorm(a; g_ffn),
+ *   y = a + (silu(an W_gate^T) * (an W_up^T)) W_down^T.
+ */
+typedef struct {
+  int32_t d;          /* model width, = n_heads * head_dim          */
+  int32_t n_heads;
+  int32_t head_dim;   /* 64 or 128                                    */
+  int32_t ffn;        /* FFN width F                                  */
+  float rms_eps;
+  const void* w_qkv;  /* bf16 [3d, d]: rows Wq | Wk | Wv              */
+  const void* w_o;    /* bf16 [d, d]                                  */
+  const void* w_gate; /* bf16 [F, d]                                  */
+  const void* w_up;   /* bf16 [F, d]                                  */
+  const void* w_down; /* bf16 [d, F]                                  */
+  const void* g_attn; /* bf16 [d] RMSNorm gain before attention       */
+  const void* g_ffn;  /* bf16 [d] RMSNorm gain before the FFN         */
+} dcu_layer;
+
+/* Workspace bytes dcu_selective_layer needs for these shapes (max_rows <= 0 means B*N). */
+size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, int32_t max_rows);
+
+/*
+ * dcu_selective_layer -- recompute the selected rows of one layer.
+ * Dynamic-dLLM notes, Key design 1 (DCU): only the selected tokens are recomputed; every other
+ * token keeps its cached K, V and output. Attention is bidirectional over all cached rows.
+ *
+ * x_in      [B, N, d] bf16 layer input (only selected rows are read).
+ * sel_idx   [B, N] int32 ascending positions and sel_count [B] int32 (from dcu_select), or both
+ *           NULL for every row (dense mode).
+ * max_rows  host-side upper bound on sum(sel_count) used to size the workspace (<= 0: B*N).
+ *           If the device counts exceed it, only the first max_rows rows in (sequence, position)
+ *           order are recomputed.
+ * k_cache, v_cache  [B, N, n_heads, head_dim] bf16 IN/OUT: selected rows are overwritten before
+ *           attention reads the cache; other rows are untouched.
+ * y_out     [B, N, d] bf16 IN/OUT: selected rows get the layer output; other rows are untouched.
+ * workspace device scratch of at least dcu_selective_layer_workspace() bytes (256-byte aligned).
+ * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
+ *         d != n_heads*head_dim; EUNSUPPORTED if head_dim not in {64, 128}, d or ffn not a
+ *         multiple of 256, or N > 65536; EWORKSPACE if the workspace is too small.
+ */
+int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
+                        const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
+                        void* k_cache, void* v_cache, void* y_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * dllm_confidence -- confidence and argmax of each candidate position.
+ * Fast-dLLM++ notes, Key designs (overall framework): each masked position takes the argmax of its
+ * predicted distribution and that argmax's probability as its confidence c_i.
+ *
+ * logits  [R, ld] of dtype DCU_BF16 or DCU_F32; the first V columns of each row are used.
+ * conf    [R] fp32 out: 1 / sum_v exp(z_v - max z) (temperature 1; fp64 row accumulation).
+ * token   [R] int32 out: the lowest index attaining max z.
+ * Errors: EINVAL on NULL pointers, R <= 0, V <= 0, ld < V, bad dtype; EUNSUPPORTED if ld is not
+ *         a multiple of 8 (bf16) or 4 (fp32), or V > 2^31 - 1.
+ */
+int dllm_confidence(const void* logits, int32_t dtype, int64_t R, int64_t V, int64_t ld,
+                    float* conf, int32_t* token, void* stream);
+
+/*
+ * frechet_commit -- how many candidates commit this step.
+ * Fast-dLLM++ notes, Key design 1 (Theorem 4.1: L_n = max{0, sum_{j<=n} c_(j) - (n-1)},
+ * U_n = 1 - c_(n)) and Key design 2 (n* = max{n : L_n - U_n > delta}, else 1).
+ *
+ * conf      [B, m] fp32 confidences; only the first m_valid[b] slots of row b are candidates.
+ * m_valid   [B] int32 (values clamped to [0, m]), or NULL for m everywhere.
+ * delta     margin, >= 0.
+ * n_commit  [B] int32 out: n* (0 when a row has no candidates).
+ * order     [B, m] int32 out: candidate slots sorted by (conf desc, slot asc); the first
+ *           n_commit[b] commit; entries past m_valid[b] are -1.
+ * Prefix sums are fp64 and exact whenever every c is 0 or in [2^-17, 1] (always true for
+ * dllm_confidence outputs); otherwise they are taken sequentially in sorted order.
+ * Errors: EINVAL on NULL conf/n_commit/order, B <= 0, m <= 0, delta < 0 or NaN;
+ *         EUNSUPPORTED if m > 8192.
+ */
+int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m, double delta,
+                   int32_t* n_commit, int32_t* order, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCU_H */

@@ -1,0 +1,245 @@
+"""ctypes binding of libdcu.so: argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks shape / dtype / layout,
+passes raw device pointers and the current HIP stream to the C ABI, and raises DcuError on a
+non-zero status. No step of the computation happens here. If the library has not been built the
+first call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcu.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class DcuError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+
+
+class LayerDesc(ctypes.Structure):
+    """Mirror of dcu_layer in include/dcu.h."""
+    _fields_ = [("d", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn", _i32),
+                ("rms_eps", ctypes.c_float), ("w_qkv", _vp), ("w_o", _vp), ("w_gate", _vp),
+                ("w_up", _vp), ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp)]
+
+
+_lib = None
+
+EXPORTS = {
+    "dcu_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dcu_version": (ctypes.c_int, []),
+    "dcu_budget": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "dcu_distance": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "dcu_select": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                  _vp]),
+    "dcu_selective_layer_workspace": (ctypes.c_size_t,
+                                      [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
+    "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
+                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "dllm_confidence": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
+}
+
+
+def lib_path() -> str:
+    return _PATH
+
+
+def load():
+    """Load libdcu.so (torch is imported first so that one HIP runtime serves both)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_PATH):
+        raise RuntimeError(f"{_PATH} is not built; run `python -m selective_token_cache_amd.build`")
+    L = ctypes.CDLL(_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load().dcu_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load().dcu_version()
+
+
+# ----------------------------------------------------------------------------- helpers
+def _p(t: torch.Tensor | None):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return _vp(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise DcuError(fn, status)
+
+
+# ----------------------------------------------------------------------------- entry points
+def dcu_budget(s_prev: torch.Tensor | None, B: int, L: int, b_layer: int, out=None, stream=None):
+    if s_prev is not None:
+        _need(s_prev, "s_prev", torch.float32, (B, L))
+        dev = s_prev.device
+    else:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    out = torch.empty((B, L), dtype=torch.int32, device=dev) if out is None else out
+    _need(out, "budget", torch.int32, (B, L))
+    _check("dcu_budget", load().dcu_budget(_p(s_prev), B, L, b_layer, _p(out), _stream(stream)))
+    return out
+
+
+def dcu_distance(x_cur: torch.Tensor, x_prev: torch.Tensor, dist=None, mean=None, want_mean=True,
+                 stream=None):
+    """x_cur, x_prev [G, N, d] (bf16 or fp32) -> dist [G, N] fp32, mean [G] fp32 (or None)."""
+    _need(x_cur, "x_cur")
+    _need(x_prev, "x_prev", x_cur.dtype, x_cur.shape)
+    if x_cur.dim() != 3 or x_cur.dtype not in _DT:
+        raise ValueError("x_cur must be [G, N, d] bf16 or fp32")
+    G, N, d = x_cur.shape
+    dist = torch.empty((G, N), dtype=torch.float32, device=x_cur.device) if dist is None else dist
+    _need(dist, "dist", torch.float32, (G, N))
+    if want_mean and mean is None:
+        mean = torch.empty((G,), dtype=torch.float32, device=x_cur.device)
+    if mean is not None:
+        _need(mean, "mean", torch.float32, (G,))
+    st = load().dcu_distance(_p(x_cur), _p(x_prev), _DT[x_cur.dtype], G, N, d, _p(dist), _p(mean),
+                             _stream(stream))
+    _check("dcu_distance", st)
+    return dist, mean
+
+
+def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: torch.Tensor | None,
+               b_window: int, sel_idx=None, sel_count=None, stream=None):
+    """dist [B, N] fp32, budgets [B, L] int32, key_pos [B, P] int32 -> (sel_idx [B, N], sel_count [B])."""
+    _need(dist, "dist", torch.float32)
+    B, N = dist.shape
+    _need(budgets, "budgets", torch.int32)
+    if budgets.dim() != 2 or budgets.shape[0] != B:
+        raise ValueError("budgets must be [B, L]")
+    L = budgets.shape[1]
+    P = 0
+    if key_pos is not None:
+        _need(key_pos, "key_pos", torch.int32)
+        if key_pos.dim() != 2 or key_pos.shape[0] != B:
+            raise ValueError("key_pos must be [B, P]")
+        P = key_pos.shape[1]
+    sel_idx = torch.empty((B, N), dtype=torch.int32, device=dist.device) if sel_idx is None else sel_idx
+    sel_count = torch.empty((B,), dtype=torch.int32, device=dist.device) if sel_count is None else sel_count
+    _need(sel_idx, "sel_idx", torch.int32, (B, N))
+    _need(sel_count, "sel_count", torch.int32, (B,))
+    st = load().dcu_select(_p(dist), _p(budgets), L, layer, _p(key_pos) if P else None, P, B, N,
+                           b_window, _p(sel_idx), _p(sel_count), _stream(stream))
+    _check("dcu_select", st)
+    return sel_idx, sel_count
+
+
+class Layer:
+    """Holds the device weights of one layer and the matching dcu_layer descriptor."""
+
+    def __init__(self, d, n_heads, head_dim, ffn, eps, w_qkv, w_o, w_gate, w_up, w_down, g_attn,
+                 g_ffn):
+        for name, t, shape in [("w_qkv", w_qkv, (3 * d, d)), ("w_o", w_o, (d, d)),
+                               ("w_gate", w_gate, (ffn, d)), ("w_up", w_up, (ffn, d)),
+                               ("w_down", w_down, (d, ffn)), ("g_attn", g_attn, (d,)),
+                               ("g_ffn", g_ffn, (d,))]:
+            _need(t, name, torch.bfloat16, shape)
+        self.tensors = (w_qkv, w_o, w_gate, w_up, w_down, g_attn, g_ffn)
+        self.d, self.n_heads, self.head_dim, self.ffn, self.eps = d, n_heads, head_dim, ffn, eps
+        self.desc = LayerDesc(d, n_heads, head_dim, ffn, float(eps), *[_p(t) for t in self.tensors])
+
+    def workspace_bytes(self, B: int, N: int, max_rows: int = 0) -> int:
+        return int(load().dcu_selective_layer_workspace(ctypes.byref(self.desc), B, N, max_rows))
+
+
+def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_cache, v_cache,
+                        y_out, max_rows: int = 0, workspace: torch.Tensor | None = None,
+                        stream=None):
+    """Recompute the selected rows in place (k_cache, v_cache, y_out are in/out)."""
+    _need(x_in, "x_in", torch.bfloat16)
+    B, N, d = x_in.shape
+    if d != layer.d:
+        raise ValueError("x_in width does not match the layer")
+    _need(k_cache, "k_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    _need(y_out, "y_out", torch.bfloat16, (B, N, d))
+    if (sel_idx is None) != (sel_count is None):
+        raise ValueError("sel_idx and sel_count go together")
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32, (B, N))
+        _need(sel_count, "sel_count", torch.int32, (B,))
+    need = layer.workspace_bytes(B, N, max_rows)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+    _need(workspace, "workspace", torch.uint8)
+    st = load().dcu_selective_layer(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx), _p(sel_count),
+                                    B, N, max_rows, _p(k_cache), _p(v_cache), _p(y_out),
+                                    _p(workspace), workspace.numel(), _stream(stream))
+    _check("dcu_selective_layer", st)
+    return k_cache, v_cache, y_out
+
+
+def dllm_confidence(logits: torch.Tensor, V: int | None = None, conf=None, token=None, stream=None):
+    """logits [R, ld] (bf16 or fp32) -> conf [R] fp32, token [R] int32 over the first V columns."""
+    _need(logits, "logits")
+    if logits.dim() != 2 or logits.dtype not in _DT:
+        raise ValueError("logits must be [R, ld] bf16 or fp32")
+    R, ld = logits.shape
+    V = ld if V is None else V
+    conf = torch.empty((R,), dtype=torch.float32, device=logits.device) if conf is None else conf
+    token = torch.empty((R,), dtype=torch.int32, device=logits.device) if token is None else token
+    _need(conf, "conf", torch.float32, (R,))
+    _need(token, "token", torch.int32, (R,))
+    st = load().dllm_confidence(_p(logits), _DT[logits.dtype], R, V, ld, _p(conf), _p(token),
+                                _stream(stream))
+    _check("dllm_confidence", st)
+    return conf, token
+
+
+def frechet_commit(conf: torch.Tensor, delta: float, m_valid: torch.Tensor | None = None,
+                   n_commit=None, order=None, stream=None):
+    """conf [B, m] fp32 -> n_commit [B] int32, order [B, m] int32."""
+    _need(conf, "conf", torch.float32)
+    B, m = conf.shape
+    if m_valid is not None:
+        _need(m_valid, "m_valid", torch.int32, (B,))
+    n_commit = torch.empty((B,), dtype=torch.int32, device=conf.device) if n_commit is None else n_commit
+    order = torch.empty((B, m), dtype=torch.int32, device=conf.device) if order is None else order
+    _need(n_commit, "n_commit", torch.int32, (B,))
+    _need(order, "order", torch.int32, (B, m))
+    st = load().frechet_commit(_p(conf), _p(m_valid), B, m, float(delta), _p(n_commit), _p(order),
+                               _stream(stream))
+    _check("frechet_commit", st)
+    return n_commit, order

@@ -1,0 +1,110 @@
+// Shared device helpers for the gfx950 kernels (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcu.h"
+
+namespace dcu {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf_to_f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// round to nearest even; inputs are finite
+__device__ __forceinline__ uint32_t f_to_bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f_to_bf_bits(lo) | (f_to_bf_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------- streaming loads
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (data read once; keep it from displacing reused lines)
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------- wave reductions
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    T o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// inclusive prefix sum across the wave (lane order)
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// exclusive prefix sum over a whole workgroup (blockDim.x a multiple of 64, <= 1024).
+// `lds` must hold 17 ints. Returns the exclusive prefix; *total gets the block sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) lds[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      int t = lds[i];
+      lds[i] = run;
+      run += t;
+    }
+    lds[16] = run;
+  }
+  __syncthreads();
+  int res = lds[wid] + inc - v;
+  *total = lds[16];
+  __syncthreads();
+  return res;
+}
+
+// block-wide sum of ints (order-free, exact)
+__device__ __forceinline__ int block_sum_int(int v, int* lds) {
+  int total;
+  (void)block_excl_scan(v, lds, &total);
+  return total;
+}
+
+}  // namespace dcu
+
+// ------------------------------------------------------------------------------ host helpers
+#define DCU_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return DCU_EHIP;    \
+  } while (0)
+
+static inline bool dcu_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

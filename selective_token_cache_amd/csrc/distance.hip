@@ -1,0 +1,156 @@
+// dcu_distance: per-token cosine distance between a layer's input now and its cached input of the
+// previous step, and the per-group mean of those distances.
+// Dynamic-dLLM reading notes, Key design 1 (DCU): the d_i^{t,l} equation and the layer dynamics
+// s^{t,l} = (1/N) sum_i d_i^{t,l}.
+//
+// Design (HBM-bound: both rows must be read once, 4*d bytes per bf16 row pair):
+//  * one wave64 per row pair, 4 rows per 256-thread workgroup; each lane streams 16-byte chunks of
+//    both rows with 8 chunks in flight per operand;
+//  * the dot product and both squared norms accumulate in fp64 (bf16*bf16 products are exact, so
+//    the only rounding is in the fp64 sums); the distance 1 - cos is formed in fp64 and rounded
+//    once to fp32. An fp32 one-pass form would lose the ~1e-5 distances to cancellation;
+//  * a bitwise OR of (a XOR b) flags identical rows, which give exactly 0;
+//  * the group mean is a second, tiny kernel: one workgroup per group sums the fp32 distances in
+//    fp64 in a fixed order (deterministic, no atomics, no workspace).
+#include "common.h"
+
+namespace dcu {
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr int kUnroll = 8;
+
+struct Acc {
+  double dot0 = 0.0, dot1 = 0.0, na0 = 0.0, na1 = 0.0, nb0 = 0.0, nb1 = 0.0;
+  uint32_t diff = 0u;
+};
+
+__device__ __forceinline__ void acc_bf16_word(Acc& s, uint32_t wa, uint32_t wb) {
+  s.diff |= wa ^ wb;
+  const double a0 = bf_lo(wa), a1 = bf_hi(wa);
+  const double b0 = bf_lo(wb), b1 = bf_hi(wb);
+  s.dot0 = fma(a0, b0, s.dot0);
+  s.dot1 = fma(a1, b1, s.dot1);
+  s.na0 = fma(a0, a0, s.na0);
+  s.na1 = fma(a1, a1, s.na1);
+  s.nb0 = fma(b0, b0, s.nb0);
+  s.nb1 = fma(b1, b1, s.nb1);
+}
+
+__device__ __forceinline__ void acc_f32_pair(Acc& s, uint32_t wa0, uint32_t wa1, uint32_t wb0,
+                                             uint32_t wb1) {
+  s.diff |= (wa0 ^ wb0) | (wa1 ^ wb1);
+  const double a0 = __uint_as_float(wa0), a1 = __uint_as_float(wa1);
+  const double b0 = __uint_as_float(wb0), b1 = __uint_as_float(wb1);
+  s.dot0 = fma(a0, b0, s.dot0);
+  s.dot1 = fma(a1, b1, s.dot1);
+  s.na0 = fma(a0, a0, s.na0);
+  s.na1 = fma(a1, a1, s.na1);
+  s.nb0 = fma(b0, b0, s.nb0);
+  s.nb1 = fma(b1, b1, s.nb1);
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void k_distance(const uint4* __restrict__ xc,
+                                                  const uint4* __restrict__ xp, int64_t rows,
+                                                  int chunks, float* __restrict__ dist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= rows) return;
+  const uint4* a = xc + row * chunks;
+  const uint4* b = xp + row * chunks;
+  Acc s;
+  for (int base = 0; base < chunks; base += kWave * kUnroll) {
+    uint4 ra[kUnroll], rb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = base + u * kWave + lane;
+      if (c < chunks) {
+        ra[u] = load_nt(a + c);
+        rb[u] = load_nt(b + c);
+      } else {
+        ra[u] = make_uint4(0, 0, 0, 0);
+        rb[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (kBf16) {
+        acc_bf16_word(s, ra[u].x, rb[u].x);
+        acc_bf16_word(s, ra[u].y, rb[u].y);
+        acc_bf16_word(s, ra[u].z, rb[u].z);
+        acc_bf16_word(s, ra[u].w, rb[u].w);
+      } else {
+        acc_f32_pair(s, ra[u].x, ra[u].y, rb[u].x, rb[u].y);
+        acc_f32_pair(s, ra[u].z, ra[u].w, rb[u].z, rb[u].w);
+      }
+    }
+  }
+  double dot = wave_sum(s.dot0 + s.dot1);
+  double na = wave_sum(s.na0 + s.na1);
+  double nb = wave_sum(s.nb0 + s.nb1);
+  uint32_t diff = wave_or(s.diff);
+  if (lane == 0) {
+    double d;
+    if (diff == 0u) {
+      d = 0.0;
+    } else if (na == 0.0 && nb == 0.0) {
+      d = 0.0;
+    } else if (na == 0.0 || nb == 0.0) {
+      d = 1.0;
+    } else {
+      d = 1.0 - dot / sqrt(na * nb);
+      d = d < 0.0 ? 0.0 : (d > 2.0 ? 2.0 : d);
+    }
+    dist[row] = float(d);
+  }
+}
+
+// one workgroup per group; fixed per-thread strides and a fixed reduction tree
+__global__ __launch_bounds__(256) void k_group_mean(const float* __restrict__ dist, int64_t N,
+                                                    float* __restrict__ mean) {
+  __shared__ double part[4];
+  const float* p = dist + int64_t(blockIdx.x) * N;
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < N; i += blockDim.x) acc += double(p[i]);
+  acc = wave_sum(acc);
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = (part[0] + part[1]) + (part[2] + part[3]);
+    mean[blockIdx.x] = float(tot / double(N));
+  }
+}
+
+}  // namespace
+}  // namespace dcu
+
+extern "C" int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype, int64_t G,
+                            int64_t N, int64_t d, float* dist, float* mean, void* stream) {
+  if (!x_cur || !x_prev || !dist || G <= 0 || N <= 0 || d <= 0) return DCU_EINVAL;
+  if (dtype != DCU_BF16 && dtype != DCU_F32) return DCU_EINVAL;
+  const int64_t per_chunk = dtype == DCU_BF16 ? 8 : 4;
+  if (d % per_chunk != 0) return DCU_EUNSUPPORTED;
+  if (!dcu_aligned16(x_cur) || !dcu_aligned16(x_prev)) return DCU_EUNSUPPORTED;
+  if (G > (int64_t(1) << 31) - 1) return DCU_EUNSUPPORTED;
+  const int64_t chunks = d / per_chunk;
+  if (chunks > (int64_t(1) << 30)) return DCU_EUNSUPPORTED;
+  const int64_t rows = G * N;
+  const int64_t blocks = (rows + dcu::kRowsPerBlock - 1) / dcu::kRowsPerBlock;
+  if (blocks > (int64_t(1) << 31) - 1) return DCU_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint4* a = static_cast<const uint4*>(x_cur);
+  const uint4* b = static_cast<const uint4*>(x_prev);
+  if (dtype == DCU_BF16)
+    hipLaunchKernelGGL(dcu::k_distance<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a, b, rows,
+                       int(chunks), dist);
+  else
+    hipLaunchKernelGGL(dcu::k_distance<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a, b, rows,
+                       int(chunks), dist);
+  DCU_LAUNCH_CHECK();
+  if (mean) {
+    hipLaunchKernelGGL(dcu::k_group_mean, dim3(unsigned(G)), dim3(256), 0, s, dist, N, mean);
+    DCU_LAUNCH_CHECK();
+  }
+  return DCU_OK;
+}

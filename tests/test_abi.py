@@ -1,0 +1,96 @@
+"""The C ABI library loads, exports every function include/dcu.h declares, and rejects invalid
+arguments on the host before any launch (these calls never reach a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_token_cache_amd as stc
+from selective_token_cache_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcu.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.lib_path()),
+                                reason="libdcu.so not built (run the build first)")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) -
+                  {"if", "sizeof", "defined", "extern"})
+
+
+def test_every_declared_function_is_exported():
+    names = _declared()
+    assert {"dcu_distance", "dcu_budget", "dcu_select", "dcu_selective_layer", "dllm_confidence",
+            "frechet_commit"} <= set(names)
+    L = ctypes.CDLL(_lib.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(_lib.EXPORTS) == set(names)
+
+
+def test_status_strings_and_version():
+    assert stc.status_string(0) == "ok"
+    assert "invalid" in stc.status_string(1)
+    assert stc.status_string(99) == "unknown status"
+    assert stc.version() >= 100
+
+
+FAKE = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+
+
+def test_budget_validation():
+    L = stc.load()
+    assert L.dcu_budget(None, 2, 4, 8, None, None) == _lib.EINVAL           # budget NULL
+    assert L.dcu_budget(None, 0, 4, 8, FAKE, None) == _lib.EINVAL           # B <= 0
+    assert L.dcu_budget(None, 2, 0, 8, FAKE, None) == _lib.EINVAL           # L <= 0
+    assert L.dcu_budget(None, 2, 4, -1, FAKE, None) == _lib.EINVAL          # b_layer < 0
+    assert L.dcu_budget(None, 2, 4, 2**30, FAKE, None) == _lib.EINVAL       # T overflows
+    assert L.dcu_budget(None, 2, 2000, 1, FAKE, None) == _lib.EUNSUPPORTED  # L > 1024
+
+
+def test_distance_validation():
+    L = stc.load()
+    assert L.dcu_distance(None, FAKE, 1, 1, 1, 8, FAKE, None, None) == _lib.EINVAL
+    assert L.dcu_distance(FAKE, FAKE, 1, 0, 1, 8, FAKE, None, None) == _lib.EINVAL
+    assert L.dcu_distance(FAKE, FAKE, 7, 1, 1, 8, FAKE, None, None) == _lib.EINVAL
+    assert L.dcu_distance(FAKE, FAKE, 1, 1, 1, 12, FAKE, None, None) == _lib.EUNSUPPORTED
+    assert L.dcu_distance(FAKE, FAKE, 0, 1, 1, 6, FAKE, None, None) == _lib.EUNSUPPORTED
+    odd = ctypes.c_void_p(256 + 4)
+    assert L.dcu_distance(odd, FAKE, 1, 1, 1, 8, FAKE, None, None) == _lib.EUNSUPPORTED
+
+
+def test_select_validation():
+    L = stc.load()
+    args = dict(dist=FAKE, budgets=FAKE, L=4, layer=0, key_pos=FAKE, P=1, B=2, N=64, bw=8,
+                sel=FAKE, cnt=FAKE)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dcu_select(a["dist"], a["budgets"], a["L"], a["layer"], a["key_pos"], a["P"],
+                            a["B"], a["N"], a["bw"], a["sel"], a["cnt"], None)
+
+    assert call(layer=4) == _lib.EINVAL
+    assert call(layer=-1) == _lib.EINVAL
+    assert call(bw=-1) == _lib.EINVAL
+    assert call(P=-1) == _lib.EINVAL
+    assert call(key_pos=None) == _lib.EINVAL
+    assert call(sel=None) == _lib.EINVAL
+    assert call(N=0) == _lib.EINVAL
+    assert call(N=8193) == _lib.EUNSUPPORTED
+
+
+def test_confidence_and_commit_validation():
+    L = stc.load()
+    assert L.dllm_confidence(FAKE, 1, 4, 10, 8, FAKE, FAKE, None) == _lib.EINVAL      # ld < V
+    assert L.dllm_confidence(FAKE, 1, 0, 8, 8, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_confidence(FAKE, 3, 4, 8, 8, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_confidence(FAKE, 1, 4, 10, 12, FAKE, FAKE, None) == _lib.EUNSUPPORTED
+    assert L.frechet_commit(FAKE, None, 2, 16, -0.1, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.frechet_commit(FAKE, None, 2, 16, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
+    assert L.frechet_commit(FAKE, None, 0, 16, 0.1, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.frechet_commit(FAKE, None, 2, 8193, 0.1, FAKE, FAKE, None) == _lib.EUNSUPPORTED

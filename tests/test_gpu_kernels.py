@@ -1,0 +1,280 @@
+"""GPU parity of the distance, budget, select, confidence and commit kernels against the oracle.
+
+Bars: distance, mean and confidence within 1e-5 relative (exact 0 where the oracle gives 0);
+budgets, selections, tokens, commit counts and sort orders bit-exact given the same inputs;
+every kernel bitwise deterministic across two runs."""
+import numpy as np
+import pytest
+import torch
+
+import selective_token_cache_amd as stc
+from oracle import budget as obud
+from oracle import confidence as oconf
+from oracle import distance as odist
+from oracle import frechet as ofre
+from oracle import select as osel
+from tests.util import assert_rel, dev, dev_bf16
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------- distance
+@pytest.mark.parametrize("G,N,d,frac,sigma", [(3, 37, 8, 0.5, 0.1), (2, 100, 72, 0.3, 0.01),
+                                              (1, 1, 4096, 1.0, 0.01), (5, 64, 640, 0.25, 0.2)])
+def test_distance_bf16_small(G, N, d, frac, sigma):
+    _log(f"distance bf16 G={G} N={N} d={d}")
+    g = synth.rng(900, G, N, d)
+    cur = np.empty((G, N, d), np.uint16)
+    prev = np.empty_like(cur)
+    for k in range(G):
+        cur[k], prev[k], _ = synth.drift_pair(g, N, d, int(round(frac * N)), sigma)
+    dist, mean = stc.dcu_distance(dev_bf16(cur), dev_bf16(prev))
+    rd, rm = odist.distance_and_mean(cur, prev)
+    assert_rel(dist.cpu().numpy(), rd)
+    assert_rel(mean.cpu().numpy(), rm)
+
+
+def test_distance_full_size_32_layers():
+    """32 layers x N=1024 x d=4096 bf16, 30% of rows drifted by sigma_l = 0.01 (1 + l/8)."""
+    _log("distance full size")
+    L, N, d = 32, 1024, 4096
+    cur = np.empty((L, N, d), np.uint16)
+    prev = np.empty_like(cur)
+    for l in range(L):
+        cur[l], prev[l], _ = synth.drift_pair(synth.rng(2, 0, l), N, d, 307, 0.01 * (1 + l / 8))
+    dc, dp = dev_bf16(cur), dev_bf16(prev)
+    dist, mean = stc.dcu_distance(dc, dp)
+    dist2, mean2 = stc.dcu_distance(dc, dp)
+    rd, rm = odist.distance_and_mean(cur, prev)
+    got = dist.cpu().numpy()
+    assert_rel(got, rd)
+    assert_rel(mean.cpu().numpy(), rm)
+    assert np.array_equal(got, dist2.cpu().numpy())
+    assert np.array_equal(mean.cpu().numpy(), mean2.cpu().numpy())
+    assert np.sum(got > 0) > 0.25 * L * N
+
+
+def test_distance_fp32_and_edge_rows():
+    _log("distance fp32 edges")
+    g = synth.rng(901, 0)
+    d = 64
+    a = g.standard_normal((1, 10, d)).astype(np.float32)
+    b = a.copy()
+    b[0, 1] = -a[0, 1]                 # 2
+    b[0, 2] = 4 * a[0, 2]              # ~0
+    a[0, 3] = 0.0                      # one zero row -> 1
+    a[0, 4] = 0.0
+    b[0, 4] = -0.0                     # two zero rows -> 0
+    b[0, 5] = a[0, 5] + 1e-3 * g.standard_normal(d).astype(np.float32)
+    b[0, 6, 0] = np.nextafter(a[0, 6, 0], np.float32(10))   # one ulp apart
+    b[0, 7] = g.standard_normal(d).astype(np.float32)
+    dist, mean = stc.dcu_distance(dev(a), dev(b))
+    rd, rm = odist.distance_and_mean(a, b)
+    got = dist.cpu().numpy()
+    assert got[0, 0] == 0.0 and got[0, 9] == 0.0
+    assert got[0, 3] == 1.0 and got[0, 4] == 0.0
+    assert got[0, 1] == 2.0
+    assert abs(got[0, 2]) <= 1e-7            # scaled copy: zero up to fp64 rounding
+    assert abs(got[0, 6]) <= 1e-12           # one ulp apart: zero up to fp64 rounding
+    keep = [0, 1, 3, 4, 5, 7, 8, 9]
+    assert_rel(got[:, keep], rd[:, keep])
+    assert_rel(mean.cpu().numpy(), rm, rtol=1e-5 if rm[0] > 1e-6 else 1e-3)
+
+
+def test_distance_tiny_fp32_config():
+    """2 layers, N=64, d=64 fp32, 25% of rows drifted by N(0, (0.05 (1+l))^2)."""
+    cur = np.empty((2, 64, 64), np.float32)
+    prev = np.empty_like(cur)
+    for l in range(2):
+        cur[l], prev[l], _ = synth.drift_pair(synth.rng(1, 2, l), 64, 64, 16, 0.05 * (1 + l),
+                                              bf16=False)
+    dist, mean = stc.dcu_distance(dev(cur), dev(prev))
+    rd, rm = odist.distance_and_mean(cur, prev)
+    assert_rel(dist.cpu().numpy(), rd)
+    assert_rel(mean.cpu().numpy(), rm)
+
+
+# ----------------------------------------------------------------------------- budget
+def test_budget_bit_exact():
+    _log("budget")
+    g = synth.rng(902, 0)
+    for B, L, bl in [(8, 32, 32), (3, 1, 5), (2, 64, 64), (1, 1024, 3), (4, 7, 0)]:
+        s = g.uniform(0, 1e-3, (B, L)).astype(np.float32)
+        if B > 1:
+            s[1] = 0.0                                  # uniform row
+        if B > 2:
+            s[2] = 0.0
+            s[2, L // 2] = 1e-4                         # one-hot row
+        if B > 3:
+            s[3] = np.float32(2.5e-4)                   # equal shares / ties
+        got = stc.dcu_budget(dev(s), B, L, bl).cpu().numpy()
+        ref = obud.layer_budget(s, B, L, bl)
+        assert np.array_equal(got, ref), (B, L, bl)
+        assert np.all(got.sum(1) == bl * L)
+    got = stc.dcu_budget(None, 3, 5, 9).cpu().numpy()
+    assert np.all(got == 9)
+    # depth-increasing means from the drift workload
+    s = np.array([[(1 + l / 8) ** 2 * 1e-5 for l in range(32)]], np.float32)
+    assert np.array_equal(stc.dcu_budget(dev(s), 1, 32, 32).cpu().numpy(),
+                          obud.layer_budget(s, 1, 32, 32))
+
+
+# ----------------------------------------------------------------------------- select
+def _check_select(d, budgets, layer, keys, bw):
+    sel, cnt = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw)
+    sel2, cnt2 = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw)
+    B, N = d.shape
+    kp = keys if keys is not None else np.zeros((B, 0), np.int32)
+    rs, rc = osel.select(d, budgets, layer, kp, bw)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(sel.cpu().numpy(), rs)
+    assert np.array_equal(sel.cpu().numpy(), sel2.cpu().numpy())
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 1024, 2048, 4097, 8192])
+def test_select_bit_exact(N):
+    _log(f"select N={N}")
+    g = synth.rng(903, N)
+    B, L = 4, 6
+    d = g.uniform(0, 1e-3, (B, N)).astype(np.float32)
+    d[g.random((B, N)) < 0.3] = 0.0                           # unchanged rows
+    d[g.random((B, N)) < 0.1] = np.float32(5e-4)              # ties
+    d[1] = np.float32(7e-5)                                   # a row of all-equal distances
+    budgets = g.integers(-2, max(3, N // 3), (B, L)).astype(np.int32)
+    budgets[0, 2] = N + 5                                     # more than the candidates
+    budgets[2, 2] = 0
+    keys = g.integers(-2, N + 2, (B, 4)).astype(np.int32)
+    keys[3] = [-1, 0, N - 1, N // 2]
+    for bw in [0, 1, 8, 32]:
+        _check_select(d, budgets, 2, keys, bw)
+    _check_select(d, budgets, 5, None, 0)
+
+
+def test_select_identical_inputs_give_only_windows():
+    d = np.zeros((2, 1024), np.float32)
+    budgets = np.full((2, 32), 32, np.int32)
+    keys = np.array([[600, 900, -1, -1], [0, 1023, 512, 513]], np.int32)
+    sel, cnt = stc.dcu_select(dev(d), dev(budgets), 31, dev(keys), 32)
+    rs, rc = osel.select(d, budgets, 31, keys, 32)
+    assert np.array_equal(sel.cpu().numpy(), rs) and np.array_equal(cnt.cpu().numpy(), rc)
+    assert cnt.cpu().numpy().tolist() == [64, 16 + 17 + 33]
+
+
+def test_select_on_drift_distances():
+    """Distances of the 32-layer drift workload feed the selection (budgets from the means)."""
+    L, N, d = 8, 1024, 4096
+    B = 1
+    cur = np.empty((L, N, d), np.uint16)
+    prev = np.empty_like(cur)
+    for l in range(L):
+        cur[l], prev[l], _ = synth.drift_pair(synth.rng(2, 1, l), N, d, 307, 0.01 * (1 + l / 8))
+    dist, mean = stc.dcu_distance(dev_bf16(cur), dev_bf16(prev))
+    budgets = stc.dcu_budget(mean.view(1, L), 1, L, 32)
+    keys = synth.key_positions(synth.rng(2, 2), 1, 4, 512, 1024)
+    dk = dev(keys)
+    dist_h = dist.cpu().numpy()
+    bud_h = budgets.cpu().numpy()
+    assert np.array_equal(bud_h, obud.layer_budget(mean.cpu().numpy().reshape(1, L), 1, L, 32))
+    for l in range(L):
+        sel, cnt = stc.dcu_select(dist[l:l + 1].contiguous(), budgets, l, dk, 32)
+        rs, rc = osel.select(dist_h[l:l + 1], bud_h, l, keys, 32)
+        assert np.array_equal(sel.cpu().numpy(), rs) and np.array_equal(cnt.cpu().numpy(), rc)
+
+
+# ----------------------------------------------------------------------------- confidence
+@pytest.mark.parametrize("R,V,ld,bf16", [(16, 1000, 1000, False), (64, 126464, 126464, True),
+                                         (7, 1001, 1008, True), (5, 3, 4, False), (3, 9, 16, True)])
+def test_confidence(R, V, ld, bf16):
+    _log(f"confidence R={R} V={V}")
+    g = synth.rng(904, R, V)
+    z, _ = synth.planted_logits(g, R, ld, bf16=bf16)
+    if R > 2:
+        z[2] = z[2, 0]                                 # every logit equal: c = 1/V, token 0
+        if bf16:
+            z[1, [5 % V, 1 % V]] = synth.f32_to_bf16(np.array([30.0], np.float32))[0]
+        else:
+            z[1, [5 % V, 1 % V]] = 30.0                # tie between two maxima -> lower index
+    t = dev_bf16(z) if bf16 else dev(z)
+    c, tok = stc.dllm_confidence(t, V)
+    c2, tok2 = stc.dllm_confidence(t, V)
+    rc, rt = oconf.confidence64(z, V)
+    assert np.array_equal(tok.cpu().numpy(), rt)
+    assert_rel(c.cpu().numpy(), rc)
+    assert np.array_equal(c.cpu().numpy(), c2.cpu().numpy())
+
+
+def test_confidence_full_size_sampled():
+    """[8 x 256, 126464] bf16 planted logits; the oracle checks a sample of rows."""
+    _log("confidence full size")
+    R, V = 2048, 126464
+    z, _ = synth.planted_logits(synth.rng(5, 0), R, V)
+    c, tok = stc.dllm_confidence(dev_bf16(z), V)
+    rows = np.arange(0, R, 16)
+    rc, rt = oconf.confidence64(z[rows], V)
+    assert np.array_equal(tok.cpu().numpy()[rows], rt)
+    assert_rel(c.cpu().numpy()[rows], rc)
+
+
+# ----------------------------------------------------------------------------- commit
+def _check_commit(c, delta, m_valid=None):
+    t = dev(c)
+    mv = dev(m_valid) if m_valid is not None else None
+    n, order = stc.frechet_commit(t, delta, mv)
+    rn, ro = ofre.frechet_commit(c, m_valid, delta)
+    assert np.array_equal(n.cpu().numpy(), rn)
+    assert np.array_equal(order.cpu().numpy(), ro)
+
+
+def test_commit_bit_exact():
+    _log("commit")
+    g = synth.rng(905, 0)
+    c = synth.confidence_profile(g, 8, 256, 0.0, 1.0)
+    for delta in [0.0, 0.1, 0.25, 0.9]:
+        _check_commit(c, delta)
+    # high-confidence heterogeneous profiles commit many
+    c = (1 - g.uniform(0, 0.02, (4, 64)) ** 2).astype(np.float32)
+    _check_commit(c, 0.1)
+    _check_commit(c, 0.0)
+    # ties, the page's profile, valid counts and empty rows
+    c = np.zeros((4, 16), np.float32)
+    c[0, :5] = [0.99, 0.95, 0.82, 0.78, 0.74]
+    c[1] = 0.9
+    c[2, ::2] = 0.97
+    c[3] = g.uniform(0, 1, 16)
+    _check_commit(c, 0.3, np.array([5, 16, 16, 0], np.int32))
+    _check_commit(c, 0.25, np.array([5, 3, 1, 17], np.int32))
+
+
+@pytest.mark.parametrize("m", [1, 2, 255, 1000, 4096, 8192])
+def test_commit_sizes(m):
+    g = synth.rng(905, m)
+    c = (1 - g.uniform(0, 0.05, (3, m)) ** 3).astype(np.float32)
+    _check_commit(c, 0.1)
+    _check_commit(c, 0.0, np.array([m, m // 2, 0], np.int32))
+
+
+def test_commit_outside_exactness_precondition_uses_sequential_sums():
+    g = synth.rng(905, 77)
+    c = g.uniform(0.9, 1.0, (2, 300)).astype(np.float32)
+    c[0, 5] = np.float32(1e-30)       # below 2^-17
+    c[1, 7] = np.float32(1.5)         # above 1
+    _check_commit(c, 0.1)
+
+
+def test_confidence_then_commit_full_end_of_step():
+    """End of step at full size: confidence over [8 x 256, 126464] logits, then commit with
+    delta = 0.1; the commit must agree exactly with the oracle rule applied to the GPU confidences
+    (same-input parity), and the confidences with the oracle's within 1e-5."""
+    R, V = 2048, 126464
+    z, _ = synth.planted_logits(synth.rng(5, 1), R, V)
+    c, tok = stc.dllm_confidence(dev_bf16(z), V)
+    n, order = stc.frechet_commit(c.view(8, 256), 0.1)
+    ch = c.cpu().numpy().reshape(8, 256)
+    rn, ro = ofre.frechet_commit(ch, None, 0.1)
+    assert np.array_equal(n.cpu().numpy(), rn)
+    assert np.array_equal(order.cpu().numpy(), ro)
