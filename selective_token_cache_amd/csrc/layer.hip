@@ -1,0 +1,769 @@
+// dcu_selective_layer: recompute only the selected rows of one transformer layer.
+// Dynamic-dLLM reading notes, Key design 1 (DCU): the selected tokens are recomputed and every other
+// token reuses its cached values; attention is bidirectional over every cached row.
+//
+// The layer is pre-norm: xn = RMSNorm(x; g_attn), [q|k|v] = xn W_qkv^T, attention of the selected
+// queries over all N cached keys/values (no mask, scale 1/sqrt(head_dim)), a = x + o W_o^T,
+// an = RMSNorm(a; g_ffn), y = a + (silu(an W_gate^T) * an W_up^T) W_down^T.
+//
+// Kernels, in stream order (no host synchronisation; ragged per-sequence counts stay on device):
+//  1. k_plan          one workgroup: per-sequence row offsets (clamped to the workspace capacity),
+//                     the compacted row map (selected row -> global cache row), attention q-tiles;
+//  2. k_rmsnorm       gather of the selected input rows + RMSNorm -> xn (bf16);
+//  3. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches;
+//  4. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
+//                     when there are too few tiles to fill the chip) + k_attn_combine;
+//  5. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
+//  6. k_rmsnorm       RMSNorm of a -> an (bf16);
+//  7. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
+//  8. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
+//
+// GEMM design (gfx950): Y[M, Nout] = A[M, K] W[Nout, K]^T with both operands K-contiguous. One
+// 256-thread workgroup computes a 128x128 tile; 4 waves each own 64x64 as 4x4 fragments of
+// v_mfma_f32_16x16x32_bf16. W fragments are the MFMA A operand and A-row fragments the B operand,
+// so every lane ends up with 4 consecutive output columns of one row (8- or 16-byte stores).
+// K-tiles of 64 are staged through XOR-swizzled LDS (double buffered, one barrier per K-tile) with
+// the next tile's global loads in flight during the MFMAs. The grid is persistent: each workgroup
+// walks tiles so that the M-tiles sharing a weight tile run together on one XCD (shared L2).
+#include <math.h>
+
+#include "common.h"
+
+namespace dcu {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ------------------------------------------------------------------------------ workspace header
+// int32 words at the start of the workspace
+constexpr int kHdrM = 0;   // rows recomputed (sum of clamped counts)
+constexpr int kHdrTq = 1;  // attention query tiles
+constexpr int kQTile = 64;
+
+struct Ptrs {
+  int* hdr;
+  int* seq_off;   // [B+1]
+  int* tile_off;  // [B+1]
+  int* tile_seq;  // [Tq_max]
+  int* rowmap;    // [M_cap]
+  uint16_t* xn;   // [M_cap, d] (later also an)
+  uint16_t* q;    // [M_cap, d]
+  uint16_t* o;    // [M_cap, d]
+  float* a;       // [M_cap, d]
+  uint16_t* h;    // [M_cap, F]
+  float* opart;   // [S, M_cap, d]      (split attention only)
+  float* ml;      // [S, M_cap, H, 2]   (split attention only)
+};
+
+// ------------------------------------------------------------------------------ 1. plan
+__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ sel_idx,
+                                               const int32_t* __restrict__ sel_count, int B, int N,
+                                               int M_cap, Ptrs P) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    int off = 0, toff = 0;
+    for (int b = 0; b < B; ++b) {
+      int c = sel_idx ? sel_count[b] : N;
+      c = c < 0 ? 0 : (c > N ? N : c);
+      P.seq_off[b] = off;
+      P.tile_off[b] = toff;
+      const int nxt = off + c < M_cap ? off + c : M_cap;
+      toff += (nxt - off + kQTile - 1) / kQTile;
+      off = nxt;
+    }
+    P.seq_off[B] = off;
+    P.tile_off[B] = toff;
+    P.hdr[kHdrM] = off;
+    P.hdr[kHdrTq] = toff;
+  }
+  __syncthreads();
+  for (int b = 0; b < B; ++b) {
+    const int s0 = P.seq_off[b], n = P.seq_off[b + 1] - s0;
+    const int t0 = P.tile_off[b], nt = P.tile_off[b + 1] - t0;
+    for (int j = t; j < n; j += blockDim.x)
+      P.rowmap[s0 + j] = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
+    for (int j = t; j < nt; j += blockDim.x) P.tile_seq[t0 + j] = b;
+  }
+}
+
+// ------------------------------------------------------------------------------ 2/6. RMSNorm
+// one wave per row; kF32In: fp32 rows (a), else bf16 rows of x gathered through rowmap
+template <bool kF32In>
+__global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x,
+                                                 const int* __restrict__ rowmap,
+                                                 const int* __restrict__ hdr,
+                                                 const uint16_t* __restrict__ gain, int d,
+                                                 float eps, uint16_t* __restrict__ out) {
+  const int M = hdr[kHdrM];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int groups = d / 8;  // 8 elements per lane step
+  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
+    float ss = 0.0f;
+    if constexpr (kF32In) {
+      const float* row = static_cast<const float*>(x) + int64_t(r) * d;
+      for (int g = lane; g < groups; g += kWave) {
+        const float4 u = reinterpret_cast<const float4*>(row)[2 * g];
+        const float4 v = reinterpret_cast<const float4*>(row)[2 * g + 1];
+        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w + v.x * v.x + v.y * v.y + v.z * v.z +
+              v.w * v.w;
+      }
+    } else {
+      const uint16_t* row = static_cast<const uint16_t*>(x) + int64_t(rowmap[r]) * d;
+      for (int g = lane; g < groups; g += kWave) {
+        const uint4 u = reinterpret_cast<const uint4*>(row)[g];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf_lo(w[j]), hi = bf_hi(w[j]);
+          ss += lo * lo + hi * hi;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
+    uint16_t* orow = out + int64_t(r) * d;
+    for (int g = lane; g < groups; g += kWave) {
+      float v[8];
+      if constexpr (kF32In) {
+        const float* row = static_cast<const float*>(x) + int64_t(r) * d;
+        const float4 u = reinterpret_cast<const float4*>(row)[2 * g];
+        const float4 w = reinterpret_cast<const float4*>(row)[2 * g + 1];
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+      } else {
+        const uint16_t* row = static_cast<const uint16_t*>(x) + int64_t(rowmap[r]) * d;
+        const uint4 u = reinterpret_cast<const uint4*>(row)[g];
+        v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+        v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+      }
+      const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
+      const float gv[8] = {bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y),
+                           bf_lo(gg.z), bf_hi(gg.z), bf_lo(gg.w), bf_hi(gg.w)};
+      uint4 o;
+      o.x = pack_bf2(v[0] * scale * gv[0], v[1] * scale * gv[1]);
+      o.y = pack_bf2(v[2] * scale * gv[2], v[3] * scale * gv[3]);
+      o.z = pack_bf2(v[4] * scale * gv[4], v[5] * scale * gv[5]);
+      o.w = pack_bf2(v[6] * scale * gv[6], v[7] * scale * gv[7]);
+      reinterpret_cast<uint4*>(orow)[g] = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ 3/5/7/8. GEMM
+enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3 };
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kChunks = kBK / 8;  // 16-byte chunks per LDS row
+
+struct GemmArgs {
+  const uint16_t* A;    // [M, K] compacted rows (workspace)
+  const uint16_t* W;    // [Nout, K]
+  const uint16_t* W2;   // SwiGLU: up weights [Nout, K]; W holds the gate weights
+  int K, Nout;          // Nout: W rows (SwiGLU: F)
+  const int* hdr;
+  const int* rowmap;
+  int d;                // model width (row stride of x, caches, y, q, o, a)
+  uint16_t* q;          // QKV: q rows
+  uint16_t* kc;         // QKV: cache scatter targets
+  uint16_t* vc;
+  const uint16_t* x;    // RESID: residual rows (global, via rowmap)
+  float* a;             // RESID: out; DOWN: residual in
+  uint16_t* h;          // SWIGLU: out [M, F]
+  uint16_t* y;          // DOWN: scatter target
+};
+
+__device__ __forceinline__ int lds_idx(int row, int c) { return row * kChunks + (c ^ (row & 7)); }
+
+template <int EPI>
+__device__ __forceinline__ int64_t w_row(const GemmArgs& g, int n_t, int tr, const uint16_t** base) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // tile rows [0,64) for wave column 0 and [64,128) for wave column 1; in each half the first
+    // 32 rows are gate rows and the next 32 the matching up rows
+    const int wn = tr >> 6, within = tr & 63;
+    const int j = n_t * 64 + wn * 32 + (within & 31);
+    *base = within < 32 ? g.W : g.W2;
+    return j;
+  } else {
+    int n = n_t * kBN + tr;
+    n = n < g.Nout ? n : g.Nout - 1;
+    *base = g.W;
+    return n;
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
+  __shared__ u32x4 smA[2][kBM * kChunks];
+  __shared__ u32x4 smB[2][kBN * kChunks];
+  const int M = g.hdr[kHdrM];
+  if (M <= 0) return;
+  const int MT = (M + kBM - 1) / kBM;
+  const int NT = EPI == EPI_SWIGLU ? g.Nout / 64 : (g.Nout + kBN - 1) / kBN;
+  const int total = MT * NT;
+  const int G = gridDim.x;  // a multiple of 8
+  const int per_xcd = G / 8;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int KT = g.K / kBK;
+
+  for (int round = 0;; ++round) {
+    const int tile = round * G + xcd * per_xcd + slot;
+    if (tile >= total) break;
+    const int m_t = tile % MT, n_t = tile / MT;
+    const int m0 = m_t * kBM;
+
+    // per-thread global source rows for the 4 A chunks and 4 W chunks it stages
+    const uint16_t* srcA[4];
+    const uint16_t* srcB[4];
+    int ldsi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + 256 * i;
+      const int row = q >> 3, c = q & 7;
+      int ar = m0 + row;
+      ar = ar < M ? ar : M - 1;
+      srcA[i] = g.A + int64_t(ar) * g.K + c * 8;
+      const uint16_t* wb;
+      const int64_t wr = w_row<EPI>(g, n_t, row, &wb);
+      srcB[i] = wb + wr * g.K + c * 8;
+      ldsi[i] = lds_idx(row, c);
+    }
+    u32x4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ld16(srcA[i]);
+      rb[i] = ld16(srcB[i]);
+    }
+    __syncthreads();  // previous tile's epilogue no longer reads LDS
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      smA[0][ldsi[i]] = ra[i];
+      smB[0][ldsi[i]] = rb[i];
+    }
+    __syncthreads();
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+      const bool more = kt + 1 < KT;
+      if (more) {
+        const int koff = (kt + 1) * kBK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ra[i] = ld16(srcA[i] + koff);
+          rb[i] = ld16(srcB[i] + koff);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ks * 4 + (lane >> 4);
+        u32x4 fw[4], fx[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int rw = wn * 64 + f * 16 + (lane & 15);
+          const int rx = wm * 64 + f * 16 + (lane & 15);
+          fw[f] = smB[buf][lds_idx(rw, c)];
+          fx[f] = smA[buf][lds_idx(rx, c)];
+        }
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 4; ++fn) acc[fm][fn] = mfma16x16x32(fw[fn], fx[fm], acc[fm][fn]);
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          smA[buf ^ 1][ldsi[i]] = ra[i];
+          smB[buf ^ 1][ldsi[i]] = rb[i];
+        }
+      }
+      __syncthreads();
+    }
+
+    // epilogue: lane holds rows m = m0 + wm*64 + fm*16 + (lane&15), 4 consecutive columns
+    const int cg = (lane >> 4) * 4;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const int m = m0 + wm * 64 + fm * 16 + (lane & 15);
+      if (m >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          const int j = n_t * 64 + wn * 32 + fn * 16 + cg;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gt = acc[fm][fn][i], up = acc[fm][fn + 2][i];
+            v[i] = gt / (1.0f + __expf(-gt)) * up;
+          }
+          uint2 st;
+          st.x = pack_bf2(v[0], v[1]);
+          st.y = pack_bf2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
+        }
+      } else {
+        const int64_t grow = (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_DOWN)
+                                 ? int64_t(g.rowmap[m]) : 0;
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+          const int n = n_t * kBN + wn * 64 + fn * 16 + cg;
+          if (n >= g.Nout) continue;
+          const f32x4 v = acc[fm][fn];
+          if constexpr (EPI == EPI_QKV) {
+            uint2 st;
+            st.x = pack_bf2(v[0], v[1]);
+            st.y = pack_bf2(v[2], v[3]);
+            const int part = n / g.d, col = n - part * g.d;
+            uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d
+                                      : (part == 1 ? g.kc : g.vc) + grow * g.d;
+            *reinterpret_cast<uint2*>(dst + col) = st;
+          } else if constexpr (EPI == EPI_RESID) {
+            const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+            float4 o;
+            o.x = bf_lo(xr.x) + v[0];
+            o.y = bf_hi(xr.x) + v[1];
+            o.z = bf_lo(xr.y) + v[2];
+            o.w = bf_hi(xr.y) + v[3];
+            *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
+          } else {  // EPI_DOWN
+            const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+            uint2 st;
+            st.x = pack_bf2(ar.x + v[0], ar.y + v[1]);
+            st.y = pack_bf2(ar.z + v[2], ar.w + v[3]);
+            *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ 4. attention
+// Work item = (query tile of <= 64 selected rows of one sequence, head, key split). 4 waves, each
+// owning 16 queries. S^T = K Q^T is computed with the key block as the MFMA A operand, so a lane
+// holds 4 keys x 1 query per fragment; that register layout is exactly the B operand that
+// O^T = V^T P^T needs (keys permuted consistently on both sides), so P never leaves registers.
+// K is staged in XOR-swizzled LDS, V transposed (V^T, padded rows) in LDS.
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  uint16_t* o;
+  float* opart;
+  float* ml;
+  const int* hdr;
+  const int* seq_off;
+  const int* tile_off;
+  const int* tile_seq;
+  int N, H, d, splits, kps, M_cap;
+  float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+
+constexpr int kKB = 64;           // keys per block
+constexpr int kVTStride = kKB + 4;  // padded V^T row (bf16 elements)
+
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
+  constexpr int CH = DH / 8;  // 16-byte chunks per head row
+  __shared__ u32x4 smK[kKB * CH];
+  __shared__ uint16_t smVT[DH * kVTStride];
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6, grp = lane >> 4, col = lane & 15;
+  const int Tq = g.hdr[kHdrTq];
+  const int items = Tq * g.H * g.splits;
+  for (int w = blockIdx.x; w < items; w += gridDim.x) {
+    const int split = w % g.splits;
+    const int h = (w / g.splits) % g.H;
+    const int tile = w / (g.splits * g.H);
+    const int b = g.tile_seq[tile];
+    const int r0 = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile;
+    const int rend = g.seq_off[b + 1];
+    const int kbeg = split * g.kps;
+    const int kend = min(g.N, kbeg + g.kps);
+    // this wave's 16 queries; lane column `col` is its query
+    int qr = r0 + wid * 16 + col;
+    const bool qvalid = qr < rend;
+    qr = qvalid ? qr : rend - 1;
+    u32x4 qf[DH / 32];
+#pragma unroll
+    for (int kk = 0; kk < DH / 32; ++kk)
+      qf[kk] = ld16(g.q + int64_t(qr) * g.d + h * DH + kk * 32 + grp * 8);
+
+    f32x4 acc_o[DH / 16];
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_part = 0.0f;
+    const int64_t cache_base = int64_t(b) * g.N;
+
+    for (int kb0 = kbeg; kb0 < kend; kb0 += kKB) {
+      __syncthreads();  // previous block's LDS reads are done
+      // K block -> swizzled LDS
+      for (int qd = t; qd < kKB * CH; qd += 256) {
+        const int key = qd / CH, c = qd % CH;
+        int kg = kb0 + key;
+        kg = kg < kend ? kg : kend - 1;
+        smK[key * CH + (c ^ (key & (CH - 1)))] =
+            ld16(g.kc + (cache_base + kg) * g.d + h * DH + c * 8);
+      }
+      // V block -> V^T: thread takes keys (2kp, 2kp+1) x 8 head dims
+      for (int qd = t; qd < (kKB / 2) * CH; qd += 256) {
+        const int kp = qd & 31, dc = qd >> 5;
+        int k0 = kb0 + 2 * kp, k1 = k0 + 1;
+        k0 = k0 < kend ? k0 : kend - 1;
+        k1 = k1 < kend ? k1 : kend - 1;
+        const u32x4 v0 = ld16(g.vc + (cache_base + k0) * g.d + h * DH + dc * 8);
+        const u32x4 v1 = ld16(g.vc + (cache_base + k1) * g.d + h * DH + dc * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = (v0[j] & 0xffffu) | (v1[j] << 16);
+          const uint32_t hi = (v0[j] >> 16) | (v1[j] & 0xffff0000u);
+          *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j) * kVTStride + 2 * kp]) = lo;
+          *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j + 1) * kVTStride + 2 * kp]) = hi;
+        }
+      }
+      __syncthreads();
+      // S^T for 64 keys x 16 queries: 4 fragments (keys 16f + 4*grp + i)
+      f32x4 s[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        s[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key = f * 16 + col;
+#pragma unroll
+        for (int kk = 0; kk < DH / 32; ++kk) {
+          const int c = kk * 4 + grp;
+          s[f] = mfma16x16x32(smK[key * CH + (c ^ (key & (CH - 1)))], qf[kk], s[f]);
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb0 + f * 16 + grp * 4 + i;
+          const float v = key < kend ? s[f][i] * g.scale_log2 : -INFINITY;
+          s[f][i] = v;
+          mx = v > mx ? v : mx;
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.0f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(s[f][i] - m_new);
+          psum += p[i];
+        }
+        pk[f][0] = pack_bf2(p[0], p[1]);
+        pk[f][1] = pack_bf2(p[2], p[3]);
+      }
+      l_part = l_part * alpha + psum;
+#pragma unroll
+      for (int df = 0; df < DH / 16; ++df) acc_o[df] *= alpha;
+      // O^T += V^T P^T over two 32-key chunks; MFMA k index 8*grp + j maps to key
+      // 32c + 4*grp + j (j < 4) and 32c + 16 + 4*grp + (j - 4) (j >= 4)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 pb = u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]};
+#pragma unroll
+        for (int df = 0; df < DH / 16; ++df) {
+          const int row = df * 16 + col;
+          const uint2 lo = *reinterpret_cast<const uint2*>(&smVT[row * kVTStride + 32 * c + 4 * grp]);
+          const uint2 hi =
+              *reinterpret_cast<const uint2*>(&smVT[row * kVTStride + 32 * c + 16 + 4 * grp]);
+          acc_o[df] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc_o[df]);
+        }
+      }
+    }
+    float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    if (qvalid) {
+      if (g.splits == 1) {
+        const float inv = 1.0f / l_tot;
+#pragma unroll
+        for (int df = 0; df < DH / 16; ++df) {
+          uint2 st;
+          st.x = pack_bf2(acc_o[df][0] * inv, acc_o[df][1] * inv);
+          st.y = pack_bf2(acc_o[df][2] * inv, acc_o[df][3] * inv);
+          *reinterpret_cast<uint2*>(g.o + int64_t(qr) * g.d + h * DH + df * 16 + grp * 4) = st;
+        }
+      } else {
+        float* op = g.opart + (int64_t(split) * g.M_cap + qr) * g.d + h * DH;
+#pragma unroll
+        for (int df = 0; df < DH / 16; ++df)
+          *reinterpret_cast<float4*>(op + df * 16 + grp * 4) =
+              make_float4(acc_o[df][0], acc_o[df][1], acc_o[df][2], acc_o[df][3]);
+        if (grp == 0) {
+          float* mlp = g.ml + ((int64_t(split) * g.M_cap + qr) * g.H + h) * 2;
+          mlp[0] = m_run;
+          mlp[1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
+// merge the key splits of every (row, head): one wave per pair, fixed split order
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH) {
+  const int M = g.hdr[kHdrM];
+  const int lane = threadIdx.x & 63;
+  const int64_t pairs = int64_t(M) * g.H;
+  for (int64_t p = int64_t(blockIdx.x) * 4 + threadIdx.x / 64; p < pairs;
+       p += int64_t(gridDim.x) * 4) {
+    const int r = int(p / g.H), h = int(p % g.H);
+    float mx = -INFINITY;
+    for (int s = 0; s < g.splits; ++s)
+      mx = fmaxf(mx, g.ml[((int64_t(s) * g.M_cap + r) * g.H + h) * 2]);
+    float l = 0.0f;
+    float acc0 = 0.0f, acc1 = 0.0f;
+    for (int s = 0; s < g.splits; ++s) {
+      const float* mlp = g.ml + ((int64_t(s) * g.M_cap + r) * g.H + h) * 2;
+      const float f = __builtin_amdgcn_exp2f(mlp[0] - mx);
+      l += mlp[1] * f;
+      const float* op = g.opart + (int64_t(s) * g.M_cap + r) * g.d + h * DH;
+      if (lane < DH) acc0 += op[lane] * f;
+      if (lane + 64 < DH) acc1 += op[lane + 64] * f;
+    }
+    const float inv = 1.0f / l;
+    uint16_t* dst = g.o + int64_t(r) * g.d + h * DH;
+    if (lane < DH) dst[lane] = uint16_t(f_to_bf_bits(acc0 * inv));
+    if (lane + 64 < DH) dst[lane + 64] = uint16_t(f_to_bf_bits(acc1 * inv));
+  }
+}
+
+// ------------------------------------------------------------------------------ host side
+constexpr int kCUs = 256;
+
+struct Layout {
+  int M_cap, Tq_max, splits, kps;
+  size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, opart, ml, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
+  Layout L{};
+  const int64_t BN = int64_t(B) * N;
+  L.M_cap = int(max_rows <= 0 || max_rows > BN ? BN : max_rows);
+  L.Tq_max = (L.M_cap + kQTile - 1) / kQTile + B;
+  // split the keys when the query tiles alone cannot fill the chip
+  const int64_t est = int64_t((L.M_cap + kQTile - 1) / kQTile) * w->n_heads;
+  int splits = 1;
+  if (est < 2 * kCUs) {
+    splits = int((2 * kCUs + est - 1) / est);
+    const int max_splits = N / 128 > 1 ? N / 128 : 1;
+    splits = splits < max_splits ? splits : max_splits;
+    splits = splits < 1 ? 1 : splits;
+  }
+  L.splits = splits;
+  L.kps = ((N + splits - 1) / splits + kKB - 1) / kKB * kKB;
+  const size_t d = size_t(w->d), F = size_t(w->ffn), M = size_t(L.M_cap);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.hdr = take(64);
+  L.seq_off = take(sizeof(int) * (B + 1));
+  L.tile_off = take(sizeof(int) * (B + 1));
+  L.tile_seq = take(sizeof(int) * L.Tq_max);
+  L.rowmap = take(sizeof(int) * M);
+  L.xn = take(2 * M * d);
+  L.q = take(2 * M * d);
+  L.o = take(2 * M * d);
+  L.a = take(4 * M * d);
+  L.h = take(2 * M * F);
+  if (splits > 1) {
+    L.opart = take(4 * size_t(splits) * M * d);
+    L.ml = take(4 * size_t(splits) * M * w->n_heads * 2);
+  }
+  L.total = off;
+  return L;
+}
+
+int validate(const dcu_layer* w, int B, int N) {
+  if (!w || B <= 0 || N <= 0) return DCU_EINVAL;
+  if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
+    return DCU_EINVAL;
+  if (w->d <= 0 || w->n_heads <= 0 || w->head_dim <= 0 || w->ffn <= 0) return DCU_EINVAL;
+  if (int64_t(w->n_heads) * w->head_dim != w->d) return DCU_EINVAL;
+  if (!(w->rms_eps >= 0.0f)) return DCU_EINVAL;
+  if (w->head_dim != 32 && w->head_dim != 64 && w->head_dim != 128) return DCU_EUNSUPPORTED;
+  if (w->d % 64 != 0 || w->ffn % 64 != 0) return DCU_EUNSUPPORTED;
+  if (N > 65536 || int64_t(B) * N > (int64_t(1) << 28)) return DCU_EUNSUPPORTED;
+  const void* ps[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn, w->g_ffn};
+  for (const void* p : ps)
+    if (!dcu_aligned16(p)) return DCU_EUNSUPPORTED;
+  return DCU_OK;
+}
+
+int gemm_grid(int M_cap, int NT) {
+  const int64_t tiles = int64_t((M_cap + kBM - 1) / kBM) * NT;
+  int64_t gsz = tiles < 2 * kCUs ? tiles : 2 * kCUs;
+  gsz = (gsz + 7) / 8 * 8;
+  return int(gsz < 8 ? 8 : gsz);
+}
+
+}  // namespace
+}  // namespace dcu
+
+extern "C" size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N,
+                                                int32_t max_rows) {
+  if (dcu::validate(w, B, N) != DCU_OK) return 0;
+  return dcu::make_layout(w, B, N, max_rows).total;
+}
+
+extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
+                                   const int32_t* sel_count, int32_t B, int32_t N,
+                                   int32_t max_rows, void* k_cache, void* v_cache, void* y_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dcu;
+  int st = validate(w, B, N);
+  if (st != DCU_OK) return st;
+  if (!x_in || !k_cache || !v_cache || !y_out) return DCU_EINVAL;
+  if ((sel_idx == nullptr) != (sel_count == nullptr)) return DCU_EINVAL;
+  if (!dcu_aligned16(x_in) || !dcu_aligned16(k_cache) || !dcu_aligned16(v_cache) ||
+      !dcu_aligned16(y_out))
+    return DCU_EUNSUPPORTED;
+  const Layout L = make_layout(w, B, N, max_rows);
+  if (!workspace || workspace_bytes < L.total) return DCU_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DCU_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Ptrs P;
+  P.hdr = reinterpret_cast<int*>(ws + L.hdr);
+  P.seq_off = reinterpret_cast<int*>(ws + L.seq_off);
+  P.tile_off = reinterpret_cast<int*>(ws + L.tile_off);
+  P.tile_seq = reinterpret_cast<int*>(ws + L.tile_seq);
+  P.rowmap = reinterpret_cast<int*>(ws + L.rowmap);
+  P.xn = reinterpret_cast<uint16_t*>(ws + L.xn);
+  P.q = reinterpret_cast<uint16_t*>(ws + L.q);
+  P.o = reinterpret_cast<uint16_t*>(ws + L.o);
+  P.a = reinterpret_cast<float*>(ws + L.a);
+  P.h = reinterpret_cast<uint16_t*>(ws + L.h);
+  P.opart = L.splits > 1 ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
+  P.ml = L.splits > 1 ? reinterpret_cast<float*>(ws + L.ml) : nullptr;
+  const int d = w->d, F = w->ffn, H = w->n_heads, DH = w->head_dim;
+  const uint16_t* x = static_cast<const uint16_t*>(x_in);
+
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, sel_idx, sel_count, int(B), int(N),
+                     L.M_cap, P);
+  DCU_LAUNCH_CHECK();
+
+  const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
+  hipLaunchKernelGGL(k_rmsnorm<false>, dim3(norm_blocks), dim3(256), 0, s,
+                     static_cast<const void*>(x), P.rowmap, P.hdr,
+                     static_cast<const uint16_t*>(w->g_attn), d, w->rms_eps, P.xn);
+  DCU_LAUNCH_CHECK();
+
+  GemmArgs ga{};
+  ga.hdr = P.hdr;
+  ga.rowmap = P.rowmap;
+  ga.d = d;
+  // QKV projection, k/v scattered into the caches
+  ga.A = P.xn;
+  ga.W = static_cast<const uint16_t*>(w->w_qkv);
+  ga.K = d;
+  ga.Nout = 3 * d;
+  ga.q = P.q;
+  ga.kc = static_cast<uint16_t*>(k_cache);
+  ga.vc = static_cast<uint16_t*>(v_cache);
+  hipLaunchKernelGGL(k_gemm<EPI_QKV>, dim3(gemm_grid(L.M_cap, (3 * d + kBN - 1) / kBN)),
+                     dim3(256), 0, s, ga);
+  DCU_LAUNCH_CHECK();
+
+  // attention over the updated caches
+  AttnArgs aa{};
+  aa.q = P.q;
+  aa.kc = static_cast<const uint16_t*>(k_cache);
+  aa.vc = static_cast<const uint16_t*>(v_cache);
+  aa.o = P.o;
+  aa.opart = P.opart;
+  aa.ml = P.ml;
+  aa.hdr = P.hdr;
+  aa.seq_off = P.seq_off;
+  aa.tile_off = P.tile_off;
+  aa.tile_seq = P.tile_seq;
+  aa.N = N;
+  aa.H = H;
+  aa.d = d;
+  aa.splits = L.splits;
+  aa.kps = L.kps;
+  aa.M_cap = L.M_cap;
+  aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
+  const int64_t items = int64_t(L.Tq_max) * H * L.splits;
+  const int attn_blocks = int(items < 4 * kCUs ? items : 4 * kCUs);
+  if (DH == 128)
+    hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  else if (DH == 64)
+    hipLaunchKernelGGL(k_attn<64>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  else
+    hipLaunchKernelGGL(k_attn<32>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  DCU_LAUNCH_CHECK();
+  if (L.splits > 1) {
+    const int64_t pairs = int64_t(L.M_cap) * H;
+    const int cb = int((pairs + 3) / 4 < 4096 ? (pairs + 3) / 4 : 4096);
+    hipLaunchKernelGGL(k_attn_combine, dim3(cb), dim3(256), 0, s, aa, DH);
+    DCU_LAUNCH_CHECK();
+  }
+
+  // output projection + residual -> a (fp32)
+  ga.A = P.o;
+  ga.W = static_cast<const uint16_t*>(w->w_o);
+  ga.K = d;
+  ga.Nout = d;
+  ga.x = x;
+  ga.a = P.a;
+  hipLaunchKernelGGL(k_gemm<EPI_RESID>, dim3(gemm_grid(L.M_cap, (d + kBN - 1) / kBN)), dim3(256),
+                     0, s, ga);
+  DCU_LAUNCH_CHECK();
+
+  // RMSNorm before the FFN -> an (reuses the xn buffer)
+  hipLaunchKernelGGL(k_rmsnorm<true>, dim3(norm_blocks), dim3(256), 0, s,
+                     static_cast<const void*>(P.a), P.rowmap, P.hdr,
+                     static_cast<const uint16_t*>(w->g_ffn), d, w->rms_eps, P.xn);
+  DCU_LAUNCH_CHECK();
+
+  // gate and up together, SwiGLU epilogue -> h
+  ga.A = P.xn;
+  ga.W = static_cast<const uint16_t*>(w->w_gate);
+  ga.W2 = static_cast<const uint16_t*>(w->w_up);
+  ga.K = d;
+  ga.Nout = F;
+  ga.h = P.h;
+  hipLaunchKernelGGL(k_gemm<EPI_SWIGLU>, dim3(gemm_grid(L.M_cap, F / 64)), dim3(256), 0, s, ga);
+  DCU_LAUNCH_CHECK();
+
+  // down projection + residual, scattered back into y_out
+  ga.A = P.h;
+  ga.W = static_cast<const uint16_t*>(w->w_down);
+  ga.W2 = nullptr;
+  ga.K = F;
+  ga.Nout = d;
+  ga.y = static_cast<uint16_t*>(y_out);
+  hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(gemm_grid(L.M_cap, (d + kBN - 1) / kBN)), dim3(256),
+                     0, s, ga);
+  DCU_LAUNCH_CHECK();
+  return DCU_OK;
+}

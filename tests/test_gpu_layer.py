@@ -1,0 +1,172 @@
+"""GPU parity of dcu_selective_layer against the oracle's fp64 layer on the same bf16 inputs.
+
+Bars: rel-L2 <= 1e-2 per tensor (K, V and output rows that were recomputed); rows outside the
+selection bitwise untouched; bitwise-deterministic across runs. Caches start from synthetic bf16
+contents (the state a previous step left behind), shared by both sides."""
+import numpy as np
+import pytest
+import torch
+
+import selective_token_cache_amd as stc
+from oracle import layer as olayer
+from tests.util import dev, dev_bf16, host_bf16, rel_l2
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class Case:
+    def __init__(self, shape, B, N, seed, std=0.02):
+        g = synth.rng(950, seed)
+        self.shape, self.B, self.N = shape, B, N
+        self.w = synth.layer_weights(g, shape, std=std, gain_jitter=0.2)
+        self.x = synth.normal_bf16(g, (B, N, shape.d))
+        # a previous step's cache contents, scaled like projections of unit-RMS rows
+        kv_std = std * np.sqrt(shape.d)
+        self.kc = synth.normal_bf16(g, (B, N, shape.n_heads, shape.head_dim), kv_std)
+        self.vc = synth.normal_bf16(g, (B, N, shape.n_heads, shape.head_dim), kv_std)
+        self.y = synth.normal_bf16(g, (B, N, shape.d))
+        self.g = g
+
+    def layer(self):
+        s = self.shape
+        t = {k: dev_bf16(v) for k, v in self.w.items()}
+        self._t = t
+        return stc.Layer(s.d, s.n_heads, s.head_dim, s.ffn, s.eps, t["w_qkv"], t["w_o"],
+                         t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"])
+
+    def run_gpu(self, sel, cnt, max_rows=0, reps=1):
+        L = self.layer()
+        out = []
+        for _ in range(reps):
+            kc, vc, y = dev_bf16(self.kc), dev_bf16(self.vc), dev_bf16(self.y)
+            stc.dcu_selective_layer(L, dev_bf16(self.x), None if sel is None else dev(sel),
+                                    None if cnt is None else dev(cnt), kc, vc, y,
+                                    max_rows=max_rows)
+            torch.cuda.synchronize()
+            out.append((host_bf16(kc), host_bf16(vc), host_bf16(y)))
+        return out
+
+    def run_oracle(self, sel, cnt):
+        s = self.shape
+        return olayer.selective_layer(self.w, s.n_heads, s.head_dim, s.eps, self.x, sel, cnt,
+                                      self.kc, self.vc, self.y)
+
+
+def _rows(sel, cnt, B, N):
+    if sel is None:
+        return [np.arange(N) for _ in range(B)]
+    return [sel[b, :cnt[b]].astype(np.int64) for b in range(B)]
+
+
+def _compare(case, got, ref, rows):
+    kc, vc, y = got
+    rk, rv, ry = ref
+    f = synth.bf16_to_f32
+    for b, r in enumerate(rows):
+        keep = np.setdiff1d(np.arange(case.N), r)
+        assert np.array_equal(kc[b, keep], case.kc[b, keep])
+        assert np.array_equal(vc[b, keep], case.vc[b, keep])
+        assert np.array_equal(y[b, keep], case.y[b, keep])
+    allr = [(b, r) for b, r in enumerate(rows) if len(r)]
+    if not allr:
+        return
+    gk = np.concatenate([f(kc[b, r]).reshape(len(r), -1) for b, r in allr])
+    gv = np.concatenate([f(vc[b, r]).reshape(len(r), -1) for b, r in allr])
+    gy = np.concatenate([f(y[b, r]) for b, r in allr])
+    ok = np.concatenate([rk[b, r].reshape(len(r), -1) for b, r in allr])
+    ov = np.concatenate([rv[b, r].reshape(len(r), -1) for b, r in allr])
+    oy = np.concatenate([ry[b, r] for b, r in allr])
+    ek, ev, ey = rel_l2(gk, ok), rel_l2(gv, ov), rel_l2(gy, oy)
+    _log(f"  rel-L2 K {ek:.2e} V {ev:.2e} Y {ey:.2e}")
+    assert ek <= TOL and ev <= TOL and ey <= TOL
+
+
+def _random_selection(g, B, N, counts):
+    sel = np.full((B, N), -1, np.int32)
+    for b, c in enumerate(counts):
+        sel[b, :c] = np.sort(g.choice(N, size=c, replace=False))
+    return sel, np.asarray(counts, np.int32)
+
+
+@pytest.mark.parametrize("shape,B,N,counts", [
+    (synth.TINY, 1, 64, [20]),                                                   # tiny fp32 config shapes
+    (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 3, 200, [130, 1, 0]),
+    (synth.LayerShape(d=512, n_heads=4, head_dim=128, ffn=768), 2, 300, [64, 257]),
+    (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 4, 77, [77, 5, 33, 64]),
+])
+def test_selective_layer_small_shapes(shape, B, N, counts):
+    _log(f"layer d={shape.d} H={shape.n_heads} dh={shape.head_dim} F={shape.ffn} B={B} N={N}")
+    case = Case(shape, B, N, seed=shape.d + N)
+    sel, cnt = _random_selection(case.g, B, N, counts)
+    (got, got2) = case.run_gpu(sel, cnt, reps=2)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
+
+
+def test_dense_mode_small():
+    shape = synth.LayerShape(d=256, n_heads=2, head_dim=128, ffn=320)
+    case = Case(shape, 2, 150, seed=7)
+    (got,) = case.run_gpu(None, None)
+    _compare(case, got, case.run_oracle(None, None), _rows(None, None, 2, 150))
+
+
+def test_empty_selection_and_max_rows_clamp():
+    shape = synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=128)
+    case = Case(shape, 3, 100, seed=8)
+    sel, cnt = _random_selection(case.g, 3, 100, [0, 0, 0])
+    (got,) = case.run_gpu(sel, cnt)
+    assert np.array_equal(got[0], case.kc) and np.array_equal(got[2], case.y)
+    # counts 40 + 50 + 30 with room for 70 rows: sequence 0 fully, sequence 1 its first 30 rows
+    sel, cnt = _random_selection(case.g, 3, 100, [40, 50, 30])
+    (got,) = case.run_gpu(sel, cnt, max_rows=70)
+    cl = np.array([40, 30, 0], np.int32)
+    _compare(case, got, case.run_oracle(sel, cl), _rows(sel, cl, 3, 100))
+
+
+def test_full_size_single_sequence_64_rows():
+    """One LLaDA-8B-shaped layer (d=4096, 32 heads x 128, FFN 12288), batch 1, N=1024, 64 rows:
+    a 32-wide window around one key in [512, 1024) plus 32 scattered rows."""
+    _log("layer full size batch 1")
+    case = Case(synth.LLADA8B, 1, 1024, seed=3)
+    key = int(case.g.integers(512, 1024))
+    lo = max(0, min(key - 16, 1024 - 32))
+    win = set(range(lo, lo + 32))
+    rest = np.setdiff1d(np.arange(1024), list(win))
+    extra = set(case.g.choice(rest, size=32, replace=False).tolist())
+    rows = np.array(sorted(win | extra), np.int32)
+    sel = np.full((1, 1024), -1, np.int32)
+    sel[0, :64] = rows
+    cnt = np.array([64], np.int32)
+    (got, got2) = case.run_gpu(sel, cnt, reps=2)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, 1, 1024))
+
+
+def test_full_size_batched_sampled():
+    """Batch 8, N=1024, LLaDA-8B shapes, ~150 rows per sequence; the oracle recomputes one
+    sequence completely (its rows depend only on that sequence's cache)."""
+    _log("layer full size batch 8")
+    shape = synth.LLADA8B
+    case = Case(shape, 8, 1024, seed=4)
+    counts = [150, 90, 200, 64, 128, 170, 99, 140]
+    sel, cnt = _random_selection(case.g, 8, 1024, counts)
+    (got,) = case.run_gpu(sel, cnt)
+    b = 2
+    ref = olayer.selective_layer(case.w, shape.n_heads, shape.head_dim, shape.eps,
+                                 case.x[b:b + 1], sel[b:b + 1], cnt[b:b + 1], case.kc[b:b + 1],
+                                 case.vc[b:b + 1], case.y[b:b + 1])
+    sub = Case.__new__(Case)
+    sub.kc, sub.vc, sub.y, sub.N = case.kc[b:b + 1], case.vc[b:b + 1], case.y[b:b + 1], 1024
+    _compare(sub, tuple(t[b:b + 1] for t in got), ref, _rows(sel[b:b + 1], cnt[b:b + 1], 1, 1024))
+    # every other sequence: untouched outside its selection
+    for bb in range(8):
+        keep = np.setdiff1d(np.arange(1024), sel[bb, :cnt[bb]])
+        assert np.array_equal(got[2][bb, keep], case.y[bb, keep])
