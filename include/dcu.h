@@ -59,7 +59,8 @@ int dcu_version(void);
  * Dynamic-dLLM notes, Key design 1 (DCU), budget equation: the total T = b_layer * L of each
  * sequence is split across the L layers in proportion to the previous step's layer means.
  *
- * s_prev  [B, L] fp32 layer means of the previous step, or NULL for "no previous step".
+ * s_prev  [L, B] fp32 layer means of the previous step, layer-major (each layer's dcu_distance
+ *         call writes its B means contiguously), or NULL for "no previous step".
  * budget  [B, L] int32 out. Each row sums to exactly T: floor of T*s/sum(s) plus one for the
  *         largest remainders (ties to the lower layer), computed in IEEE fp64 in a fixed order.
  *         A NULL s_prev, or a row whose means sum to 0, gives b_layer to every layer.
@@ -118,7 +119,7 @@ int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t lay
 typedef struct {
   int32_t d;          /* model width, = n_heads * head_dim          */
   int32_t n_heads;
-  int32_t head_dim;   /* 64 or 128                                    */
+  int32_t head_dim;   /* 32, 64 or 128                                */
   int32_t ffn;        /* FFN width F                                  */
   float rms_eps;
   const void* w_qkv;  /* bf16 [3d, d]: rows Wq | Wk | Wv              */
@@ -149,13 +150,31 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  * y_out     [B, N, d] bf16 IN/OUT: selected rows get the layer output; other rows are untouched.
  * workspace device scratch of at least dcu_selective_layer_workspace() bytes (256-byte aligned).
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
- *         d != n_heads*head_dim; EUNSUPPORTED if head_dim not in {64, 128}, d or ffn not a
- *         multiple of 256, or N > 65536; EWORKSPACE if the workspace is too small.
+ *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if head_dim not in {32, 64, 128}, d
+ *         or ffn not a multiple of 64, N > 65536, B*N > 2^28, or a pointer not 16-byte aligned;
+ *         EWORKSPACE if the workspace is too small or not 256-byte aligned.
  */
 int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
                         const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
                         void* k_cache, void* v_cache, void* y_out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * dcu_selective_layer_staged -- dcu_selective_layer with per-stage timing marks, for measurement.
+ * Identical work and results; additionally records the caller-created hipEvent_t events[0] before
+ * the first kernel and events[i] after stage i on `stream`, for the DCU_LAYER_STAGES stages
+ *   1 plan (row offsets and map), 2 gather + RMSNorm, 3 QKV projection + K/V scatter,
+ *   4 attention (+ split combine), 5 output projection + residual, 6 RMSNorm,
+ *   7 gate/up projection + SwiGLU, 8 down projection + residual + scatter.
+ * events may be NULL (then this is dcu_selective_layer); otherwise n_events must be at least
+ * DCU_LAYER_STAGES + 1 (EINVAL). A failed event record returns DCU_EHIP.
+ */
+#define DCU_LAYER_STAGES 8
+int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
+                               const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
+                               void* k_cache, void* v_cache, void* y_out, void* workspace,
+                               size_t workspace_bytes, void* stream, void* const* events,
+                               int32_t n_events);
 
 /*
  * dllm_confidence -- confidence and argmax of each candidate position.

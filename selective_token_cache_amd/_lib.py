@@ -49,6 +49,10 @@ EXPORTS = {
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
                                            _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "dcu_selective_layer_staged": (ctypes.c_int,
+                                   [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32, _i32, _vp,
+                                    _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                    ctypes.POINTER(_vp), _i32]),
     "dllm_confidence": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
 }
@@ -110,8 +114,9 @@ def _check(fn: str, status: int):
 
 # ----------------------------------------------------------------------------- entry points
 def dcu_budget(s_prev: torch.Tensor | None, B: int, L: int, b_layer: int, out=None, stream=None):
+    """s_prev [L, B] fp32 (layer-major previous-step means) or None -> budget [B, L] int32."""
     if s_prev is not None:
-        _need(s_prev, "s_prev", torch.float32, (B, L))
+        _need(s_prev, "s_prev", torch.float32, (L, B))
         dev = s_prev.device
     else:
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -184,10 +189,18 @@ class Layer:
         return int(load().dcu_selective_layer_workspace(ctypes.byref(self.desc), B, N, max_rows))
 
 
+LAYER_STAGES = ("plan", "gather_rmsnorm", "qkv_scatter", "attention", "o_proj_residual",
+                "rmsnorm", "gate_up_swiglu", "down_residual_scatter")
+
+
 def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_cache, v_cache,
                         y_out, max_rows: int = 0, workspace: torch.Tensor | None = None,
-                        stream=None):
-    """Recompute the selected rows in place (k_cache, v_cache, y_out are in/out)."""
+                        stream=None, events=None):
+    """Recompute the selected rows in place (k_cache, v_cache, y_out are in/out).
+
+    events: optional sequence of len(LAYER_STAGES) + 1 torch.cuda.Event(enable_timing=True);
+    event 0 is recorded before the first kernel and event i after stage i, on the library's
+    stream (dcu_selective_layer_staged)."""
     _need(x_in, "x_in", torch.bfloat16)
     B, N, d = x_in.shape
     if d != layer.d:
@@ -204,10 +217,22 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
     _need(workspace, "workspace", torch.uint8)
-    st = load().dcu_selective_layer(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx), _p(sel_count),
-                                    B, N, max_rows, _p(k_cache), _p(v_cache), _p(y_out),
-                                    _p(workspace), workspace.numel(), _stream(stream))
-    _check("dcu_selective_layer", st)
+    if events is None:
+        st = load().dcu_selective_layer(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
+                                        _p(sel_count), B, N, max_rows, _p(k_cache), _p(v_cache),
+                                        _p(y_out), _p(workspace), workspace.numel(),
+                                        _stream(stream))
+        _check("dcu_selective_layer", st)
+    else:
+        if len(events) < len(LAYER_STAGES) + 1:
+            raise ValueError(f"need {len(LAYER_STAGES) + 1} events")
+        arr = (_vp * len(events))(*[_vp(e.cuda_event) for e in events])
+        st = load().dcu_selective_layer_staged(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
+                                               _p(sel_count), B, N, max_rows, _p(k_cache),
+                                               _p(v_cache), _p(y_out), _p(workspace),
+                                               workspace.numel(), _stream(stream), arr,
+                                               len(events))
+        _check("dcu_selective_layer_staged", st)
     return k_cache, v_cache, y_out
 
 

@@ -15,7 +15,7 @@
 namespace dcu {
 namespace {
 
-__global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_prev, int L,
+__global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_prev, int B, int L,
                                                  int b_layer, int32_t* __restrict__ budget) {
   __shared__ float s_s[1024];
   __shared__ double s_r[1024];
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_pre
     if (l < L) out[l] = b_layer;
     return;
   }
-  if (l < L) s_s[l] = s_prev[int64_t(b) * L + l];
+  if (l < L) s_s[l] = s_prev[int64_t(l) * B + b];  // layer-major [L, B]
   __syncthreads();
   if (l == 0) {
     double S = 0.0;
@@ -85,7 +85,7 @@ extern "C" int dcu_budget(const float* s_prev, int32_t B, int32_t L, int32_t b_l
   if (L > 1024) return DCU_EUNSUPPORTED;
   const int threads = ((L + 63) / 64) * 64;
   hipLaunchKernelGGL(dcu::k_budget, dim3(unsigned(B)), dim3(threads), 0,
-                     static_cast<hipStream_t>(stream), s_prev, int(L), int(b_layer), budget);
+                     static_cast<hipStream_t>(stream), s_prev, int(B), int(L), int(b_layer), budget);
   DCU_LAUNCH_CHECK();
   return DCU_OK;
 }

@@ -634,11 +634,14 @@ extern "C" size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, i
   return dcu::make_layout(w, B, N, max_rows).total;
 }
 
-extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
-                                   const int32_t* sel_count, int32_t B, int32_t N,
-                                   int32_t max_rows, void* k_cache, void* v_cache, void* y_out,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
+                                          const int32_t* sel_idx, const int32_t* sel_count,
+                                          int32_t B, int32_t N, int32_t max_rows, void* k_cache,
+                                          void* v_cache, void* y_out, void* workspace,
+                                          size_t workspace_bytes, void* stream,
+                                          void* const* events, int32_t n_events) {
   using namespace dcu;
+  if (events != nullptr && n_events < DCU_LAYER_STAGES + 1) return DCU_EINVAL;
   int st = validate(w, B, N);
   if (st != DCU_OK) return st;
   if (!x_in || !k_cache || !v_cache || !y_out) return DCU_EINVAL;
@@ -666,16 +669,24 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
   P.ml = L.splits > 1 ? reinterpret_cast<float*>(ws + L.ml) : nullptr;
   const int d = w->d, F = w->ffn, H = w->n_heads, DH = w->head_dim;
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
+  int stage = 0;
+  auto mark = [&]() -> bool {
+    if (!events) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(events[stage++]), s) == hipSuccess;
+  };
+  if (!mark()) return DCU_EHIP;
 
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, sel_idx, sel_count, int(B), int(N),
                      L.M_cap, P);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
   hipLaunchKernelGGL(k_rmsnorm<false>, dim3(norm_blocks), dim3(256), 0, s,
                      static_cast<const void*>(x), P.rowmap, P.hdr,
                      static_cast<const uint16_t*>(w->g_attn), d, w->rms_eps, P.xn);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   GemmArgs ga{};
   ga.hdr = P.hdr;
@@ -692,6 +703,7 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
   hipLaunchKernelGGL(k_gemm<EPI_QKV>, dim3(gemm_grid(L.M_cap, (3 * d + kBN - 1) / kBN)),
                      dim3(256), 0, s, ga);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   // attention over the updated caches
   AttnArgs aa{};
@@ -727,6 +739,7 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
     hipLaunchKernelGGL(k_attn_combine, dim3(cb), dim3(256), 0, s, aa, DH);
     DCU_LAUNCH_CHECK();
   }
+  if (!mark()) return DCU_EHIP;
 
   // output projection + residual -> a (fp32)
   ga.A = P.o;
@@ -738,12 +751,14 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
   hipLaunchKernelGGL(k_gemm<EPI_RESID>, dim3(gemm_grid(L.M_cap, (d + kBN - 1) / kBN)), dim3(256),
                      0, s, ga);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   // RMSNorm before the FFN -> an (reuses the xn buffer)
   hipLaunchKernelGGL(k_rmsnorm<true>, dim3(norm_blocks), dim3(256), 0, s,
                      static_cast<const void*>(P.a), P.rowmap, P.hdr,
                      static_cast<const uint16_t*>(w->g_ffn), d, w->rms_eps, P.xn);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   // gate and up together, SwiGLU epilogue -> h
   ga.A = P.xn;
@@ -754,6 +769,7 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
   ga.h = P.h;
   hipLaunchKernelGGL(k_gemm<EPI_SWIGLU>, dim3(gemm_grid(L.M_cap, F / 64)), dim3(256), 0, s, ga);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
 
   // down projection + residual, scattered back into y_out
   ga.A = P.h;
@@ -765,5 +781,14 @@ extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const i
   hipLaunchKernelGGL(k_gemm<EPI_DOWN>, dim3(gemm_grid(L.M_cap, (d + kBN - 1) / kBN)), dim3(256),
                      0, s, ga);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
   return DCU_OK;
+}
+
+extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
+                                   const int32_t* sel_count, int32_t B, int32_t N,
+                                   int32_t max_rows, void* k_cache, void* v_cache, void* y_out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return dcu_selective_layer_staged(w, x_in, sel_idx, sel_count, B, N, max_rows, k_cache, v_cache,
+                                    y_out, workspace, workspace_bytes, stream, nullptr, 0);
 }

@@ -112,7 +112,7 @@ def test_budget_bit_exact():
             s[2, L // 2] = 1e-4                         # one-hot row
         if B > 3:
             s[3] = np.float32(2.5e-4)                   # equal shares / ties
-        got = stc.dcu_budget(dev(s), B, L, bl).cpu().numpy()
+        got = stc.dcu_budget(dev(s.T.copy()), B, L, bl).cpu().numpy()
         ref = obud.layer_budget(s, B, L, bl)
         assert np.array_equal(got, ref), (B, L, bl)
         assert np.all(got.sum(1) == bl * L)
@@ -120,7 +120,7 @@ def test_budget_bit_exact():
     assert np.all(got == 9)
     # depth-increasing means from the drift workload
     s = np.array([[(1 + l / 8) ** 2 * 1e-5 for l in range(32)]], np.float32)
-    assert np.array_equal(stc.dcu_budget(dev(s), 1, 32, 32).cpu().numpy(),
+    assert np.array_equal(stc.dcu_budget(dev(s.T.copy()), 1, 32, 32).cpu().numpy(),
                           obud.layer_budget(s, 1, 32, 32))
 
 
@@ -174,7 +174,7 @@ def test_select_on_drift_distances():
     for l in range(L):
         cur[l], prev[l], _ = synth.drift_pair(synth.rng(2, 1, l), N, d, 307, 0.01 * (1 + l / 8))
     dist, mean = stc.dcu_distance(dev_bf16(cur), dev_bf16(prev))
-    budgets = stc.dcu_budget(mean.view(1, L), 1, L, 32)
+    budgets = stc.dcu_budget(mean.view(L, 1), 1, L, 32)
     keys = synth.key_positions(synth.rng(2, 2), 1, 4, 512, 1024)
     dk = dev(keys)
     dist_h = dist.cpu().numpy()
