@@ -1,0 +1,245 @@
+// Persistent bf16 MFMA GEMM core for gfx950: Y[M, Nout] = A[M, K] * W[Nout, K]^T, both operands
+// K-contiguous (row-major activations, [out, in] weights), fp32 accumulation.
+//
+// * One 256-thread workgroup (4 waves in a WGM x WGN grid) computes a BM x BN tile; each wave owns
+//   WM x WN as (WM/16) x (WN/16) fragments of v_mfma_f32_16x16x32_bf16. The weight fragment is the
+//   MFMA A operand and the activation fragment the B operand, so each lane ends with 4 consecutive
+//   output columns of one output row.
+// * K advances in tiles of BK (32 or 64). Tiles stream global -> LDS with global_load_lds_dwordx4 (no VGPR
+//   staging) through STAGES distinct LDS buffers: while the MFMAs consume tile kt, the loads of tiles
+//   kt+1 .. kt+STAGES-1 are in flight. Each buffer is a separate __shared__ array and the stage index
+//   is a compile-time constant, so the compiler only waits on the DMA group that is actually consumed
+//   (a raw s_barrier is used: __syncthreads would drain every outstanding load).
+// * LDS rows are BK bf16; chunk c of row r is stored at c ^ (r & 7) (BK = 64) or c ^ ((r >> 2) & 3)
+//   (BK = 32), which spreads the 16 rows read by one MFMA operand load over the banks. The DMA
+//   writes 64 consecutive chunks per instruction, so the swizzle is applied by choosing which global
+//   chunk each lane fetches.
+// * Rows of A beyond M are clamped to row M-1 (valid memory; their results are never stored); the
+//   prefetch of K-tiles past the end is clamped to the last tile (its buffer is never consumed), which
+//   keeps the number of DMA groups in flight uniform.
+// * Tiles are walked persistently; tile ids are remapped so that consecutive M-tiles sharing one
+//   weight tile run on the same XCD (workgroup i runs on XCD i % 8) and share its L2.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace dcu {
+namespace gemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define DCU_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One wave-wide 16-byte-per-lane DMA: lane i copies 16 bytes from gptr to LDS byte address
+// lds_addr + 16 i. Written as asm so that the compiler does not add its own (conservative) waits
+// for the LDS writes: completion is tracked explicitly with s_waitcnt vmcnt before each barrier.
+// No output registers; "memory" keeps other memory accesses from moving across it.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = n (0..63) and lgkmcnt = 0; expcnt left at its maximum
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// chunk c of row r in a stage buffer with RC 16-byte chunks per row (RC = BK / 8)
+template <int RC>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (RC == 8)
+    return row * 8 + (c ^ (row & 7));
+  else
+    return row * 4 + (c ^ ((row >> 2) & 3));
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int NW_ = 4, int MF_ = 16, int BK_ = 64>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_, NW = NW_;
+  static constexpr int MF = MF_, BK = BK_, RC = BK / 8;
+  static constexpr int ROWS_PER_DMA = 64 / RC;  // rows written by one wave-wide 16-byte DMA
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WGM = BM / WM, WGN = BN / WN;
+  static_assert(WGM * WGN == NW, "wave grid");
+  static constexpr int FM = WM / MF, FN = WN / MF;
+  static constexpr int ROWS = BM + BN;                 // LDS rows per stage
+  static constexpr int CHUNKS = ROWS * RC;             // 16-byte chunks per stage
+  static constexpr int NQ = ROWS / (ROWS_PER_DMA * NW);  // DMA instructions per wave per stage
+  static_assert(ROWS % (ROWS_PER_DMA * NW) == 0, "rows per stage");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert((STAGES - 2) * NQ < 64, "vmcnt range");
+  using acc_t = typename std::conditional<MF == 16, f32x4, f32x16>::type;
+};
+
+// Row source of the weight operand for tile n_t and tile row tr (0 <= tr < BN). The default maps
+// tile row tr to weight row n_t*BN + tr (clamped); a policy may interleave two matrices.
+struct PlainRows {
+  const uint16_t* W;
+  int Nout;
+  template <int BN>
+  __device__ __forceinline__ const uint16_t* row(int n_t, int tr, int K) const {
+    int n = n_t * BN + tr;
+    n = n < Nout ? n : Nout - 1;
+    return W + int64_t(n) * K;
+  }
+  template <int BN>
+  __device__ __forceinline__ int tiles() const { return (Nout + BN - 1) / BN; }
+};
+
+// Gate/up interleave: each wave's WN tile rows are WN/2 gate rows followed by the WN/2 up rows of
+// the same output columns, so matching gate and up accumulators land in the same lane.
+template <int WN>
+struct GateUpRows {
+  const uint16_t* Wg;
+  const uint16_t* Wu;
+  int F;
+  template <int BN>
+  __device__ __forceinline__ const uint16_t* row(int n_t, int tr, int K) const {
+    const int wn = tr / WN, within = tr % WN;
+    const int j = n_t * (BN / 2) + wn * (WN / 2) + (within % (WN / 2));
+    return (within < WN / 2 ? Wg : Wu) + int64_t(j) * K;
+  }
+  template <int BN>
+  __device__ __forceinline__ int tiles() const { return F / (BN / 2); }
+};
+
+// Main loop over one tile. acc is [FM][FN] f32x4. Buffers b0..b3 are the stage arrays.
+template <class C, class WRows>
+__device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C::FN], const uint16_t* A,
+                                              int M, int K, int m0, int n_t, const WRows& wr,
+                                              u32x4* b0, u32x4* b1, u32x4* b2, u32x4* b3) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+  const int KT = K / C::BK;
+  // per-lane global source rows of this wave's DMA instructions
+  const uint16_t* src[C::NQ];
+#pragma unroll
+  for (int i = 0; i < C::NQ; ++i) {
+    const int q = i * C::NW + wid;
+    const int row = q * C::ROWS_PER_DMA + lane / C::RC;
+    const int pc = lane % C::RC;
+    const int c = C::RC == 8 ? (pc ^ (row & 7)) : (pc ^ ((row >> 2) & 3));
+    const uint16_t* base;
+    if (row < C::BM) {
+      int ar = m0 + row;
+      ar = ar < M ? ar : M - 1;
+      base = A + int64_t(ar) * K;
+    } else {
+      base = wr.template row<C::BN>(n_t, row - C::BM, K);
+    }
+    src[i] = base + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
+
+  // the wave index as a scalar, so every DMA's LDS base (M0) is computed without readfirstlane
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  // all DMA instructions of a stage are issued back to back and kept together by a scheduling
+  // barrier: interleaving them with LDS reads would make every M0 write wait for those reads
+  auto issue = [&](auto sidx, int kt) {
+    constexpr int S = decltype(sidx)::value;
+    u32x4* buf = S == 0 ? b0 : (S == 1 ? b1 : (S == 2 ? b2 : b3));
+    const int kc = kt < KT ? kt : KT - 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int q = i * C::NW + wid_s;
+      dma16(static_cast<const void*>(src[i] + kc * C::BK),
+            uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(buf + q * 64))));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](auto sidx) {
+    constexpr int S = decltype(sidx)::value;
+    const u32x4* buf = S == 0 ? b0 : (S == 1 ? b1 : (S == 2 ? b2 : b3));
+    if constexpr (C::MF == 16) {
+#pragma unroll
+      for (int ks = 0; ks < C::BK / 32; ++ks) {
+        const int c = ks * 4 + (lane >> 4);
+        u32x4 fw[C::FN], fx[C::FM];
+#pragma unroll
+        for (int f = 0; f < C::FN; ++f)
+          fw[f] = buf[swz<C::RC>(C::BM + wn * C::WN + f * 16 + (lane & 15), c)];
+#pragma unroll
+        for (int f = 0; f < C::FM; ++f) fx[f] = buf[swz<C::RC>(wm * C::WM + f * 16 + (lane & 15), c)];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma(fw[j], fx[i], acc[i][j]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::BK / 16; ++ks) {
+        const int c = ks * 2 + (lane >> 5);
+        u32x4 fw[C::FN], fx[C::FM];
+#pragma unroll
+        for (int f = 0; f < C::FN; ++f)
+          fw[f] = buf[swz<C::RC>(C::BM + wn * C::WN + f * 32 + (lane & 31), c)];
+#pragma unroll
+        for (int f = 0; f < C::FM; ++f) fx[f] = buf[swz<C::RC>(wm * C::WM + f * 32 + (lane & 31), c)];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32(fw[j], fx[i], acc[i][j]);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // prologue: tiles 0 .. STAGES-2
+  issue(I0{}, 0);
+  if constexpr (C::STAGES > 2) issue(I1{}, 1);
+  if constexpr (C::STAGES > 3) issue(I2{}, 2);
+  // steady state, unrolled by STAGES so that every buffer index is a constant
+  auto iter = [&](auto cur, int kt) {
+    constexpr int S = decltype(cur)::value;
+    constexpr int NXT = (S + C::STAGES - 1) % C::STAGES;
+    wait_vm_lgkm0<(C::STAGES - 2) * C::NQ>();
+    __builtin_amdgcn_s_barrier();
+    issue(std::integral_constant<int, NXT>{}, kt + C::STAGES - 1);
+    compute(cur);
+  };
+  for (int kt = 0; kt < KT; kt += C::STAGES) {
+    iter(I0{}, kt);
+    if (kt + 1 < KT) iter(I1{}, kt + 1); else break;
+    if constexpr (C::STAGES > 2) { if (kt + 2 < KT) iter(I2{}, kt + 2); else break; }
+    if constexpr (C::STAGES > 3) { if (kt + 3 < KT) iter(I3{}, kt + 3); else break; }
+  }
+  // drain the clamped prefetches before the buffers are reused by the next tile
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// Persistent tile walk: the round-th tile of this workgroup, remapped XCD-major.
+__device__ __forceinline__ bool next_tile(int round, int total, int MT, int* m_t, int* n_t) {
+  const int G = gridDim.x, per_xcd = G >> 3;
+  const int tile = round * G + (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= total) return false;
+  *m_t = tile % MT;
+  *n_t = tile / MT;
+  return true;
+}
+
+}  // namespace gemm
+}  // namespace dcu
