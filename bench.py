@@ -39,7 +39,8 @@ V, M_CAND = 126464, 256
 B_LAYER, B_WINDOW, N_KEYS, DELTA = 32, 32, 4, 0.1
 CFG = 5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_swiglu.json")
-KERNEL_SOURCES = ["selective_token_cache_amd/csrc/layer.hip", "selective_token_cache_amd/csrc/common.h"]
+KERNEL_SOURCES = ["selective_token_cache_amd/csrc/layer.hip", "selective_token_cache_amd/csrc/gemm.h",
+                  "selective_token_cache_amd/csrc/common.h"]
 
 
 def log(msg):
@@ -72,7 +73,97 @@ def stage_flops_bytes(M: int):
     }
 
 
+def summarize_profiles(ktrace_dir, fetch_dir, write_dir, bench_json, steps, cmds):
+    """Write the committed profile summaries from rocprofv3 outputs of the commands in `cmds`:
+    the kernel-trace average of the gate/up GEMM over the timed steps' launches (the last
+    steps*32), and its per-launch HBM-side bytes from FETCH_SIZE / WRITE_SIZE scaled by what those
+    counters read for a plain 1 GiB device copy (the runtime's copy kernel) in the same run."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        return list(csv.DictReader(open(glob.glob(os.path.join(d, f"*{suffix}"))[0])))
+
+    tag = "k_gemm<2,"
+    kt = [r for r in rows(ktrace_dir, "_kernel_trace.csv") if tag in r["Kernel_Name"]]
+    kt.sort(key=lambda r: int(r["Start_Timestamp"]))
+    timed = kt[-steps * L:]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+    avg_us = sum(durs) / len(durs)
+    bj = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    stats = rows(ktrace_dir, "_kernel_stats.csv")
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+
+    def counter(d, name):
+        rs = rows(d, "_counter_collection.csv")
+        g = [float(r["Counter_Value"]) for r in rs if tag in r["Kernel_Name"]][-L:]
+        cp = [float(r["Counter_Value"]) for r in rs
+              if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer") and int(r["Grid_Size"]) >= 131072][-3:]
+        return sum(g) / len(g), sum(cp) / len(cp)
+
+    f_k, f_cp = counter(fetch_dir, "FETCH_SIZE")
+    w_k, w_cp = counter(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = f_cp / gib_kib, w_cp / gib_kib
+    fetch_b = f_k * 1024 / f_scale
+    write_b = w_k * 1024 / w_scale
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    traffic = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU), 128x128 tiles",
+               "workload": "full 32-layer step, batch 8, N=1024, LLaDA-8B shapes",
+               "source_sha256": source_hash(),
+               "fetch_size_kib_per_launch": round(f_k, 1), "write_size_kib_per_launch": round(w_k, 1),
+               "copy_1GiB_fetch_kib": round(f_cp, 1), "copy_1GiB_write_kib": round(w_cp, 1),
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+               "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+               "traffic_bytes_per_launch": int(fetch_b + write_b),
+               "algorithmic_bytes_per_launch": None,
+               "commands": cmds[1:]}
+    M_avg = bj["rows_per_step"] / L
+    alg = 2 * F * D * 2 + M_avg * D * 2 + M_avg * F * 2
+    traffic["algorithmic_bytes_per_launch"] = int(alg)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+    lines = [
+        "# gate/up projection GEMM (k_gemm<EPI_SWIGLU>) -- full 32-layer DCU step, batch 8, N=1024",
+        "",
+        "Kernel trace command (run from the repository root):",
+        "",
+        "    " + cmds[0],
+        "",
+        f"Timed-region launches (last {steps} steps x {L} layers = {len(durs)} launches):",
+        f"  rocprofv3 average duration  {avg_us:9.2f} us",
+        f"  bench.py HIP-event average  {bj['roofline']['avg_launch_us']:9.2f} us",
+        f"  algorithmic flops / launch  {bj['roofline']['algorithmic_flops_per_launch']:.4e}",
+        f"  achieved (bench)            {bj['roofline']['achieved']} TFLOP/s of {bj['roofline']['peak']}",
+        "",
+        "Counter runs:",
+        "",
+        "    " + cmds[1],
+        "    " + cmds[2],
+        "",
+        f"  FETCH_SIZE per launch {f_k:12.1f} KiB; 1 GiB copy reads as {f_cp:12.1f} KiB (scale {f_scale:.4f})",
+        f"  WRITE_SIZE per launch {w_k:12.1f} KiB; 1 GiB copy writes as {w_cp:12.1f} KiB (scale {w_scale:.4f})",
+        f"  traffic per launch    {(fetch_b + write_b) / 1e6:9.1f} MB (fetch {fetch_b / 1e6:.1f}, write {write_b / 1e6:.1f})",
+        f"  algorithmic per launch {alg / 1e6:8.1f} MB (weights 2*F*d*2 B + rows read and written)",
+        "",
+        "Whole-run kernel statistics (includes setup: weight generation, dense cache fill, warm-up):",
+        "",
+        f"  {'kernel':90s} {'calls':>6s} {'avg us':>10s} {'pct':>6s}",
+    ]
+    for r in stats[:16]:
+        lines.append(f"  {r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}")
+    out = os.path.join(ROOT, "profiles", "gemm_gate_up_swiglu_full_step_b8_n1024.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        a = sys.argv[2:]
+        summarize_profiles(a[0], a[1], a[2], a[3], int(a[4]), a[5:8])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
