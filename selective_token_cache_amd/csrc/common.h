@@ -15,15 +15,16 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf_to_f(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// round to nearest even; inputs are finite
-__device__ __forceinline__ uint32_t f_to_bf_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f_to_bf_bits(lo) | (f_to_bf_bits(hi) << 16);
+  const bf16x2_t b = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
 }
+// fp32 -> bf16 bit pattern, round to nearest even
+__device__ __forceinline__ uint32_t f_to_bf_bits(float f) { return pack_bf2(f, 0.0f) & 0xffffu; }
 
 // ---------------------------------------------------------------------------- streaming loads
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

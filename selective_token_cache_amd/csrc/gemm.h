@@ -121,13 +121,15 @@ struct GateUpRows {
 };
 
 // Main loop over one tile. acc is [FM][FN] f32x4. Buffers b0..b3 are the stage arrays.
+// K-tiles [kt0, kt1) of the tile (all of K when kt1 < 0).
 template <class C, class WRows>
 __device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C::FN], const uint16_t* A,
                                               int M, int K, int m0, int n_t, const WRows& wr,
-                                              u32x4* b0, u32x4* b1, u32x4* b2, u32x4* b3) {
+                                              u32x4* b0, u32x4* b1, u32x4* b2, u32x4* b3,
+                                              int kt0 = 0, int kt1 = -1) {
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
   const int wm = wid / C::WGN, wn = wid % C::WGN;
-  const int KT = K / C::BK;
+  const int KT = (kt1 < 0 ? K / C::BK : kt1) - kt0;
   // per-lane global source rows of this wave's DMA instructions
   const uint16_t* src[C::NQ];
 #pragma unroll
@@ -144,7 +146,7 @@ __device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C:
     } else {
       base = wr.template row<C::BN>(n_t, row - C::BM, K);
     }
-    src[i] = base + c * 8;
+    src[i] = base + c * 8 + kt0 * C::BK;
   }
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)

@@ -175,7 +175,33 @@ struct GemmArgs {
   float* a;             // RESID: out; DOWN: residual in
   uint16_t* h;          // SWIGLU: out [M, F]
   uint16_t* y;          // DOWN: scatter target
+  float* part;          // RESID / DOWN: split-K partial sums [kMaxSplitK, part_rows, Nout], or null
+  int part_rows;        // min(row capacity, kSplitRowsMax)
 };
+
+// Split-K for the projections with few output tiles (output and down projections, Nout = d): when
+// the tiles alone leave workgroup slots idle, each tile's K range is cut into S segments whose fp32
+// partial sums go to the workspace; k_splitk_epilogue then sums them in fixed order and applies the
+// residual / scatter epilogue (deterministic, no atomics). S is a function of the row count on the
+// device, so the host needs only an upper bound for the workspace.
+constexpr int kMaxSplitK = 4;
+constexpr int kSplitRowsMax = 2048;
+
+__host__ __device__ inline int choose_splitk(int tiles, int slots, int KT, int M) {
+  if (M > kSplitRowsMax || tiles >= slots) return 1;
+  int best = 1;
+  float best_cost = 1.0f;
+  for (int S = 2; S <= kMaxSplitK; ++S) {
+    if (KT / S < 8) break;
+    const int rounds = (tiles * S + slots - 1) / slots;
+    const float cost = float(rounds) / float(S);
+    if (cost < best_cost - 1e-6f) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 // Tile shapes: 256x256 with 8 waves (128x64 each) where the output has many columns and M is large
 // enough; 128x128 with 4 waves (64x64 each, two workgroups per CU) otherwise.
@@ -258,11 +284,72 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
     wr = Rows{g.W, g.Nout};
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
-  int m_t, n_t;
-  for (int round = 0; gemm::next_tile(round, MT * NT, MT, &m_t, &n_t); ++round) {
+  const int KT = g.K / C::BK;
+  const int S = (EPI == EPI_RESID || EPI == EPI_DOWN) && g.part
+                    ? choose_splitk(MT * NT, gridDim.x, KT, M) : 1;
+  int unit, seg;
+  for (int round = 0; gemm::next_tile(round, MT * NT * S, MT * S, &unit, &seg); ++round) {
+    // unit = m_t * S + segment (consecutive units share the weight tile), seg = n_t
+    const int m_t = unit / S, s = unit % S, n_t = seg;
     gemm::f32x4 acc[C::FM][C::FN];
-    gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3);
-    gemm_epilogue<EPI, C>(g, acc, M, m_t * C::BM, n_t);
+    const int kt0 = KT * s / S, kt1 = KT * (s + 1) / S;
+    gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
+    if (S == 1) {
+      gemm_epilogue<EPI, C>(g, acc, M, m_t * C::BM, n_t);
+    } else {
+      const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+      const int wm = wid / C::WGN, wn = wid % C::WGN;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        const int m = m_t * C::BM + wm * C::WM + fm * 16 + (lane & 15);
+        if (m >= M) continue;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const int n = n_t * C::BN + wn * C::WN + fn * 16 + (lane >> 4) * 4;
+          if (n >= g.Nout) continue;
+          *reinterpret_cast<float4*>(g.part + (int64_t(s) * g.part_rows + m) * g.Nout + n) =
+              make_float4(acc[fm][fn][0], acc[fm][fn][1], acc[fm][fn][2], acc[fm][fn][3]);
+        }
+      }
+    }
+  }
+}
+
+// Sum of the split-K partials in segment order, then the RESID or DOWN epilogue; 4 columns per
+// thread. Exits at once when the GEMM did not split.
+template <int EPI, class C>
+__global__ __launch_bounds__(256) void k_splitk_epilogue(GemmArgs g, int slots) {
+  const int M = g.hdr[kHdrM];
+  const int MT = (M + C::BM - 1) / C::BM;
+  const int NT = (g.Nout + C::BN - 1) / C::BN;
+  const int S = choose_splitk(MT * NT, slots, g.K / C::BK, M);
+  if (S == 1) return;
+  const int q4 = g.Nout / 4;
+  const int64_t total = int64_t(M) * q4;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int m = int(i / q4), n = int(i % q4) * 4;
+    float4 v = *reinterpret_cast<const float4*>(g.part + int64_t(m) * g.Nout + n);
+    for (int s = 1; s < S; ++s) {
+      const float4 p =
+          *reinterpret_cast<const float4*>(g.part + (int64_t(s) * g.part_rows + m) * g.Nout + n);
+      v.x += p.x;
+      v.y += p.y;
+      v.z += p.z;
+      v.w += p.w;
+    }
+    const int64_t grow = int64_t(g.rowmap[m]);
+    if constexpr (EPI == EPI_RESID) {
+      const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+      *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
+          make_float4(bf_lo(xr.x) + v.x, bf_hi(xr.x) + v.y, bf_lo(xr.y) + v.z, bf_hi(xr.y) + v.w);
+    } else {
+      const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+      uint2 st;
+      st.x = pack_bf2(ar.x + v.x, ar.y + v.y);
+      st.y = pack_bf2(ar.z + v.z, ar.w + v.w);
+      *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+    }
   }
 }
 
@@ -271,7 +358,10 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
 // owning 16 queries. S^T = K Q^T is computed with the key block as the MFMA A operand, so a lane
 // holds 4 keys x 1 query per fragment; that register layout is exactly the B operand that
 // O^T = V^T P^T needs (keys permuted consistently on both sides), so P never leaves registers.
-// K is staged in XOR-swizzled LDS, V transposed (V^T, padded rows) in LDS.
+// K and V blocks of 64 keys stream global -> LDS by DMA through kAttnStages distinct buffers (row
+// layout, 16-byte chunk swizzle c ^ (key & (CH-1))), so global latency is hidden behind the blocks
+// being consumed. Each V block is then transposed inside LDS into a padded V^T tile (pairs of keys
+// packed into 32-bit words), from which the V^T operand is read with two 8-byte loads per fragment.
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kc;
@@ -287,17 +377,34 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
-constexpr int kKB = 64;           // keys per block
+constexpr int kKB = 64;             // keys per block
+constexpr int kAttnStages = 3;      // LDS stages of (K, V) blocks
 constexpr int kVTStride = kKB + 4;  // padded V^T row (bf16 elements)
+
+template <int CH>
+__device__ __forceinline__ int kswz(int key, int c) { return key * CH + (c ^ (key & (CH - 1))); }
 
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
-  constexpr int CH = DH / 8;  // 16-byte chunks per head row
-  __shared__ u32x4 smK[kKB * CH];
+  constexpr int CH = DH / 8;            // 16-byte chunks per head row
+  constexpr int BLK = kKB * CH;         // chunks per K (or V) block
+  constexpr int NQ = BLK / 64 / 4;      // DMA instructions per wave per block, per operand
+  static_assert(NQ >= 1, "block size");
+  __shared__ u32x4 k0[BLK], k1[BLK], k2[BLK];
+  __shared__ u32x4 v0[BLK], v1[BLK], v2[BLK];
   __shared__ uint16_t smVT[DH * kVTStride];
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6, grp = lane >> 4, col = lane & 15;
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   const int Tq = g.hdr[kHdrTq];
   const int items = Tq * g.H * g.splits;
+  // per-lane (row, logical chunk) of this wave's DMA instructions
+  int drow[NQ], dcol[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int p = (i * 4 + wid) * 64 + lane;
+    drow[i] = p / CH;
+    dcol[i] = (p % CH) ^ (drow[i] & (CH - 1));
+  }
   for (int w = blockIdx.x; w < items; w += gridDim.x) {
     const int split = w % g.splits;
     const int h = (w / g.splits) % g.H;
@@ -307,6 +414,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
     const int rend = g.seq_off[b + 1];
     const int kbeg = split * g.kps;
     const int kend = min(g.N, kbeg + g.kps);
+    const int nblk = (kend - kbeg + kKB - 1) / kKB;
     // this wave's 16 queries; lane column `col` is its query
     int qr = r0 + wid * 16 + col;
     const bool qvalid = qr < rend;
@@ -320,35 +428,52 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
 #pragma unroll
     for (int i = 0; i < DH / 16; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_part = 0.0f;
-    const int64_t cache_base = int64_t(b) * g.N;
+    const uint16_t* kbase = g.kc + int64_t(b) * g.N * g.d + h * DH;
+    const uint16_t* vbase = g.vc + int64_t(b) * g.N * g.d + h * DH;
 
-    for (int kb0 = kbeg; kb0 < kend; kb0 += kKB) {
-      __syncthreads();  // previous block's LDS reads are done
-      // K block -> swizzled LDS
-      for (int qd = t; qd < kKB * CH; qd += 256) {
-        const int key = qd / CH, c = qd % CH;
-        int kg = kb0 + key;
-        kg = kg < kend ? kg : kend - 1;
-        smK[key * CH + (c ^ (key & (CH - 1)))] =
-            ld16(g.kc + (cache_base + kg) * g.d + h * DH + c * 8);
+    auto issue = [&](auto sidx, int j) {
+      constexpr int S = decltype(sidx)::value;
+      u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
+      u32x4* vb = S == 0 ? v0 : (S == 1 ? v1 : v2);
+      const int jj = j < nblk ? j : nblk - 1;
+      const int key0 = kbeg + jj * kKB;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) {
+        int key = key0 + drow[i];
+        key = key < kend ? key : kend - 1;
+        const int64_t off = int64_t(key) * g.d + dcol[i] * 8;
+        const uint32_t lo = uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(kb + (i * 4 + wid_s) * 64)));
+        const uint32_t lv = uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(vb + (i * 4 + wid_s) * 64)));
+        gemm::dma16(kbase + off, lo);
+        gemm::dma16(vbase + off, lv);
       }
-      // V block -> V^T: thread takes keys (2kp, 2kp+1) x 8 head dims
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // V block (row layout) -> V^T tile: thread takes keys (2kp, 2kp+1) x 8 head dims
+    auto transpose_v = [&](auto sidx) {
+      constexpr int S = decltype(sidx)::value;
+      const u32x4* vb = S == 0 ? v0 : (S == 1 ? v1 : v2);
+#pragma unroll
       for (int qd = t; qd < (kKB / 2) * CH; qd += 256) {
         const int kp = qd & 31, dc = qd >> 5;
-        int k0 = kb0 + 2 * kp, k1 = k0 + 1;
-        k0 = k0 < kend ? k0 : kend - 1;
-        k1 = k1 < kend ? k1 : kend - 1;
-        const u32x4 v0 = ld16(g.vc + (cache_base + k0) * g.d + h * DH + dc * 8);
-        const u32x4 v1 = ld16(g.vc + (cache_base + k1) * g.d + h * DH + dc * 8);
+        const u32x4 a = vb[kswz<CH>(2 * kp, dc)];
+        const u32x4 c = vb[kswz<CH>(2 * kp + 1, dc)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = (v0[j] & 0xffffu) | (v1[j] << 16);
-          const uint32_t hi = (v0[j] >> 16) | (v1[j] & 0xffff0000u);
+          const uint32_t lo = (a[j] & 0xffffu) | (c[j] << 16);
+          const uint32_t hi = (a[j] >> 16) | (c[j] & 0xffff0000u);
           *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j) * kVTStride + 2 * kp]) = lo;
           *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j + 1) * kVTStride + 2 * kp]) = hi;
         }
       }
-      __syncthreads();
+    };
+
+    auto compute = [&](auto sidx, int j) {
+      constexpr int S = decltype(sidx)::value;
+      const u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
+      const int kb0 = kbeg + j * kKB;
       // S^T for 64 keys x 16 queries: 4 fragments (keys 16f + 4*grp + i)
       f32x4 s[4];
 #pragma unroll
@@ -356,10 +481,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
         s[f] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = f * 16 + col;
 #pragma unroll
-        for (int kk = 0; kk < DH / 32; ++kk) {
-          const int c = kk * 4 + grp;
-          s[f] = mfma16x16x32(smK[key * CH + (c ^ (key & (CH - 1)))], qf[kk], s[f]);
-        }
+        for (int kk = 0; kk < DH / 32; ++kk)
+          s[f] = mfma16x16x32(kb[kswz<CH>(key, kk * 4 + grp)], qf[kk], s[f]);
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -406,7 +529,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
           acc_o[df] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc_o[df]);
         }
       }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    auto iter = [&](auto cur, int j) {
+      constexpr int S = decltype(cur)::value;
+      constexpr int NXT = (S + kAttnStages - 1) % kAttnStages;
+      gemm::wait_vm_lgkm0<(kAttnStages - 2) * 2 * NQ>();
+      __builtin_amdgcn_s_barrier();  // block j has landed; the previous block is fully consumed
+      issue(std::integral_constant<int, NXT>{}, j + kAttnStages - 1);
+      transpose_v(cur);
+      constexpr int kInFlight = (kAttnStages - 1) * 2 * NQ;  // DMA groups j+1 .. j+STAGES-1
+      gemm::wait_vm_lgkm0<kInFlight>();                        // only the LDS writes above
+      __builtin_amdgcn_s_barrier();  // V^T of block j is complete
+      compute(cur, j);
+    };
+    if (nblk > 0) {
+      issue(I0{}, 0);
+      issue(I1{}, 1);
+      for (int j = 0; j < nblk; j += kAttnStages) {
+        iter(I0{}, j);
+        if (j + 1 < nblk) iter(I1{}, j + 1); else break;
+        if (j + 2 < nblk) iter(I2{}, j + 2); else break;
+      }
+      gemm::wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
     }
+
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
     if (qvalid) {
@@ -467,8 +618,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH) {
 constexpr int kCUs = 256;
 
 struct Layout {
-  int M_cap, Tq_max, splits, kps;
-  size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, opart, ml, total;
+  int M_cap, Tq_max, splits, kps, part_rows;
+  size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -487,8 +638,8 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
     splits = splits < max_splits ? splits : max_splits;
     splits = splits < 1 ? 1 : splits;
   }
-  L.splits = splits;
   L.kps = ((N + splits - 1) / splits + kKB - 1) / kKB * kKB;
+  L.splits = (N + L.kps - 1) / L.kps;  // every split starts below N
   const size_t d = size_t(w->d), F = size_t(w->ffn), M = size_t(L.M_cap);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -506,6 +657,8 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   L.o = take(2 * M * d);
   L.a = take(4 * M * d);
   L.h = take(2 * M * F);
+  L.part_rows = L.M_cap < kSplitRowsMax ? L.M_cap : kSplitRowsMax;
+  L.part = take(4 * size_t(kMaxSplitK) * L.part_rows * d);
   if (splits > 1) {
     L.opart = take(4 * size_t(splits) * M * d);
     L.ml = take(4 * size_t(splits) * M * w->n_heads * 2);
@@ -539,9 +692,30 @@ int gemm_grid(int M_cap, int NT) {
   return int(gsz < 8 ? 8 : gsz);
 }
 
+// Workgroup slots of the persistent grid: resident workgroups when the tiles of the largest possible
+// row count fill them, otherwise enough slots for every tile, or for every split-K segment when the
+// kernel may split (the split count is then chosen on the device from the actual row count).
+template <class C>
+int gemm_grid_slots(int EPI, int M_cap, int NT) {
+  const int per_cu = C::NW == 4 ? 2 : 1;  // LDS: 64 KB (4 waves) or 128 KB (8 waves) per workgroup
+  const int resident = per_cu * kCUs;
+  if (EPI == EPI_RESID || EPI == EPI_DOWN) return resident;
+  return gemm_grid<C>(M_cap, NT);
+}
+
 template <int EPI, class C>
 void launch_gemm(const GemmArgs& ga, int M_cap, int NT, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<EPI, C>), dim3(gemm_grid<C>(M_cap, NT)), dim3(C::THREADS), 0, s, ga);
+  hipLaunchKernelGGL((k_gemm<EPI, C>), dim3(gemm_grid_slots<C>(EPI, M_cap, NT)), dim3(C::THREADS),
+                     0, s, ga);
+}
+
+template <int EPI, class C>
+void launch_splitk_epilogue(const GemmArgs& ga, int M_cap, int NT, hipStream_t s) {
+  const int slots = gemm_grid_slots<C>(EPI, M_cap, NT);
+  const int64_t work = int64_t(M_cap < kSplitRowsMax ? M_cap : kSplitRowsMax) * (ga.Nout / 4);
+  const int blocks = int((work + 255) / 256 < 2048 ? (work + 255) / 256 : 2048);
+  hipLaunchKernelGGL((k_splitk_epilogue<EPI, C>), dim3(blocks < 1 ? 1 : blocks), dim3(256), 0, s, ga,
+                     slots);
 }
 
 // Rows above which the wide-output GEMMs (QKV, gate/up) use the 256x256 tile.
@@ -652,7 +826,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.M_cap = L.M_cap;
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   const int64_t items = int64_t(L.Tq_max) * H * L.splits;
-  const int attn_blocks = int(items < 4 * kCUs ? items : 4 * kCUs);
+  const int attn_blocks = int(items < 2 * kCUs ? items : 2 * kCUs);
   if (DH == 128)
     hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
   else if (DH == 64)
@@ -675,7 +849,11 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.Nout = d;
   ga.x = x;
   ga.a = P.a;
+  ga.part = reinterpret_cast<float*>(ws + L.part);
+  ga.part_rows = L.part_rows;
   launch_gemm<EPI_RESID, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  DCU_LAUNCH_CHECK();
+  launch_splitk_epilogue<EPI_RESID, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -708,6 +886,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(y_out);
   launch_gemm<EPI_DOWN, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  DCU_LAUNCH_CHECK();
+  launch_splitk_epilogue<EPI_DOWN, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   return DCU_OK;

@@ -99,6 +99,8 @@ def _random_selection(g, B, N, counts):
     (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 3, 200, [130, 1, 0]),
     (synth.LayerShape(d=512, n_heads=4, head_dim=128, ffn=768), 2, 300, [64, 257]),
     (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 4, 77, [77, 5, 33, 64]),
+    # K long enough for the split-K path of the output (K = 1024) and down (K = 2048) projections
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 2, 256, [100, 37]),
 ])
 def test_selective_layer_small_shapes(shape, B, N, counts):
     _log(f"layer d={shape.d} H={shape.n_heads} dh={shape.head_dim} F={shape.ffn} B={B} N={N}")
