@@ -175,37 +175,51 @@ struct GemmArgs {
   float* a;             // RESID: out; DOWN: residual in
   uint16_t* h;          // SWIGLU: out [M, F]
   uint16_t* y;          // DOWN: scatter target
-  float* part;          // RESID / DOWN: split-K partial sums [kMaxSplitK, part_rows, Nout], or null
-  int part_rows;        // min(row capacity, kSplitRowsMax)
+  float* part;          // split tail partial tiles [2 * grid, BM * BN] fp32
 };
 
-// Split-K for the projections with few output tiles (output and down projections, Nout = d): when
-// the tiles alone leave workgroup slots idle, each tile's K range is cut into S segments whose fp32
-// partial sums go to the workspace; k_splitk_epilogue then sums them in fixed order and applies the
-// residual / scatter epilogue (deterministic, no atomics). S is a function of the row count on the
-// device, so the host needs only an upper bound for the workspace.
+// Tail splitting: with a persistent grid of G workgroup slots and T output tiles, the last round holds
+// T mod G tiles and leaves the other slots idle. Those tail tiles (all tiles when T < G) are cut
+// along K into S segments whose fp32 partial tiles go to the workspace; k_gemm_fixup sums them in
+// segment order and applies the epilogue (deterministic, no atomics). S depends on the row count, so
+// it is chosen on the device; kernel and fixup evaluate the same function.
 constexpr int kMaxSplitK = 4;
-constexpr int kSplitRowsMax = 2048;
 
-__host__ __device__ inline int choose_splitk(int tiles, int slots, int KT, int M) {
-  if (M > kSplitRowsMax || tiles >= slots) return 1;
-  int best = 1;
-  float best_cost = 1.0f;
-  for (int S = 2; S <= kMaxSplitK; ++S) {
-    if (KT / S < 8) break;
-    const int rounds = (tiles * S + slots - 1) / slots;
-    const float cost = float(rounds) / float(S);
-    if (cost < best_cost - 1e-6f) {
-      best = S;
-      best_cost = cost;
+struct SplitPlan {
+  int full;  // tiles computed whole (ids 0 .. full-1)
+  int rem;   // tail tiles (ids full .. full+rem-1), each in S segments
+  int S;
+};
+
+__host__ __device__ inline SplitPlan plan_split(int T, int G, int KT) {
+  SplitPlan p{T, 0, 1};
+  if (T <= 0) return p;
+  if (T < G) {
+    // every tile: pick S minimising rounds / S with at most 2 rounds of units
+    float best = 1.0f;
+    for (int S = 2; S <= kMaxSplitK; ++S) {
+      if (KT / S < 8 || T * S > 2 * G) break;
+      const float cost = float((T * S + G - 1) / G) / float(S);
+      if (cost < best - 1e-6f) {
+        best = cost;
+        p.S = S;
+      }
     }
+    if (p.S > 1) p = SplitPlan{0, T, p.S};
+    return p;
   }
-  return best;
+  const int rem = T % G;
+  if (rem == 0 || 2 * rem > G) return p;
+  int S = G / rem;
+  S = S < kMaxSplitK ? S : kMaxSplitK;
+  while (S > 1 && KT / S < 8) --S;
+  if (S > 1) p = SplitPlan{T - rem, rem, S};
+  return p;
 }
 
-// Tile shapes: 256x256 with 8 waves (128x64 each) where the output has many columns and M is large
-// enough; 128x128 with 4 waves (64x64 each, two workgroups per CU) otherwise.
-using CfgBig = gemm::Cfg<256, 256, 128, 64, 2, 8>;
+// Tile shape: 128x128 with 4 waves (64x64 each), two workgroups per CU. (A 256x256 tile with 8 waves
+// is faster on the dense shape in isolation but exceeds the 256 registers per wave with the fused
+// epilogues and spills.)
 using CfgSmall = gemm::Cfg<128, 128, 64, 64, 2, 4>;
 
 template <int EPI, class C>
@@ -285,29 +299,37 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
   const int KT = g.K / C::BK;
-  const int S = (EPI == EPI_RESID || EPI == EPI_DOWN) && g.part
-                    ? choose_splitk(MT * NT, gridDim.x, KT, M) : 1;
-  int unit, seg;
-  for (int round = 0; gemm::next_tile(round, MT * NT * S, MT * S, &unit, &seg); ++round) {
-    // unit = m_t * S + segment (consecutive units share the weight tile), seg = n_t
-    const int m_t = unit / S, s = unit % S, n_t = seg;
+  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT);
+  const int units = sp.full + sp.rem * sp.S;
+  int lin, zero;
+  for (int round = 0; gemm::next_tile(round, units, units, &lin, &zero); ++round) {
+    int tile, s = 0, kt0 = 0, kt1 = KT;
+    if (lin < sp.full) {
+      tile = lin;
+    } else {
+      const int v = lin - sp.full;
+      tile = sp.full + v / sp.S;
+      s = v % sp.S;
+      kt0 = KT * s / sp.S;
+      kt1 = KT * (s + 1) / sp.S;
+    }
+    const int m_t = tile % MT, n_t = tile / MT;  // consecutive tiles share the weight tile
     gemm::f32x4 acc[C::FM][C::FN];
-    const int kt0 = KT * s / S, kt1 = KT * (s + 1) / S;
     gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
-    if (S == 1) {
+    if (lin < sp.full) {
       gemm_epilogue<EPI, C>(g, acc, M, m_t * C::BM, n_t);
     } else {
+      // tile-local partial: [BM rows][BN weight rows of the tile]
       const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
       const int wm = wid / C::WGN, wn = wid % C::WGN;
+      float* pt = g.part + int64_t(lin - sp.full) * (C::BM * C::BN);
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
-        const int m = m_t * C::BM + wm * C::WM + fm * 16 + (lane & 15);
-        if (m >= M) continue;
+        const int r = wm * C::WM + fm * 16 + (lane & 15);
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
-          const int n = n_t * C::BN + wn * C::WN + fn * 16 + (lane >> 4) * 4;
-          if (n >= g.Nout) continue;
-          *reinterpret_cast<float4*>(g.part + (int64_t(s) * g.part_rows + m) * g.Nout + n) =
+          const int c = wn * C::WN + fn * 16 + (lane >> 4) * 4;
+          *reinterpret_cast<float4*>(pt + r * C::BN + c) =
               make_float4(acc[fm][fn][0], acc[fm][fn][1], acc[fm][fn][2], acc[fm][fn][3]);
         }
       }
@@ -315,40 +337,73 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
   }
 }
 
-// Sum of the split-K partials in segment order, then the RESID or DOWN epilogue; 4 columns per
+// Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
 // thread. Exits at once when the GEMM did not split.
 template <int EPI, class C>
-__global__ __launch_bounds__(256) void k_splitk_epilogue(GemmArgs g, int slots) {
+__global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   const int M = g.hdr[kHdrM];
+  if (M <= 0) return;
   const int MT = (M + C::BM - 1) / C::BM;
-  const int NT = (g.Nout + C::BN - 1) / C::BN;
-  const int S = choose_splitk(MT * NT, slots, g.K / C::BK, M);
-  if (S == 1) return;
-  const int q4 = g.Nout / 4;
-  const int64_t total = int64_t(M) * q4;
+  const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
+  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK);
+  if (sp.rem == 0) return;
+  constexpr int OUTC = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;  // output columns per tile
+  constexpr int Q = C::BM * OUTC / 4;                          // float4 groups per tile
+  const int64_t total = int64_t(sp.rem) * Q;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * blockDim.x) {
-    const int m = int(i / q4), n = int(i % q4) * 4;
-    float4 v = *reinterpret_cast<const float4*>(g.part + int64_t(m) * g.Nout + n);
-    for (int s = 1; s < S; ++s) {
-      const float4 p =
-          *reinterpret_cast<const float4*>(g.part + (int64_t(s) * g.part_rows + m) * g.Nout + n);
-      v.x += p.x;
-      v.y += p.y;
-      v.z += p.z;
-      v.w += p.w;
-    }
-    const int64_t grow = int64_t(g.rowmap[m]);
-    if constexpr (EPI == EPI_RESID) {
-      const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
-      *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
-          make_float4(bf_lo(xr.x) + v.x, bf_hi(xr.x) + v.y, bf_lo(xr.y) + v.z, bf_hi(xr.y) + v.w);
-    } else {
-      const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+    const int tt = int(i / Q), q = int(i % Q);
+    const int r = q / (OUTC / 4), c4 = (q % (OUTC / 4)) * 4;
+    const int tile = sp.full + tt;
+    const int m_t = tile % MT, n_t = tile / MT;
+    const int m = m_t * C::BM + r;
+    if (m >= M) continue;
+    const float* pt = g.part + int64_t(tt) * sp.S * (C::BM * C::BN);
+    if constexpr (EPI == EPI_SWIGLU) {
+      // output column c4..c4+3 of the tile = wave column wn, within-wave columns w..w+3
+      const int wn = c4 / (C::WN / 2), w = c4 % (C::WN / 2);
+      const int cg = wn * C::WN + w, cu = cg + C::WN / 2;
+      float4 gt = *reinterpret_cast<const float4*>(pt + r * C::BN + cg);
+      float4 up = *reinterpret_cast<const float4*>(pt + r * C::BN + cu);
+      for (int s2 = 1; s2 < sp.S; ++s2) {
+        const float* ps = pt + int64_t(s2) * (C::BM * C::BN) + r * C::BN;
+        const float4 a = *reinterpret_cast<const float4*>(ps + cg);
+        const float4 b = *reinterpret_cast<const float4*>(ps + cu);
+        gt.x += a.x; gt.y += a.y; gt.z += a.z; gt.w += a.w;
+        up.x += b.x; up.y += b.y; up.z += b.z; up.w += b.w;
+      }
+      const int j = n_t * (C::BN / 2) + c4;
       uint2 st;
-      st.x = pack_bf2(ar.x + v.x, ar.y + v.y);
-      st.y = pack_bf2(ar.z + v.z, ar.w + v.w);
-      *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+      st.x = pack_bf2(gt.x / (1.0f + __expf(-gt.x)) * up.x, gt.y / (1.0f + __expf(-gt.y)) * up.y);
+      st.y = pack_bf2(gt.z / (1.0f + __expf(-gt.z)) * up.z, gt.w / (1.0f + __expf(-gt.w)) * up.w);
+      *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
+    } else {
+      const int n = n_t * C::BN + c4;
+      if (n >= g.Nout) continue;
+      float4 v = *reinterpret_cast<const float4*>(pt + r * C::BN + c4);
+      for (int s2 = 1; s2 < sp.S; ++s2) {
+        const float4 a = *reinterpret_cast<const float4*>(pt + int64_t(s2) * (C::BM * C::BN) + r * C::BN + c4);
+        v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+      }
+      const int64_t grow = int64_t(g.rowmap[m]);
+      if constexpr (EPI == EPI_QKV) {
+        uint2 st;
+        st.x = pack_bf2(v.x, v.y);
+        st.y = pack_bf2(v.z, v.w);
+        const int part = n / g.d, col = n - part * g.d;
+        uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
+        *reinterpret_cast<uint2*>(dst + col) = st;
+      } else if constexpr (EPI == EPI_RESID) {
+        const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+        *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
+            make_float4(bf_lo(xr.x) + v.x, bf_hi(xr.x) + v.y, bf_lo(xr.y) + v.z, bf_hi(xr.y) + v.w);
+      } else {  // EPI_DOWN
+        const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+        uint2 st;
+        st.x = pack_bf2(ar.x + v.x, ar.y + v.y);
+        st.y = pack_bf2(ar.z + v.z, ar.w + v.w);
+        *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+      }
     }
   }
 }
@@ -428,25 +483,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
 #pragma unroll
     for (int i = 0; i < DH / 16; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_part = 0.0f;
-    const uint16_t* kbase = g.kc + int64_t(b) * g.N * g.d + h * DH;
-    const uint16_t* vbase = g.vc + int64_t(b) * g.N * g.d + h * DH;
+    // per-lane source offsets of block 0 (elements from the sequence/head base); full blocks
+    // advance by 64 rows, the ragged last block clamps its rows to the last valid key
+    const int64_t head_base = int64_t(b) * g.N * g.d + h * DH;
+    int64_t doff[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) doff[i] = int64_t(kbeg + drow[i]) * g.d + dcol[i] * 8;
+    const int64_t blk_step = int64_t(kKB) * g.d;
 
     auto issue = [&](auto sidx, int j) {
       constexpr int S = decltype(sidx)::value;
       u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
       u32x4* vb = S == 0 ? v0 : (S == 1 ? v1 : v2);
       const int jj = j < nblk ? j : nblk - 1;
-      const int key0 = kbeg + jj * kKB;
+      const bool full = kbeg + (jj + 1) * kKB <= kend;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
-        int key = key0 + drow[i];
-        key = key < kend ? key : kend - 1;
-        const int64_t off = int64_t(key) * g.d + dcol[i] * 8;
+        int64_t off;
+        if (full) {
+          off = head_base + doff[i] + jj * blk_step;
+        } else {
+          int key = kbeg + jj * kKB + drow[i];
+          key = key < kend ? key : kend - 1;
+          off = head_base + int64_t(key) * g.d + dcol[i] * 8;
+        }
         const uint32_t lo = uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(kb + (i * 4 + wid_s) * 64)));
         const uint32_t lv = uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(vb + (i * 4 + wid_s) * 64)));
-        gemm::dma16(kbase + off, lo);
-        gemm::dma16(vbase + off, lv);
+        gemm::dma16(g.kc + off, lo);
+        gemm::dma16(g.vc + off, lv);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -484,21 +549,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
         for (int kk = 0; kk < DH / 32; ++kk)
           s[f] = mfma16x16x32(kb[kswz<CH>(key, kk * 4 + grp)], qf[kk], s[f]);
       }
+      // raw scores; the scale log2(e)/sqrt(dh) > 0 is applied inside exp2 (fma), and only the
+      // ragged last block masks keys past the end
+      if (kb0 + kKB > kend) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb0 + f * 16 + grp * 4 + i >= kend) s[f][i] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + f * 16 + grp * 4 + i;
-          const float v = key < kend ? s[f][i] * g.scale_log2 : -INFINITY;
-          s[f][i] = v;
-          mx = v > mx ? v : mx;
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[f][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      mx *= g.scale_log2;
+      // lazy rescaling: the reference max only moves when a score exceeds it by more than 2^8, so
+      // exp2(score - m_ref) <= 256 and the accumulators are rescaled rarely (exact after the final
+      // division by the same-referenced sum)
+      const bool grow = mx > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int df = 0; df < DH / 16; ++df) acc_o[df] *= alpha;
+      }
       float psum = 0.0f;
       uint32_t pk[4][2];
 #pragma unroll
@@ -506,15 +585,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s[f][i] - m_new);
+          p[i] = __builtin_amdgcn_exp2f(fmaf(s[f][i], g.scale_log2, -m_run));
           psum += p[i];
         }
         pk[f][0] = pack_bf2(p[0], p[1]);
         pk[f][1] = pack_bf2(p[2], p[3]);
       }
-      l_part = l_part * alpha + psum;
-#pragma unroll
-      for (int df = 0; df < DH / 16; ++df) acc_o[df] *= alpha;
+      l_part += psum;
       // O^T += V^T P^T over two 32-key chunks; MFMA k index 8*grp + j maps to key
       // 32c + 4*grp + j (j < 4) and 32c + 16 + 4*grp + (j - 4) (j >= 4)
 #pragma unroll
@@ -618,7 +695,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH) {
 constexpr int kCUs = 256;
 
 struct Layout {
-  int M_cap, Tq_max, splits, kps, part_rows;
+  int M_cap, Tq_max, splits, kps;
   size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, total;
 };
 
@@ -657,8 +734,8 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   L.o = take(2 * M * d);
   L.a = take(4 * M * d);
   L.h = take(2 * M * F);
-  L.part_rows = L.M_cap < kSplitRowsMax ? L.M_cap : kSplitRowsMax;
-  L.part = take(4 * size_t(kMaxSplitK) * L.part_rows * d);
+  // split tail partials: at most 2 * (resident workgroups) tile segments of 128 x 128 fp32
+  L.part = take(size_t(4) * 2 * (2 * kCUs) * CfgSmall::BM * CfgSmall::BN);
   if (splits > 1) {
     L.opart = take(4 * size_t(splits) * M * d);
     L.ml = take(4 * size_t(splits) * M * w->n_heads * 2);
@@ -683,43 +760,26 @@ int validate(const dcu_layer* w, int B, int N) {
   return DCU_OK;
 }
 
-template <class C>
-int gemm_grid(int M_cap, int NT) {
-  const int per_cu = C::NW == 4 ? 2 : 1;  // LDS: 64 KB (4 waves) or 128 KB (8 waves) per workgroup
-  const int64_t tiles = int64_t((M_cap + C::BM - 1) / C::BM) * NT;
-  int64_t gsz = tiles < int64_t(per_cu) * kCUs ? tiles : int64_t(per_cu) * kCUs;
-  gsz = (gsz + 7) / 8 * 8;
-  return int(gsz < 8 ? 8 : gsz);
-}
 
-// Workgroup slots of the persistent grid: resident workgroups when the tiles of the largest possible
-// row count fill them, otherwise enough slots for every tile, or for every split-K segment when the
-// kernel may split (the split count is then chosen on the device from the actual row count).
+// The persistent projection grids always hold the resident workgroup count, so that the tail of a
+// tile walk can be split over idle slots (the split plan is a function of the device row count).
 template <class C>
-int gemm_grid_slots(int EPI, int M_cap, int NT) {
+int gemm_slots() {
   const int per_cu = C::NW == 4 ? 2 : 1;  // LDS: 64 KB (4 waves) or 128 KB (8 waves) per workgroup
-  const int resident = per_cu * kCUs;
-  if (EPI == EPI_RESID || EPI == EPI_DOWN) return resident;
-  return gemm_grid<C>(M_cap, NT);
+  return per_cu * kCUs;
 }
 
 template <int EPI, class C>
-void launch_gemm(const GemmArgs& ga, int M_cap, int NT, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<EPI, C>), dim3(gemm_grid_slots<C>(EPI, M_cap, NT)), dim3(C::THREADS),
-                     0, s, ga);
+void launch_gemm(const GemmArgs& ga, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm<EPI, C>), dim3(gemm_slots<C>()), dim3(C::THREADS), 0, s, ga);
 }
 
 template <int EPI, class C>
-void launch_splitk_epilogue(const GemmArgs& ga, int M_cap, int NT, hipStream_t s) {
-  const int slots = gemm_grid_slots<C>(EPI, M_cap, NT);
-  const int64_t work = int64_t(M_cap < kSplitRowsMax ? M_cap : kSplitRowsMax) * (ga.Nout / 4);
-  const int blocks = int((work + 255) / 256 < 2048 ? (work + 255) / 256 : 2048);
-  hipLaunchKernelGGL((k_splitk_epilogue<EPI, C>), dim3(blocks < 1 ? 1 : blocks), dim3(256), 0, s, ga,
-                     slots);
+void launch_fixup(const GemmArgs& ga, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_fixup<EPI, C>), dim3(512), dim3(256), 0, s, ga, gemm_slots<C>());
 }
 
-// Rows above which the wide-output GEMMs (QKV, gate/up) use the 256x256 tile.
-constexpr int kBigTileRows = 512;
+
 
 }  // namespace
 }  // namespace dcu
@@ -785,6 +845,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   if (!mark()) return DCU_EHIP;
 
   GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(ws + L.part);
   ga.hdr = P.hdr;
   ga.rowmap = P.rowmap;
   ga.d = d;
@@ -796,13 +857,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.q = P.q;
   ga.kc = static_cast<uint16_t*>(k_cache);
   ga.vc = static_cast<uint16_t*>(v_cache);
-  // the 256x256 tile needs more than the 256 registers a wave of an 8-wave workgroup can hold once
-  // the epilogues are fused (it spills), so it stays disabled until its register use is reduced
-  const bool big = false && L.M_cap > kBigTileRows && F % (CfgBig::BN / 2) == 0;
-  if (big)
-    launch_gemm<EPI_QKV, CfgBig>(ga, L.M_cap, (3 * d + CfgBig::BN - 1) / CfgBig::BN, s);
-  else
-    launch_gemm<EPI_QKV, CfgSmall>(ga, L.M_cap, (3 * d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  launch_gemm<EPI_QKV, CfgSmall>(ga, s);
+  DCU_LAUNCH_CHECK();
+  launch_fixup<EPI_QKV, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -849,11 +906,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.Nout = d;
   ga.x = x;
   ga.a = P.a;
-  ga.part = reinterpret_cast<float*>(ws + L.part);
-  ga.part_rows = L.part_rows;
-  launch_gemm<EPI_RESID, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+
+  launch_gemm<EPI_RESID, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
-  launch_splitk_epilogue<EPI_RESID, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  launch_fixup<EPI_RESID, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -871,10 +927,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = d;
   ga.Nout = F;
   ga.h = P.h;
-  if (big)
-    launch_gemm<EPI_SWIGLU, CfgBig>(ga, L.M_cap, F / (CfgBig::BN / 2), s);
-  else
-    launch_gemm<EPI_SWIGLU, CfgSmall>(ga, L.M_cap, F / (CfgSmall::BN / 2), s);
+  launch_gemm<EPI_SWIGLU, CfgSmall>(ga, s);
+  DCU_LAUNCH_CHECK();
+  launch_fixup<EPI_SWIGLU, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -885,9 +940,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = F;
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(y_out);
-  launch_gemm<EPI_DOWN, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  launch_gemm<EPI_DOWN, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
-  launch_splitk_epilogue<EPI_DOWN, CfgSmall>(ga, L.M_cap, (d + CfgSmall::BN - 1) / CfgSmall::BN, s);
+  launch_fixup<EPI_DOWN, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   return DCU_OK;
