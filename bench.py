@@ -61,8 +61,7 @@ def stage_flops_bytes(M: int):
     return {
         "distance": dict(bytes=2 * B * N * D * w + B * N * 4),
         "select": dict(bytes=B * N * 4 + B * N * 4),
-        "plan": dict(bytes=B * N * 4),
-        "gather_rmsnorm": dict(bytes=2 * M * D * w),
+        "gather_rmsnorm": dict(bytes=2 * M * D * w + B * N * 4),
         "qkv_scatter": dict(flops=2 * M * 3 * D * D, bytes=3 * D * D * w + M * D * w + 3 * M * D * w),
         "attention": dict(flops=4 * M * N * D, bytes=B * 2 * N * D * w + 2 * M * D * w),
         "o_proj_residual": dict(flops=2 * M * D * D, bytes=D * D * w + 2 * M * D * w + M * D * 4),
@@ -70,6 +69,7 @@ def stage_flops_bytes(M: int):
         "gate_up_swiglu": dict(flops=2 * M * 2 * F * D, bytes=2 * F * D * w + M * D * w + M * F * w),
         "down_residual_scatter": dict(flops=2 * M * D * F,
                                       bytes=D * F * w + M * F * w + M * D * 4 + M * D * w),
+        "qkv_fixup": {}, "o_proj_fixup": {}, "gate_up_fixup": {}, "down_fixup": {},
     }
 
 

@@ -151,7 +151,8 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  * workspace device scratch of at least dcu_selective_layer_workspace() bytes (256-byte aligned).
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
  *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if head_dim not in {32, 64, 128}, d
- *         or ffn not a multiple of 64, N > 65536, B*N > 2^28, or a pointer not 16-byte aligned;
+ *         or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte
+ *         aligned;
  *         EWORKSPACE if the workspace is too small or not 256-byte aligned.
  */
 int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
@@ -163,13 +164,16 @@ int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel
  * dcu_selective_layer_staged -- dcu_selective_layer with per-stage timing marks, for measurement.
  * Identical work and results; additionally records the caller-created hipEvent_t events[0] before
  * the first kernel and events[i] after stage i on `stream`, for the DCU_LAYER_STAGES stages
- *   1 plan (row offsets and map), 2 gather + RMSNorm, 3 QKV projection + K/V scatter,
- *   4 attention (+ split combine), 5 output projection + residual, 6 RMSNorm,
- *   7 gate/up projection + SwiGLU, 8 down projection + residual + scatter.
+ *   1 row offsets and map + gather + RMSNorm, 2 QKV projection + K/V scatter,
+ *   3 its split-tail fixup, 4 attention (+ split combine), 5 output projection + residual,
+ *   6 its fixup, 7 RMSNorm, 8 gate/up projection + SwiGLU, 9 its fixup,
+ *   10 down projection + residual + scatter, 11 its fixup.
+ * (A fixup kernel finishes the tiles whose K range was split over idle workgroups; it exits at
+ * once when the projection did not split.)
  * events may be NULL (then this is dcu_selective_layer); otherwise n_events must be at least
  * DCU_LAYER_STAGES + 1 (EINVAL). A failed event record returns DCU_EHIP.
  */
-#define DCU_LAYER_STAGES 8
+#define DCU_LAYER_STAGES 11
 int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
                                const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
                                void* k_cache, void* v_cache, void* y_out, void* workspace,

@@ -189,8 +189,9 @@ class Layer:
         return int(load().dcu_selective_layer_workspace(ctypes.byref(self.desc), B, N, max_rows))
 
 
-LAYER_STAGES = ("plan", "gather_rmsnorm", "qkv_scatter", "attention", "o_proj_residual",
-                "rmsnorm", "gate_up_swiglu", "down_residual_scatter")
+LAYER_STAGES = ("gather_rmsnorm", "qkv_scatter", "qkv_fixup", "attention",
+                "o_proj_residual", "o_proj_fixup", "rmsnorm", "gate_up_swiglu", "gate_up_fixup",
+                "down_residual_scatter", "down_fixup")
 
 
 def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_cache, v_cache,

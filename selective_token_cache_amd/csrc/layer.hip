@@ -7,14 +7,14 @@
 // an = RMSNorm(a; g_ffn), y = a + (silu(an W_gate^T) * an W_up^T) W_down^T.
 //
 // Kernels, in stream order (no host synchronisation; ragged per-sequence counts stay on device):
-//  1. k_plan          one workgroup: per-sequence row offsets (clamped to the workspace capacity),
-//                     the compacted row map (selected row -> global cache row), attention q-tiles;
-//  2. k_rmsnorm       gather of the selected input rows + RMSNorm -> xn (bf16);
+//  1. k_gather_rmsnorm  per-sequence row offsets (clamped to the workspace capacity) from the
+//                     counts, the compacted row map (selected row -> global cache row), attention
+//                     query-tile tables, and the gather of the selected input rows + RMSNorm -> xn;
 //  3. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches;
 //  4. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
 //                     when there are too few tiles to fill the chip) + k_attn_combine;
 //  5. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
-//  6. k_rmsnorm       RMSNorm of a -> an (bf16);
+//  6. k_rmsnorm_f32   RMSNorm of a -> an (bf16);
 //  7. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
 //  8. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
 //
@@ -63,95 +63,131 @@ struct Ptrs {
   float* ml;      // [S, M_cap, H, 2]   (split attention only)
 };
 
-// ------------------------------------------------------------------------------ 1. plan
-__global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ sel_idx,
-                                               const int32_t* __restrict__ sel_count, int B, int N,
-                                               int M_cap, Ptrs P) {
-  const int t = threadIdx.x;
-  if (t == 0) {
-    int off = 0, toff = 0;
-    for (int b = 0; b < B; ++b) {
-      int c = sel_idx ? sel_count[b] : N;
+// ------------------------------------------------------------------------------ 1+2. plan, gather, RMSNorm
+constexpr int kMaxSeqs = 4096;  // sequences per call (LDS prefix of the per-sequence counts)
+
+// Per-sequence row offsets (counts clamped to [0, N], running total clamped to M_cap) into LDS
+// off[0..B]; every workgroup of the kernel evaluates the same prefix.
+__device__ void row_offsets(const int32_t* __restrict__ sel_count, int B, int N, int M_cap,
+                            int* off, int* scan_lds) {
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += blockDim.x) {
+    const int b = c0 + threadIdx.x;
+    int c = 0;
+    if (b < B) {
+      c = sel_count ? sel_count[b] : N;
       c = c < 0 ? 0 : (c > N ? N : c);
-      P.seq_off[b] = off;
-      P.tile_off[b] = toff;
-      const int nxt = off + c < M_cap ? off + c : M_cap;
-      toff += (nxt - off + kQTile - 1) / kQTile;
-      off = nxt;
     }
-    P.seq_off[B] = off;
-    P.tile_off[B] = toff;
-    P.hdr[kHdrM] = off;
-    P.hdr[kHdrTq] = toff;
+    int tot;
+    const int ex = block_excl_scan(c, scan_lds, &tot);
+    if (b < B) off[b] = carry + ex;
+    carry += tot;
   }
+  if (threadIdx.x == 0) off[B] = carry;
   __syncthreads();
-  for (int b = 0; b < B; ++b) {
-    const int s0 = P.seq_off[b], n = P.seq_off[b + 1] - s0;
-    const int t0 = P.tile_off[b], nt = P.tile_off[b + 1] - t0;
-    for (int j = t; j < n; j += blockDim.x)
-      P.rowmap[s0 + j] = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
-    for (int j = t; j < nt; j += blockDim.x) P.tile_seq[t0 + j] = b;
-  }
+  // clamp the running total to the row capacity (later sequences lose rows first)
+  for (int b = threadIdx.x; b <= B; b += blockDim.x) off[b] = off[b] < M_cap ? off[b] : M_cap;
+  __syncthreads();
 }
 
-// ------------------------------------------------------------------------------ 2/6. RMSNorm
-// one wave per row; kF32In: fp32 rows (a), else bf16 rows of x gathered through rowmap
-template <bool kF32In>
-__global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x,
-                                                 const int* __restrict__ rowmap,
-                                                 const int* __restrict__ hdr,
-                                                 const uint16_t* __restrict__ gain, int d,
-                                                 float eps, uint16_t* __restrict__ out) {
-  const int M = hdr[kHdrM];
+// Gather of the selected rows of x + RMSNorm -> xn (bf16). Also publishes, from workgroup 0, the
+// row count, per-sequence offsets and attention query-tile tables that the later kernels read,
+// and writes the row map (selected row -> global cache row) for every row it normalises.
+__global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ sel_idx,
+                                                        const int32_t* __restrict__ sel_count,
+                                                        int B, int N, int M_cap,
+                                                        const uint16_t* __restrict__ gain, int d,
+                                                        float eps, uint16_t* __restrict__ out,
+                                                        Ptrs P) {
+  __shared__ int off[kMaxSeqs + 1];
+  __shared__ int scan_lds[17];
+  row_offsets(sel_count, B, N, M_cap, off, scan_lds);
+  const int M = off[B];
+  if (blockIdx.x == 0) {
+    int toff = 0;
+    for (int b = 0; b < B; ++b) {  // uniform loop; tiles of 64 query rows per sequence
+      const int nt = (off[b + 1] - off[b] + kQTile - 1) / kQTile;
+      for (int j = threadIdx.x; j < nt; j += blockDim.x) P.tile_seq[toff + j] = b;
+      if (threadIdx.x == 0) {
+        P.seq_off[b] = off[b];
+        P.tile_off[b] = toff;
+      }
+      toff += nt;
+    }
+    if (threadIdx.x == 0) {
+      P.seq_off[B] = M;
+      P.tile_off[B] = toff;
+      P.hdr[kHdrM] = M;
+      P.hdr[kHdrTq] = toff;
+    }
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int groups = d / 8;  // 8 elements per lane step
   for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
+    // sequence of row r: the last b with off[b] <= r
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo, j = r - off[b];
+    const int grow = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
+    if (lane == 0) P.rowmap[r] = grow;
+    const uint16_t* row = x + int64_t(grow) * d;
     float ss = 0.0f;
-    if constexpr (kF32In) {
-      const float* row = static_cast<const float*>(x) + int64_t(r) * d;
-      for (int g = lane; g < groups; g += kWave) {
-        const float4 u = reinterpret_cast<const float4*>(row)[2 * g];
-        const float4 v = reinterpret_cast<const float4*>(row)[2 * g + 1];
-        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w + v.x * v.x + v.y * v.y + v.z * v.z +
-              v.w * v.w;
-      }
-    } else {
-      const uint16_t* row = static_cast<const uint16_t*>(x) + int64_t(rowmap[r]) * d;
-      for (int g = lane; g < groups; g += kWave) {
-        const uint4 u = reinterpret_cast<const uint4*>(row)[g];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int g = lane; g < groups; g += kWave) {
+      const uint4 u = reinterpret_cast<const uint4*>(row)[g];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = bf_lo(w[j]), hi = bf_hi(w[j]);
-          ss += lo * lo + hi * hi;
-        }
+      for (int k = 0; k < 4; ++k) {
+        const float a = bf_lo(w[k]), c = bf_hi(w[k]);
+        ss += a * a + c * c;
       }
     }
     ss = wave_sum(ss);
     const float scale = 1.0f / sqrtf(ss / float(d) + eps);
     uint16_t* orow = out + int64_t(r) * d;
     for (int g = lane; g < groups; g += kWave) {
-      float v[8];
-      if constexpr (kF32In) {
-        const float* row = static_cast<const float*>(x) + int64_t(r) * d;
-        const float4 u = reinterpret_cast<const float4*>(row)[2 * g];
-        const float4 w = reinterpret_cast<const float4*>(row)[2 * g + 1];
-        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
-        v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
-      } else {
-        const uint16_t* row = static_cast<const uint16_t*>(x) + int64_t(rowmap[r]) * d;
-        const uint4 u = reinterpret_cast<const uint4*>(row)[g];
-        v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
-        v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
-      }
+      const uint4 u = reinterpret_cast<const uint4*>(row)[g];
       const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
-      const float gv[8] = {bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y),
-                           bf_lo(gg.z), bf_hi(gg.z), bf_lo(gg.w), bf_hi(gg.w)};
       uint4 o;
-      o.x = pack_bf2(v[0] * scale * gv[0], v[1] * scale * gv[1]);
-      o.y = pack_bf2(v[2] * scale * gv[2], v[3] * scale * gv[3]);
-      o.z = pack_bf2(v[4] * scale * gv[4], v[5] * scale * gv[5]);
-      o.w = pack_bf2(v[6] * scale * gv[6], v[7] * scale * gv[7]);
+      o.x = pack_bf2(bf_lo(u.x) * scale * bf_lo(gg.x), bf_hi(u.x) * scale * bf_hi(gg.x));
+      o.y = pack_bf2(bf_lo(u.y) * scale * bf_lo(gg.y), bf_hi(u.y) * scale * bf_hi(gg.y));
+      o.z = pack_bf2(bf_lo(u.z) * scale * bf_lo(gg.z), bf_hi(u.z) * scale * bf_hi(gg.z));
+      o.w = pack_bf2(bf_lo(u.w) * scale * bf_lo(gg.w), bf_hi(u.w) * scale * bf_hi(gg.w));
+      reinterpret_cast<uint4*>(orow)[g] = o;
+    }
+  }
+}
+
+// RMSNorm of the fp32 rows a -> bf16, one wave per row
+__global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ a,
+                                                     const int* __restrict__ hdr,
+                                                     const uint16_t* __restrict__ gain, int d,
+                                                     float eps, uint16_t* __restrict__ out) {
+  const int M = hdr[kHdrM];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int groups = d / 8;
+  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
+    const float4* row = reinterpret_cast<const float4*>(a + int64_t(r) * d);
+    float ss = 0.0f;
+    for (int g = lane; g < groups; g += kWave) {
+      const float4 u = row[2 * g], v = row[2 * g + 1];
+      ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w + v.x * v.x + v.y * v.y + v.z * v.z +
+            v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
+    uint16_t* orow = out + int64_t(r) * d;
+    for (int g = lane; g < groups; g += kWave) {
+      const float4 u = row[2 * g], v = row[2 * g + 1];
+      const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
+      uint4 o;
+      o.x = pack_bf2(u.x * scale * bf_lo(gg.x), u.y * scale * bf_hi(gg.x));
+      o.y = pack_bf2(u.z * scale * bf_lo(gg.y), u.w * scale * bf_hi(gg.y));
+      o.z = pack_bf2(v.x * scale * bf_lo(gg.z), v.y * scale * bf_hi(gg.z));
+      o.w = pack_bf2(v.z * scale * bf_lo(gg.w), v.w * scale * bf_hi(gg.w));
       reinterpret_cast<uint4*>(orow)[g] = o;
     }
   }
@@ -753,7 +789,7 @@ int validate(const dcu_layer* w, int B, int N) {
   if (!(w->rms_eps >= 0.0f)) return DCU_EINVAL;
   if (w->head_dim != 32 && w->head_dim != 64 && w->head_dim != 128) return DCU_EUNSUPPORTED;
   if (w->d % 64 != 0 || w->ffn % 64 != 0) return DCU_EUNSUPPORTED;
-  if (N > 65536 || int64_t(B) * N > (int64_t(1) << 28)) return DCU_EUNSUPPORTED;
+  if (N > 65536 || int64_t(B) * N > (int64_t(1) << 28) || B > kMaxSeqs) return DCU_EUNSUPPORTED;
   const void* ps[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn, w->g_ffn};
   for (const void* p : ps)
     if (!dcu_aligned16(p)) return DCU_EUNSUPPORTED;
@@ -832,15 +868,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   };
   if (!mark()) return DCU_EHIP;
 
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(1024), 0, s, sel_idx, sel_count, int(B), int(N),
-                     L.M_cap, P);
-  DCU_LAUNCH_CHECK();
-  if (!mark()) return DCU_EHIP;
-
   const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
-  hipLaunchKernelGGL(k_rmsnorm<false>, dim3(norm_blocks), dim3(256), 0, s,
-                     static_cast<const void*>(x), P.rowmap, P.hdr,
-                     static_cast<const uint16_t*>(w->g_attn), d, w->rms_eps, P.xn);
+  hipLaunchKernelGGL(k_gather_rmsnorm, dim3(norm_blocks), dim3(256), 0, s, x, sel_idx, sel_count,
+                     int(B), int(N), L.M_cap, static_cast<const uint16_t*>(w->g_attn), d,
+                     w->rms_eps, P.xn, P);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -859,6 +890,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.vc = static_cast<uint16_t*>(v_cache);
   launch_gemm<EPI_QKV, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_QKV, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
@@ -909,13 +941,13 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
 
   launch_gemm<EPI_RESID, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_RESID, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
   // RMSNorm before the FFN -> an (reuses the xn buffer)
-  hipLaunchKernelGGL(k_rmsnorm<true>, dim3(norm_blocks), dim3(256), 0, s,
-                     static_cast<const void*>(P.a), P.rowmap, P.hdr,
+  hipLaunchKernelGGL(k_rmsnorm_f32, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr,
                      static_cast<const uint16_t*>(w->g_ffn), d, w->rms_eps, P.xn);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
@@ -929,6 +961,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.h = P.h;
   launch_gemm<EPI_SWIGLU, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_SWIGLU, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
@@ -942,6 +975,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.y = static_cast<uint16_t*>(y_out);
   launch_gemm<EPI_DOWN, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
+  if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_DOWN, CfgSmall>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
