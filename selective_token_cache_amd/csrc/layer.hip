@@ -449,10 +449,11 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
 // owning 16 queries. S^T = K Q^T is computed with the key block as the MFMA A operand, so a lane
 // holds 4 keys x 1 query per fragment; that register layout is exactly the B operand that
 // O^T = V^T P^T needs (keys permuted consistently on both sides), so P never leaves registers.
-// K and V blocks of 64 keys stream global -> LDS by DMA through kAttnStages distinct buffers (row
-// layout, 16-byte chunk swizzle c ^ (key & (CH-1))), so global latency is hidden behind the blocks
-// being consumed. Each V block is then transposed inside LDS into a padded V^T tile (pairs of keys
-// packed into 32-bit words), from which the V^T operand is read with two 8-byte loads per fragment.
+// K and V blocks of 64 keys stream global -> LDS by DMA through kAttnStages distinct buffers in row
+// layout with a 16-byte chunk swizzle. The V^T operand is read straight from the row-layout V block
+// with the gfx950 transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4i + e receives element e of the 8-byte rows addressed by lanes i, i+4, i+8, i+12, so when those
+// lanes address 4 consecutive head dims of 4 keys, every lane ends with 4 keys of one head dim.
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kc;
@@ -468,22 +469,37 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
-constexpr int kKB = 64;             // keys per block
-constexpr int kAttnStages = 3;      // LDS stages of (K, V) blocks
-constexpr int kVTStride = kKB + 4;  // padded V^T row (bf16 elements)
+constexpr int kKB = 64;         // keys per block
+constexpr int kAttnStages = 2;  // LDS stages of (K, V) blocks: 64 KB at head_dim 128, 2 WGs per CU
 
+// Chunk swizzle of a key row: 8 consecutive keys land on distinct 16-byte bank groups (the K
+// fragment reads), and keys 4G..4G+3 x two adjacent chunks land on distinct 8-byte bank pairs
+// (the transposing V reads).
 template <int CH>
-__device__ __forceinline__ int kswz(int key, int c) { return key * CH + (c ^ (key & (CH - 1))); }
+__device__ __forceinline__ int kvsw(int key) {
+  return ((((key & 3) << 1) | ((key >> 2) & 1))) & (CH - 1);
+}
+template <int CH>
+__device__ __forceinline__ int kswz(int key, int c) { return key * CH + (c ^ kvsw<CH>(key)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
 
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
+__global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs g) {
   constexpr int CH = DH / 8;            // 16-byte chunks per head row
   constexpr int BLK = kKB * CH;         // chunks per K (or V) block
   constexpr int NQ = BLK / 64 / 4;      // DMA instructions per wave per block, per operand
+  constexpr int ST = kAttnStages;
   static_assert(NQ >= 1, "block size");
-  __shared__ u32x4 k0[BLK], k1[BLK], k2[BLK];
-  __shared__ u32x4 v0[BLK], v1[BLK], v2[BLK];
-  __shared__ uint16_t smVT[DH * kVTStride];
+  static_assert(ST == 2 || ST == 3, "stages");
+  __shared__ u32x4 k0[BLK], k1[BLK], k2[ST > 2 ? BLK : 1];
+  __shared__ u32x4 v0[BLK], v1[BLK], v2[ST > 2 ? BLK : 1];
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6, grp = lane >> 4, col = lane & 15;
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   const int Tq = g.hdr[kHdrTq];
@@ -494,7 +510,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
   for (int i = 0; i < NQ; ++i) {
     const int p = (i * 4 + wid) * 64 + lane;
     drow[i] = p / CH;
-    dcol[i] = (p % CH) ^ (drow[i] & (CH - 1));
+    dcol[i] = (p % CH) ^ kvsw<CH>(drow[i]);
+  }
+  // per-lane halfword offsets of the transposing V reads: this lane addresses key 4*grp + j
+  // (j = (lane >> 2) & 3) and head dims 16*df + 4*(lane & 3) .. +3 of the block
+  int vto[DH / 16];
+  {
+    const int i = lane & 3, key = 4 * grp + ((lane >> 2) & 3);
+#pragma unroll
+    for (int df = 0; df < DH / 16; ++df) {
+      const int dc = 2 * df + (i >> 1);
+      vto[df] = key * DH + ((dc ^ kvsw<CH>(key)) * 8) + 4 * (i & 1);
+    }
   }
   for (int w = blockIdx.x; w < items; w += gridDim.x) {
     const int split = w % g.splits;
@@ -552,28 +579,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // V block (row layout) -> V^T tile: thread takes keys (2kp, 2kp+1) x 8 head dims
-    auto transpose_v = [&](auto sidx) {
-      constexpr int S = decltype(sidx)::value;
-      const u32x4* vb = S == 0 ? v0 : (S == 1 ? v1 : v2);
-#pragma unroll
-      for (int qd = t; qd < (kKB / 2) * CH; qd += 256) {
-        const int kp = qd & 31, dc = qd >> 5;
-        const u32x4 a = vb[kswz<CH>(2 * kp, dc)];
-        const u32x4 c = vb[kswz<CH>(2 * kp + 1, dc)];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = (a[j] & 0xffffu) | (c[j] << 16);
-          const uint32_t hi = (a[j] >> 16) | (c[j] & 0xffff0000u);
-          *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j) * kVTStride + 2 * kp]) = lo;
-          *reinterpret_cast<uint32_t*>(&smVT[(dc * 8 + 2 * j + 1) * kVTStride + 2 * kp]) = hi;
-        }
-      }
-    };
-
     auto compute = [&](auto sidx, int j) {
       constexpr int S = decltype(sidx)::value;
       const u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
+      const uint16_t* vh = reinterpret_cast<const uint16_t*>(S == 0 ? v0 : (S == 1 ? v1 : v2));
       const int kb0 = kbeg + j * kKB;
       // S^T for 64 keys x 16 queries: 4 fragments (keys 16f + 4*grp + i)
       f32x4 s[4];
@@ -635,10 +644,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
         const u32x4 pb = u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]};
 #pragma unroll
         for (int df = 0; df < DH / 16; ++df) {
-          const int row = df * 16 + col;
-          const uint2 lo = *reinterpret_cast<const uint2*>(&smVT[row * kVTStride + 32 * c + 4 * grp]);
-          const uint2 hi =
-              *reinterpret_cast<const uint2*>(&smVT[row * kVTStride + 32 * c + 16 + 4 * grp]);
+          const u32x2 lo = lds_read_tr16(vh + vto[df] + (32 * c) * DH);
+          const u32x2 hi = lds_read_tr16(vh + vto[df] + (32 * c + 16) * DH);
           acc_o[df] = mfma16x16x32(u32x4{lo.x, lo.y, hi.x, hi.y}, pb, acc_o[df]);
         }
       }
@@ -649,23 +656,21 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs g) {
     using I2 = std::integral_constant<int, 2>;
     auto iter = [&](auto cur, int j) {
       constexpr int S = decltype(cur)::value;
-      constexpr int NXT = (S + kAttnStages - 1) % kAttnStages;
-      gemm::wait_vm_lgkm0<(kAttnStages - 2) * 2 * NQ>();
+      constexpr int NXT = (S + ST - 1) % ST;
+      gemm::wait_vm_lgkm0<(ST - 2) * 2 * NQ>();
       __builtin_amdgcn_s_barrier();  // block j has landed; the previous block is fully consumed
-      issue(std::integral_constant<int, NXT>{}, j + kAttnStages - 1);
-      transpose_v(cur);
-      constexpr int kInFlight = (kAttnStages - 1) * 2 * NQ;  // DMA groups j+1 .. j+STAGES-1
-      gemm::wait_vm_lgkm0<kInFlight>();                        // only the LDS writes above
-      __builtin_amdgcn_s_barrier();  // V^T of block j is complete
+      issue(std::integral_constant<int, NXT>{}, j + ST - 1);
       compute(cur, j);
     };
     if (nblk > 0) {
       issue(I0{}, 0);
-      issue(I1{}, 1);
-      for (int j = 0; j < nblk; j += kAttnStages) {
+      if constexpr (ST == 3) issue(I1{}, 1);
+      for (int j = 0; j < nblk; j += ST) {
         iter(I0{}, j);
         if (j + 1 < nblk) iter(I1{}, j + 1); else break;
-        if (j + 2 < nblk) iter(I2{}, j + 2); else break;
+        if constexpr (ST == 3) {
+          if (j + 2 < nblk) iter(I2{}, j + 2); else break;
+        }
       }
       gemm::wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
