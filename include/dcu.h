@@ -148,7 +148,11 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  * k_cache, v_cache  [B, N, n_heads, head_dim] bf16 IN/OUT: selected rows are overwritten before
  *           attention reads the cache; other rows are untouched.
  * y_out     [B, N, d] bf16 IN/OUT: selected rows get the layer output; other rows are untouched.
- * workspace device scratch of at least dcu_selective_layer_workspace() bytes (256-byte aligned).
+ * workspace device scratch of at least dcu_selective_layer_workspace() bytes (256-byte aligned),
+ *           owned by the caller; its contents on entry do not matter. Calls that share a
+ *           workspace must be ordered (same stream): it holds the row map, activations and
+ *           split-K partial tiles of one call.
+ * Results are bitwise reproducible for a given device: every reduction runs in a fixed order.
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
  *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if head_dim not in {32, 64, 128}, d
  *         or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte

@@ -90,9 +90,93 @@ __device__ void row_offsets(const int32_t* __restrict__ sel_count, int B, int N,
   __syncthreads();
 }
 
+// RMSNorm of one row by one wave: out = x * (1 / sqrt(mean(x^2) + eps)) * gain, fp32 arithmetic,
+// bf16 out. NC > 0: the lane's NC 8-element groups (lane, lane + 64, ...) are loaded at once and kept
+// in registers, so the row costs a single round trip to memory; NC == 0: two passes over the row.
+// The per-lane accumulation order is the same in both forms.
+template <int NC, bool kF32>
+__device__ __forceinline__ void rms_row(const void* __restrict__ row_v,
+                                        const uint16_t* __restrict__ gain, int d, float eps,
+                                        uint16_t* __restrict__ orow, int lane) {
+  const int groups = d / 8;
+  auto load = [&](int g, float (&v)[8]) {
+    if constexpr (kF32) {
+      const float4* row = static_cast<const float4*>(row_v);
+      const float4 u = row[2 * g], w = row[2 * g + 1];
+      v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+      v[4] = w.x; v[5] = w.y; v[6] = w.z; v[7] = w.w;
+    } else {
+      const uint4 u = static_cast<const uint4*>(row_v)[g];
+      v[0] = bf_lo(u.x); v[1] = bf_hi(u.x); v[2] = bf_lo(u.y); v[3] = bf_hi(u.y);
+      v[4] = bf_lo(u.z); v[5] = bf_hi(u.z); v[6] = bf_lo(u.w); v[7] = bf_hi(u.w);
+    }
+  };
+  auto sumsq = [](const float (&v)[8]) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) ss += v[k] * v[k] + v[k + 1] * v[k + 1];
+    return ss;
+  };
+  auto store = [&](int g, const float (&v)[8], float scale) {
+    const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
+    uint4 o;
+    o.x = pack_bf2(v[0] * scale * bf_lo(gg.x), v[1] * scale * bf_hi(gg.x));
+    o.y = pack_bf2(v[2] * scale * bf_lo(gg.y), v[3] * scale * bf_hi(gg.y));
+    o.z = pack_bf2(v[4] * scale * bf_lo(gg.z), v[5] * scale * bf_hi(gg.z));
+    o.w = pack_bf2(v[6] * scale * bf_lo(gg.w), v[7] * scale * bf_hi(gg.w));
+    reinterpret_cast<uint4*>(orow)[g] = o;
+  };
+  float ss = 0.0f;
+  if constexpr (NC > 0) {
+    float v[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int g = lane + c * kWave;
+      if (g < groups) {
+        load(g, v[c]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[c][k] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ss += sumsq(v[c]);
+    ss = wave_sum(ss);
+    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int g = lane + c * kWave;
+      if (g < groups) store(g, v[c], scale);
+    }
+  } else {
+    for (int g = lane; g < groups; g += kWave) {
+      float v[8];
+      load(g, v);
+      ss += sumsq(v);
+    }
+    ss = wave_sum(ss);
+    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
+    for (int g = lane; g < groups; g += kWave) {
+      float v[8];
+      load(g, v);
+      store(g, v, scale);
+    }
+  }
+}
+
+// 8-element groups per lane held in registers for a row of d elements (0: two-pass form)
+inline int rms_nc(int d, bool f32) {
+  const int per_lane = (d / 8 + kWave - 1) / kWave;
+  const int cap = f32 ? 8 : 16;
+  for (int nc = 1; nc <= cap; nc *= 2)
+    if (per_lane <= nc) return nc;
+  return 0;
+}
+
 // Gather of the selected rows of x + RMSNorm -> xn (bf16). Also publishes, from workgroup 0, the
 // row count, per-sequence offsets and attention query-tile tables that the later kernels read,
 // and writes the row map (selected row -> global cache row) for every row it normalises.
+template <int NC>
 __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restrict__ x,
                                                         const int32_t* __restrict__ sel_idx,
                                                         const int32_t* __restrict__ sel_count,
@@ -123,7 +207,6 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
     }
   }
   const int lane = threadIdx.x & (kWave - 1);
-  const int groups = d / 8;  // 8 elements per lane step
   for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
     // sequence of row r: the last b with off[b] <= r
     int lo = 0, hi = B - 1;
@@ -134,63 +217,20 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
     const int b = lo, j = r - off[b];
     const int grow = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
     if (lane == 0) P.rowmap[r] = grow;
-    const uint16_t* row = x + int64_t(grow) * d;
-    float ss = 0.0f;
-    for (int g = lane; g < groups; g += kWave) {
-      const uint4 u = reinterpret_cast<const uint4*>(row)[g];
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float a = bf_lo(w[k]), c = bf_hi(w[k]);
-        ss += a * a + c * c;
-      }
-    }
-    ss = wave_sum(ss);
-    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
-    uint16_t* orow = out + int64_t(r) * d;
-    for (int g = lane; g < groups; g += kWave) {
-      const uint4 u = reinterpret_cast<const uint4*>(row)[g];
-      const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
-      uint4 o;
-      o.x = pack_bf2(bf_lo(u.x) * scale * bf_lo(gg.x), bf_hi(u.x) * scale * bf_hi(gg.x));
-      o.y = pack_bf2(bf_lo(u.y) * scale * bf_lo(gg.y), bf_hi(u.y) * scale * bf_hi(gg.y));
-      o.z = pack_bf2(bf_lo(u.z) * scale * bf_lo(gg.z), bf_hi(u.z) * scale * bf_hi(gg.z));
-      o.w = pack_bf2(bf_lo(u.w) * scale * bf_lo(gg.w), bf_hi(u.w) * scale * bf_hi(gg.w));
-      reinterpret_cast<uint4*>(orow)[g] = o;
-    }
+    rms_row<NC, false>(x + int64_t(grow) * d, gain, d, eps, out + int64_t(r) * d, lane);
   }
 }
 
 // RMSNorm of the fp32 rows a -> bf16, one wave per row
+template <int NC>
 __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ a,
                                                      const int* __restrict__ hdr,
                                                      const uint16_t* __restrict__ gain, int d,
                                                      float eps, uint16_t* __restrict__ out) {
   const int M = hdr[kHdrM];
   const int lane = threadIdx.x & (kWave - 1);
-  const int groups = d / 8;
-  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
-    const float4* row = reinterpret_cast<const float4*>(a + int64_t(r) * d);
-    float ss = 0.0f;
-    for (int g = lane; g < groups; g += kWave) {
-      const float4 u = row[2 * g], v = row[2 * g + 1];
-      ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w + v.x * v.x + v.y * v.y + v.z * v.z +
-            v.w * v.w;
-    }
-    ss = wave_sum(ss);
-    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
-    uint16_t* orow = out + int64_t(r) * d;
-    for (int g = lane; g < groups; g += kWave) {
-      const float4 u = row[2 * g], v = row[2 * g + 1];
-      const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
-      uint4 o;
-      o.x = pack_bf2(u.x * scale * bf_lo(gg.x), u.y * scale * bf_hi(gg.x));
-      o.y = pack_bf2(u.z * scale * bf_lo(gg.y), u.w * scale * bf_hi(gg.y));
-      o.z = pack_bf2(v.x * scale * bf_lo(gg.z), v.y * scale * bf_hi(gg.z));
-      o.w = pack_bf2(v.z * scale * bf_lo(gg.w), v.w * scale * bf_hi(gg.w));
-      reinterpret_cast<uint4*>(orow)[g] = o;
-    }
-  }
+  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4)
+    rms_row<NC, true>(a + int64_t(r) * d, gain, d, eps, out + int64_t(r) * d, lane);
 }
 
 // ------------------------------------------------------------------------------ 3/5/7/8. GEMM
@@ -874,9 +914,21 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   if (!mark()) return DCU_EHIP;
 
   const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
-  hipLaunchKernelGGL(k_gather_rmsnorm, dim3(norm_blocks), dim3(256), 0, s, x, sel_idx, sel_count,
-                     int(B), int(N), L.M_cap, static_cast<const uint16_t*>(w->g_attn), d,
-                     w->rms_eps, P.xn, P);
+  {
+    const uint16_t* ga_ = static_cast<const uint16_t*>(w->g_attn);
+#define DCU_GATHER(NC)                                                                        \
+  hipLaunchKernelGGL(k_gather_rmsnorm<NC>, dim3(norm_blocks), dim3(256), 0, s, x, sel_idx,    \
+                     sel_count, int(B), int(N), L.M_cap, ga_, d, w->rms_eps, P.xn, P)
+    switch (rms_nc(d, false)) {
+      case 1: DCU_GATHER(1); break;
+      case 2: DCU_GATHER(2); break;
+      case 4: DCU_GATHER(4); break;
+      case 8: DCU_GATHER(8); break;
+      case 16: DCU_GATHER(16); break;
+      default: DCU_GATHER(0); break;
+    }
+#undef DCU_GATHER
+  }
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -952,8 +1004,20 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   if (!mark()) return DCU_EHIP;
 
   // RMSNorm before the FFN -> an (reuses the xn buffer)
-  hipLaunchKernelGGL(k_rmsnorm_f32, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr,
-                     static_cast<const uint16_t*>(w->g_ffn), d, w->rms_eps, P.xn);
+  {
+    const uint16_t* gf_ = static_cast<const uint16_t*>(w->g_ffn);
+#define DCU_RMS(NC)                                                                        \
+  hipLaunchKernelGGL(k_rmsnorm_f32<NC>, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr, gf_, d, \
+                     w->rms_eps, P.xn)
+    switch (rms_nc(d, true)) {
+      case 1: DCU_RMS(1); break;
+      case 2: DCU_RMS(2); break;
+      case 4: DCU_RMS(4); break;
+      case 8: DCU_RMS(8); break;
+      default: DCU_RMS(0); break;
+    }
+#undef DCU_RMS
+  }
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
