@@ -414,7 +414,10 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
 }
 
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
-// thread. Exits at once when the GEMM did not split.
+// thread and item, kFixupU items per thread and round, with every partial of those items loaded
+// before any is used (memory-level parallelism). Exits at once when the GEMM did not split.
+constexpr int kFixupU = 2;
+
 template <int EPI, class C>
 __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   const int M = g.hdr[kHdrM];
@@ -425,60 +428,88 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   if (sp.rem == 0) return;
   constexpr int OUTC = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;  // output columns per tile
   constexpr int Q = C::BM * OUTC / 4;                          // float4 groups per tile
+  constexpr int NV = EPI == EPI_SWIGLU ? 2 : 1;                // float4 per item and partial
   const int64_t total = int64_t(sp.rem) * Q;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const int tt = int(i / Q), q = int(i % Q);
-    const int r = q / (OUTC / 4), c4 = (q % (OUTC / 4)) * 4;
-    const int tile = sp.full + tt;
-    const int m_t = tile % MT, n_t = tile / MT;
-    const int m = m_t * C::BM + r;
-    if (m >= M) continue;
-    const float* pt = g.part + int64_t(tt) * sp.S * (C::BM * C::BN);
-    if constexpr (EPI == EPI_SWIGLU) {
-      // output column c4..c4+3 of the tile = wave column wn, within-wave columns w..w+3
-      const int wn = c4 / (C::WN / 2), w = c4 % (C::WN / 2);
-      const int cg = wn * C::WN + w, cu = cg + C::WN / 2;
-      float4 gt = *reinterpret_cast<const float4*>(pt + r * C::BN + cg);
-      float4 up = *reinterpret_cast<const float4*>(pt + r * C::BN + cu);
-      for (int s2 = 1; s2 < sp.S; ++s2) {
-        const float* ps = pt + int64_t(s2) * (C::BM * C::BN) + r * C::BN;
-        const float4 a = *reinterpret_cast<const float4*>(ps + cg);
-        const float4 b = *reinterpret_cast<const float4*>(ps + cu);
-        gt.x += a.x; gt.y += a.y; gt.z += a.z; gt.w += a.w;
-        up.x += b.x; up.y += b.y; up.z += b.z; up.w += b.w;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < total;
+       i0 += stride * kFixupU) {
+    float4 v[kFixupU][NV];
+    int m_u[kFixupU], col_u[kFixupU], nt_u[kFixupU];
+    bool ok[kFixupU];
+#pragma unroll
+    for (int u = 0; u < kFixupU; ++u) {
+      const int64_t i = i0 + u * stride;
+      const int tt = int(i / Q), q = int(i % Q);
+      const int r = q / (OUTC / 4), c4 = (q % (OUTC / 4)) * 4;
+      const int tile = sp.full + tt;
+      const int m_t = tile % MT, n_t = tile / MT;
+      const int m = m_t * C::BM + r;
+      int n = n_t * C::BN + c4;
+      ok[u] = i < total && m < M && (EPI == EPI_SWIGLU || n < g.Nout);
+      m_u[u] = m;
+      col_u[u] = c4;
+      nt_u[u] = n_t;
+      // partial columns of this item: SwiGLU reads the gate and the up column of the same output
+      int cols[NV];
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int wn = c4 / (C::WN / 2), w = c4 % (C::WN / 2);
+        cols[0] = wn * C::WN + w;
+        cols[NV - 1] = cols[0] + C::WN / 2;
+      } else {
+        cols[0] = c4;
       }
-      const int j = n_t * (C::BN / 2) + c4;
-      uint2 st;
-      st.x = pack_bf2(gt.x / (1.0f + __expf(-gt.x)) * up.x, gt.y / (1.0f + __expf(-gt.y)) * up.y);
-      st.y = pack_bf2(gt.z / (1.0f + __expf(-gt.z)) * up.z, gt.w / (1.0f + __expf(-gt.w)) * up.w);
-      *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
-    } else {
-      const int n = n_t * C::BN + c4;
-      if (n >= g.Nout) continue;
-      float4 v = *reinterpret_cast<const float4*>(pt + r * C::BN + c4);
-      for (int s2 = 1; s2 < sp.S; ++s2) {
-        const float4 a = *reinterpret_cast<const float4*>(pt + int64_t(s2) * (C::BM * C::BN) + r * C::BN + c4);
-        v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+      const float* pt = g.part + int64_t(ok[u] ? tt : 0) * sp.S * (C::BM * C::BN) + r * C::BN;
+      float4 p[kMaxSplitK][NV];
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplitK; ++s2)
+#pragma unroll
+        for (int e = 0; e < NV; ++e)
+          if (ok[u] && s2 < sp.S)
+            p[s2][e] = *reinterpret_cast<const float4*>(pt + int64_t(s2) * (C::BM * C::BN) + cols[e]);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        v[u][e] = p[0][e];
+#pragma unroll
+        for (int s2 = 1; s2 < kMaxSplitK; ++s2)
+          if (s2 < sp.S) {
+            v[u][e].x += p[s2][e].x; v[u][e].y += p[s2][e].y;
+            v[u][e].z += p[s2][e].z; v[u][e].w += p[s2][e].w;
+          }
       }
-      const int64_t grow = int64_t(g.rowmap[m]);
-      if constexpr (EPI == EPI_QKV) {
+    }
+#pragma unroll
+    for (int u = 0; u < kFixupU; ++u) {
+      if (!ok[u]) continue;
+      const int m = m_u[u], c4 = col_u[u], n_t = nt_u[u];
+      if constexpr (EPI == EPI_SWIGLU) {
+        const float4 gt = v[u][0], up = v[u][NV - 1];
+        const int j = n_t * (C::BN / 2) + c4;
         uint2 st;
-        st.x = pack_bf2(v.x, v.y);
-        st.y = pack_bf2(v.z, v.w);
-        const int part = n / g.d, col = n - part * g.d;
-        uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
-        *reinterpret_cast<uint2*>(dst + col) = st;
-      } else if constexpr (EPI == EPI_RESID) {
-        const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
-        *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
-            make_float4(bf_lo(xr.x) + v.x, bf_hi(xr.x) + v.y, bf_lo(xr.y) + v.z, bf_hi(xr.y) + v.w);
-      } else {  // EPI_DOWN
-        const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
-        uint2 st;
-        st.x = pack_bf2(ar.x + v.x, ar.y + v.y);
-        st.y = pack_bf2(ar.z + v.z, ar.w + v.w);
-        *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+        st.x = pack_bf2(gt.x / (1.0f + __expf(-gt.x)) * up.x, gt.y / (1.0f + __expf(-gt.y)) * up.y);
+        st.y = pack_bf2(gt.z / (1.0f + __expf(-gt.z)) * up.z, gt.w / (1.0f + __expf(-gt.w)) * up.w);
+        *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
+      } else {
+        const float4 w = v[u][0];
+        const int n = n_t * C::BN + c4;
+        const int64_t grow = int64_t(g.rowmap[m]);
+        if constexpr (EPI == EPI_QKV) {
+          uint2 st;
+          st.x = pack_bf2(w.x, w.y);
+          st.y = pack_bf2(w.z, w.w);
+          const int part = n / g.d, col = n - part * g.d;
+          uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
+          *reinterpret_cast<uint2*>(dst + col) = st;
+        } else if constexpr (EPI == EPI_RESID) {
+          const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+          *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
+              make_float4(bf_lo(xr.x) + w.x, bf_hi(xr.x) + w.y, bf_lo(xr.y) + w.z, bf_hi(xr.y) + w.w);
+        } else {  // EPI_DOWN
+          const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+          uint2 st;
+          st.x = pack_bf2(ar.x + w.x, ar.y + w.y);
+          st.y = pack_bf2(ar.z + w.z, ar.w + w.w);
+          *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+        }
       }
     }
   }
@@ -857,7 +888,7 @@ void launch_gemm(const GemmArgs& ga, hipStream_t s) {
 
 template <int EPI, class C>
 void launch_fixup(const GemmArgs& ga, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_fixup<EPI, C>), dim3(512), dim3(256), 0, s, ga, gemm_slots<C>());
+  hipLaunchKernelGGL((k_gemm_fixup<EPI, C>), dim3(2048), dim3(256), 0, s, ga, gemm_slots<C>());
 }
 
 
