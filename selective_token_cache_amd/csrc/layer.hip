@@ -536,12 +536,41 @@ struct AttnArgs {
   const int* seq_off;
   const int* tile_off;
   const int* tile_seq;
-  int N, H, d, splits, kps, M_cap;
+  int N, H, d, S_max;
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
 constexpr int kKB = 64;         // keys per block
 constexpr int kAttnStages = 2;  // LDS stages of (K, V) blocks: 64 KB at head_dim 128, 2 WGs per CU
+
+// Work plan of the attention grid (G persistent workgroups, two per CU) for the device-side
+// query-tile count. Items are (query tile, head) pairs. When there are fewer items than CUs
+// (items < G / 2, e.g. one sequence or few selected rows) every item is split along the keys into
+// S ranges so that the units fill the chip; otherwise every item runs whole. (Splitting only the
+// items of a partial last round was measured slower at batch 8: 65.6 vs 57.6 us per layer, since
+// the short units and the merge cost more than the half-empty round, whose workgroups run alone
+// on their CUs.) A split unit writes its unnormalised fp32 output and (max, sum) to a unit-indexed
+// slot; k_attn_combine merges an item's S units in split order. Split units: items * S < G + items.
+constexpr int kAttnMaxUnits = 4 * 256;  // 2 * (2 workgroups per CU * 256 CUs)
+
+struct AttnPlan {
+  int full, rem, S, kps;
+};
+
+__device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
+  const int whole = (N + kKB - 1) / kKB * kKB;
+  AttnPlan p{items, 0, 1, whole};
+  if (items <= 0) return p;
+  if (2 * items >= G) return p;
+  const int rem = items;
+  int S = (G + items - 1) / items;
+  S = S < S_max ? S : S_max;
+  if (S <= 1) return p;
+  const int kps = ((N + S - 1) / S + kKB - 1) / kKB * kKB;
+  const int S_eff = (N + kps - 1) / kps;  // every range starts below N
+  if (S_eff <= 1) return p;
+  return AttnPlan{items - rem, rem, S_eff, kps};
+}
 
 // Chunk swizzle of a key row: 8 consecutive keys land on distinct 16-byte bank groups (the K
 // fragment reads), and keys 4G..4G+3 x two adjacent chunks land on distinct 8-byte bank pairs
@@ -574,7 +603,8 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
   const int t = threadIdx.x, lane = t & 63, wid = t >> 6, grp = lane >> 4, col = lane & 15;
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   const int Tq = g.hdr[kHdrTq];
-  const int items = Tq * g.H * g.splits;
+  const AttnPlan ap = attn_plan(Tq * g.H, gridDim.x, g.N, g.S_max);
+  const int units = ap.full + ap.rem * ap.S;
   // per-lane (row, logical chunk) of this wave's DMA instructions
   int drow[NQ], dcol[NQ];
 #pragma unroll
@@ -594,15 +624,19 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
       vto[df] = key * DH + ((dc ^ kvsw<CH>(key)) * 8) + 4 * (i & 1);
     }
   }
-  for (int w = blockIdx.x; w < items; w += gridDim.x) {
-    const int split = w % g.splits;
-    const int h = (w / g.splits) % g.H;
-    const int tile = w / (g.splits * g.H);
+  for (int w = blockIdx.x; w < units; w += gridDim.x) {
+    // whole item, or split unit v of item full + v / S covering key range v mod S
+    const int v = w - ap.full;
+    const int item = w < ap.full ? w : ap.full + v / ap.S;
+    const int split = w < ap.full ? 0 : v % ap.S;
+    const int h = item % g.H;
+    const int tile = item / g.H;
     const int b = g.tile_seq[tile];
     const int r0 = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile;
     const int rend = g.seq_off[b + 1];
-    const int kbeg = split * g.kps;
-    const int kend = min(g.N, kbeg + g.kps);
+    // whole items cover every key; split units their range
+    const int kbeg = split * ap.kps;
+    const int kend = w < ap.full ? g.N : min(g.N, kbeg + ap.kps);
     const int nblk = (kend - kbeg + kKB - 1) / kKB;
     // this wave's 16 queries; lane column `col` is its query
     int qr = r0 + wid * 16 + col;
@@ -750,7 +784,7 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
     if (qvalid) {
-      if (g.splits == 1) {
+      if (w < ap.full) {
         const float inv = 1.0f / l_tot;
 #pragma unroll
         for (int df = 0; df < DH / 16; ++df) {
@@ -760,13 +794,15 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
           *reinterpret_cast<uint2*>(g.o + int64_t(qr) * g.d + h * DH + df * 16 + grp * 4) = st;
         }
       } else {
-        float* op = g.opart + (int64_t(split) * g.M_cap + qr) * g.d + h * DH;
+        // unit slot v: [kQTile query rows][DH] fp32 and [kQTile][2] (max, sum)
+        const int qi = wid * 16 + col;
+        float* op = g.opart + (int64_t(v) * kQTile + qi) * DH;
 #pragma unroll
         for (int df = 0; df < DH / 16; ++df)
           *reinterpret_cast<float4*>(op + df * 16 + grp * 4) =
               make_float4(acc_o[df][0], acc_o[df][1], acc_o[df][2], acc_o[df][3]);
         if (grp == 0) {
-          float* mlp = g.ml + ((int64_t(split) * g.M_cap + qr) * g.H + h) * 2;
+          float* mlp = g.ml + (int64_t(v) * kQTile + qi) * 2;
           mlp[0] = m_run;
           mlp[1] = l_tot;
         }
@@ -775,24 +811,32 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
   }
 }
 
-// merge the key splits of every (row, head): one wave per pair, fixed split order
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH) {
-  const int M = g.hdr[kHdrM];
+// merge the S units of every split item, one wave per (item, query row), in split order; exits at
+// once when the plan split nothing
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH, int attn_grid) {
+  const AttnPlan ap = attn_plan(g.hdr[kHdrTq] * g.H, attn_grid, g.N, g.S_max);
+  if (ap.rem == 0) return;
   const int lane = threadIdx.x & 63;
-  const int64_t pairs = int64_t(M) * g.H;
+  const int64_t pairs = int64_t(ap.rem) * kQTile;
   for (int64_t p = int64_t(blockIdx.x) * 4 + threadIdx.x / 64; p < pairs;
        p += int64_t(gridDim.x) * 4) {
-    const int r = int(p / g.H), h = int(p % g.H);
+    const int k = int(p / kQTile), j = int(p % kQTile);
+    const int item = ap.full + k;
+    const int h = item % g.H, tile = item / g.H;
+    const int b = g.tile_seq[tile];
+    const int r = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile + j;
+    if (r >= g.seq_off[b + 1]) continue;
     float mx = -INFINITY;
-    for (int s = 0; s < g.splits; ++s)
-      mx = fmaxf(mx, g.ml[((int64_t(s) * g.M_cap + r) * g.H + h) * 2]);
+    for (int s2 = 0; s2 < ap.S; ++s2)
+      mx = fmaxf(mx, g.ml[((int64_t(k) * ap.S + s2) * kQTile + j) * 2]);
     float l = 0.0f;
     float acc0 = 0.0f, acc1 = 0.0f;
-    for (int s = 0; s < g.splits; ++s) {
-      const float* mlp = g.ml + ((int64_t(s) * g.M_cap + r) * g.H + h) * 2;
+    for (int s2 = 0; s2 < ap.S; ++s2) {
+      const int64_t slot = (int64_t(k) * ap.S + s2) * kQTile + j;
+      const float* mlp = g.ml + slot * 2;
       const float f = __builtin_amdgcn_exp2f(mlp[0] - mx);
       l += mlp[1] * f;
-      const float* op = g.opart + (int64_t(s) * g.M_cap + r) * g.d + h * DH;
+      const float* op = g.opart + slot * DH;
       if (lane < DH) acc0 += op[lane] * f;
       if (lane + 64 < DH) acc1 += op[lane + 64] * f;
     }
@@ -807,7 +851,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH) {
 constexpr int kCUs = 256;
 
 struct Layout {
-  int M_cap, Tq_max, splits, kps;
+  int M_cap, Tq_max;
   size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, total;
 };
 
@@ -818,17 +862,6 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   const int64_t BN = int64_t(B) * N;
   L.M_cap = int(max_rows <= 0 || max_rows > BN ? BN : max_rows);
   L.Tq_max = (L.M_cap + kQTile - 1) / kQTile + B;
-  // split the keys when the query tiles alone cannot fill the chip
-  const int64_t est = int64_t((L.M_cap + kQTile - 1) / kQTile) * w->n_heads;
-  int splits = 1;
-  if (est < 2 * kCUs) {
-    splits = int((2 * kCUs + est - 1) / est);
-    const int max_splits = N / 128 > 1 ? N / 128 : 1;
-    splits = splits < max_splits ? splits : max_splits;
-    splits = splits < 1 ? 1 : splits;
-  }
-  L.kps = ((N + splits - 1) / splits + kKB - 1) / kKB * kKB;
-  L.splits = (N + L.kps - 1) / L.kps;  // every split starts below N
   const size_t d = size_t(w->d), F = size_t(w->ffn), M = size_t(L.M_cap);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -848,10 +881,9 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   L.h = take(2 * M * F);
   // split tail partials: at most 2 * (resident workgroups) tile segments of 128 x 128 fp32
   L.part = take(size_t(4) * 2 * (2 * kCUs) * CfgSmall::BM * CfgSmall::BN);
-  if (splits > 1) {
-    L.opart = take(4 * size_t(splits) * M * d);
-    L.ml = take(4 * size_t(splits) * M * w->n_heads * 2);
-  }
+  // attention split units: [kAttnMaxUnits][kQTile][head_dim] fp32 and [kAttnMaxUnits][kQTile][2]
+  L.opart = take(size_t(4) * kAttnMaxUnits * kQTile * w->head_dim);
+  L.ml = take(size_t(4) * kAttnMaxUnits * kQTile * 2);
   L.total = off;
   return L;
 }
@@ -933,8 +965,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   P.o = reinterpret_cast<uint16_t*>(ws + L.o);
   P.a = reinterpret_cast<float*>(ws + L.a);
   P.h = reinterpret_cast<uint16_t*>(ws + L.h);
-  P.opart = L.splits > 1 ? reinterpret_cast<float*>(ws + L.opart) : nullptr;
-  P.ml = L.splits > 1 ? reinterpret_cast<float*>(ws + L.ml) : nullptr;
+  P.opart = reinterpret_cast<float*>(ws + L.opart);
+  P.ml = reinterpret_cast<float*>(ws + L.ml);
   const int d = w->d, F = w->ffn, H = w->n_heads, DH = w->head_dim;
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
   int stage = 0;
@@ -998,12 +1030,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.N = N;
   aa.H = H;
   aa.d = d;
-  aa.splits = L.splits;
-  aa.kps = L.kps;
-  aa.M_cap = L.M_cap;
+  aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;  // key ranges of >= 128 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
-  const int64_t items = int64_t(L.Tq_max) * H * L.splits;
-  const int attn_blocks = int(items < 2 * kCUs ? items : 2 * kCUs);
+  const int attn_blocks = 2 * kCUs;  // persistent; the plan depends on the device row count
+  static_assert(2 * (2 * kCUs) <= kAttnMaxUnits, "attention split slots");
   if (DH == 128)
     hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
   else if (DH == 64)
@@ -1011,12 +1041,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   else
     hipLaunchKernelGGL(k_attn<32>, dim3(attn_blocks), dim3(256), 0, s, aa);
   DCU_LAUNCH_CHECK();
-  if (L.splits > 1) {
-    const int64_t pairs = int64_t(L.M_cap) * H;
-    const int cb = int((pairs + 3) / 4 < 4096 ? (pairs + 3) / 4 : 4096);
-    hipLaunchKernelGGL(k_attn_combine, dim3(cb), dim3(256), 0, s, aa, DH);
-    DCU_LAUNCH_CHECK();
-  }
+  // the merge exits at once unless the device-side plan split the items
+  hipLaunchKernelGGL(k_attn_combine, dim3(kCUs), dim3(256), 0, s, aa, DH, attn_blocks);
+  DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
   // output projection + residual -> a (fp32)
