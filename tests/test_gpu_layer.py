@@ -172,3 +172,26 @@ def test_full_size_batched_sampled():
     for bb in range(8):
         keep = np.setdiff1d(np.arange(1024), sel[bb, :cnt[bb]])
         assert np.array_equal(got[2][bb, keep], case.y[bb, keep])
+
+
+def test_full_size_batch8_n2048_sampled():
+    """Batched layer at N = 2048 (1024 prompt + 1024 generated), batch 8, LLaDA-8B shapes, budget 64
+    plus a 32-wide window per sequence (~96 rows each, some ragged); the oracle recomputes one
+    sequence whole and every other sequence is checked untouched outside its selection."""
+    _log("layer full size batch 8 N 2048")
+    shape = synth.LLADA8B
+    case = Case(shape, 8, 2048, seed=6)
+    counts = [96, 130, 64, 100, 81, 120, 96, 111]
+    sel, cnt = _random_selection(case.g, 8, 2048, counts)
+    (got,) = case.run_gpu(sel, cnt)
+    b = 5
+    ref = olayer.selective_layer(case.w, shape.n_heads, shape.head_dim, shape.eps,
+                                 case.x[b:b + 1], sel[b:b + 1], cnt[b:b + 1], case.kc[b:b + 1],
+                                 case.vc[b:b + 1], case.y[b:b + 1])
+    sub = Case.__new__(Case)
+    sub.kc, sub.vc, sub.y, sub.N = case.kc[b:b + 1], case.vc[b:b + 1], case.y[b:b + 1], 2048
+    _compare(sub, tuple(t[b:b + 1] for t in got), ref, _rows(sel[b:b + 1], cnt[b:b + 1], 1, 2048))
+    for bb in range(8):
+        keep = np.setdiff1d(np.arange(2048), sel[bb, :cnt[bb]])
+        assert np.array_equal(got[2][bb, keep], case.y[bb, keep])
+        assert np.array_equal(got[0][bb, keep], case.kc[bb, keep])
