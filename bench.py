@@ -1,21 +1,28 @@
 #!/usr/bin/env python3
-"""Benchmark of one full DCU denoising step plus the end of step, on one MI355X.
+"""Benchmark of the DCU hot path on one MI355X.
 
-Workload (synthetic, seeded, LLaDA-8B-shaped, bf16): batch 8, N = 1024 tokens, 32 layers of
-d = 4096 (32 heads x 128), SwiGLU FFN 12288. Per step: budgets from the previous step's layer
-means (B_layer = 32), then for every layer the token distance against the cached input, top-B plus
-window selection (B_window = 32 around 4 key positions per sequence in [512, 1024)), and the
-selective layer on the selected rows; then confidence over [8 x 256, 126464] logits with a planted
-peak and the Frechet commit (delta = 0.1). Layer inputs drift by N(0, sigma_l^2),
-sigma_l = 0.01 (1 + l/8), on a random 30% of each sequence's rows (open loop: every step sees the
-same drift, so the cache roll, a pointer swap, is not performed).
+Default workload (synthetic, seeded, LLaDA-8B-shaped, bf16): one full DCU denoising step plus the
+end of step. Batch 8, N = 1024 tokens, 32 layers of d = 4096 (32 heads x 128), SwiGLU FFN 12288.
+Per step: budgets from the previous step's layer means (B_layer = 32), then for every layer the
+token distance against the cached input, top-B plus window selection (B_window = 32 around 4 key
+positions per sequence in [512, 1024)), and the selective layer on the selected rows; then
+confidence over [8 x 256, 126464] logits with a planted peak and the Frechet commit (delta = 0.1).
+Layer inputs drift by N(0, sigma_l^2), sigma_l = 0.01 (1 + l/8), on a random 30% of each
+sequence's rows (open loop: every step sees the same drift, so the cache roll, a pointer swap, is
+not performed).
 
 Prints ONE JSON line: value = selective layer-steps/s (32 layer-steps per denoising step, end of
 step included in the time), plus recomputed tokens/s, per-stage times, the roofline of the
 dominant kernel (timed live with HIP events on the library's stream), the dense-recompute layer at
-the same shape, and the CPU oracle timed on a bounded sample of the same workload.
+the same shape (this library with every row selected, and a PyTorch reference of the same layer),
+and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+                    [--workload step|dist-select|layer-b1|layer-b8-n2048]
+
+The other workloads use the same machinery at other shapes: distance + budget + select only for 32
+layers at batch 1; one selective layer at batch 1 (~64 rows: budget 32 + a 32-wide window); the
+32-layer step without its end at batch 8, N = 2048, B_layer = 64.
 """
 from __future__ import annotations
 
@@ -33,11 +40,28 @@ METRIC = "selective layer-steps/s and recomputed tokens/s at N=1024; % HBM/MFMA 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
-B, N, L = 8, 1024, 32
+L = 32
 D, H, DH, F = 4096, 32, 128, 12288
 V, M_CAND = 126464, 256
-B_LAYER, B_WINDOW, N_KEYS, DELTA = 32, 32, 4, 0.1
-CFG = 5
+B_WINDOW, DELTA = 32, 0.1
+
+# name -> shape of the run; sigma(l) is the drift of layer l's inputs
+WORKLOADS = {
+    "step": dict(B=8, N=1024, L=32, b_layer=32, n_keys=4, key_lo=512, cfg=5, layers=True, end=True,
+                 sigma=lambda l: 0.01 * (1 + l / 8),
+                 desc="full 32-layer DCU denoising step + end of step (confidence over [8x256, 126464] "
+                      "logits, Frechet commit delta=0.1); LLaDA-8B-shaped layers, bf16"),
+    "dist-select": dict(B=1, N=1024, L=32, b_layer=32, n_keys=4, key_lo=512, cfg=2, layers=False,
+                        end=False, sigma=lambda l: 0.01 * (1 + l / 8),
+                        desc="distance + budget + select for 32 layers, batch 1, N=1024, d=4096, bf16"),
+    "layer-b1": dict(B=1, N=1024, L=1, b_layer=32, n_keys=1, key_lo=512, cfg=3, layers=True, end=False,
+                     sigma=lambda l: 0.01 * (1 + 31 / 8),
+                     desc="one selective LLaDA-8B-shaped layer, batch 1, N=1024, budget 32 + window 32"),
+    "layer-b8-n2048": dict(B=8, N=2048, L=32, b_layer=64, n_keys=4, key_lo=1024, cfg=4, layers=True,
+                           end=False, sigma=lambda l: 0.01 * (1 + l / 8),
+                           desc="32-layer DCU step without its end, batch 8, N=2048, B_layer=64, "
+                                "LLaDA-8B-shaped layers, bf16"),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_swiglu.json")
 KERNEL_SOURCES = ["selective_token_cache_amd/csrc/layer.hip", "selective_token_cache_amd/csrc/gemm.h",
                   "selective_token_cache_amd/csrc/common.h"]
@@ -55,7 +79,7 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def stage_flops_bytes(M: int):
+def stage_flops_bytes(M: int, B: int, N: int):
     """Algorithmic flops and HBM bytes of one layer's stages for M recomputed rows (whole batch)."""
     w = 2  # bf16
     return {
@@ -159,6 +183,31 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, bench_json, steps, cmds
     print(out)
 
 
+def torch_dense_layer(w, x, eps):
+    """PyTorch reference of the dense layer (every row recomputed), a cross-check outside the
+    library: vendor GEMMs (torch.nn.functional.linear on 2-D operands) and attention as two
+    batched products on contiguous bf16 operands with an fp32 softmax."""
+    import torch
+    import torch.nn.functional as Fn
+
+    Bsz, Nseq, d = x.shape
+    x2 = x.reshape(Bsz * Nseq, d)
+
+    def rms(t, g):
+        t32 = t.float()
+        return (t32 * torch.rsqrt(t32.pow(2).mean(-1, keepdim=True) + eps) * g.float()).to(torch.bfloat16)
+
+    qkv = Fn.linear(rms(x2, w["g_attn"]), w["w_qkv"])
+    q, k, v = (t.reshape(Bsz, Nseq, H, DH).transpose(1, 2).contiguous() for t in qkv.split(d, dim=1))
+    s = torch.matmul(q, k.transpose(-1, -2).contiguous()).float() * (1.0 / DH ** 0.5)
+    p = torch.softmax(s, dim=-1).to(torch.bfloat16)
+    o = torch.matmul(p, v).transpose(1, 2).reshape(Bsz * Nseq, d)
+    a = x2.float() + Fn.linear(o, w["w_o"]).float()
+    an = rms(a, w["g_ffn"])
+    h = (Fn.silu(Fn.linear(an, w["w_gate"]).float()) * Fn.linear(an, w["w_up"]).float()).to(torch.bfloat16)
+    return (a + Fn.linear(h, w["w_down"]).float()).to(torch.bfloat16)
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         a = sys.argv[2:]
@@ -168,6 +217,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="step", choices=sorted(WORKLOADS))
     ap.add_argument("--dense-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -177,6 +227,8 @@ def main():
         print(f"bench.py runs on one GPU only (the path is measured on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    wl = WORKLOADS[args.workload]
+    B, N, L_, B_LAYER, N_KEYS, CFG = wl["B"], wl["N"], wl["L"], wl["b_layer"], wl["n_keys"], wl["cfg"]
 
     import torch
 
@@ -192,62 +244,94 @@ def main():
     torch.cuda.set_device(dev)
 
     # ------------------------------------------------------------------ inputs in HBM
-    log("generating inputs")
+    log(f"generating inputs ({args.workload})")
     layers, x_cur, x_prev, kc, vc, y = [], [], [], [], [], []
-    for l in range(L):
-        w = wd.layer_weights(D, F, 0.02, CFG, l, device=dev)
-        layers.append((stc.Layer(D, H, DH, F, 1e-5, w["w_qkv"], w["w_o"], w["w_gate"], w["w_up"],
-                                 w["w_down"], w["g_attn"], w["g_ffn"]), w))
-        xc, xp = wd.drift_inputs(B, N, D, 0.3, 0.01 * (1 + l / 8), CFG, l, device=dev)
+    for l in range(L_):
+        if wl["layers"]:
+            w = wd.layer_weights(D, F, 0.02, CFG, l, device=dev)
+            layers.append((stc.Layer(D, H, DH, F, 1e-5, w["w_qkv"], w["w_o"], w["w_gate"], w["w_up"],
+                                     w["w_down"], w["g_attn"], w["g_ffn"]), w))
+            kc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
+            vc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
+            y.append(torch.empty((B, N, D), dtype=torch.bfloat16, device=dev))
+        xc, xp = wd.drift_inputs(B, N, D, 0.3, wl["sigma"](l), CFG, l, device=dev)
         x_cur.append(xc)
         x_prev.append(xp)
-        kc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
-        vc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
-        y.append(torch.empty((B, N, D), dtype=torch.bfloat16, device=dev))
-    logits = wd.planted_logits(B * M_CAND, V, CFG, device=dev)
-    keys = wd.key_positions(B, N_KEYS, N // 2, N, CFG, device=dev)
-    lay0 = layers[0][0]
-    ws = torch.empty((lay0.workspace_bytes(B, N, B * N),), dtype=torch.uint8, device=dev)
+    logits = wd.planted_logits(B * M_CAND, V, CFG, device=dev) if wl["end"] else None
+    keys = wd.key_positions(B, N_KEYS, wl["key_lo"], N, CFG, device=dev)
+    ws = None
+    if wl["layers"]:
+        ws = torch.empty((layers[0][0].workspace_bytes(B, N, B * N),), dtype=torch.uint8, device=dev)
     dist = torch.empty((B, N), dtype=torch.float32, device=dev)
-    s_buf = [torch.zeros((L, B), dtype=torch.float32, device=dev) for _ in range(2)]
-    budgets = torch.empty((B, L), dtype=torch.int32, device=dev)
-    sel_idx = torch.empty((L, B, N), dtype=torch.int32, device=dev)
-    sel_cnt = torch.empty((L, B), dtype=torch.int32, device=dev)
+    s_buf = [torch.zeros((L_, B), dtype=torch.float32, device=dev) for _ in range(2)]
+    budgets = torch.empty((B, L_), dtype=torch.int32, device=dev)
+    sel_idx = torch.empty((L_, B, N), dtype=torch.int32, device=dev)
+    sel_cnt = torch.empty((L_, B), dtype=torch.int32, device=dev)
     conf = torch.empty((B * M_CAND,), dtype=torch.float32, device=dev)
     tok = torch.empty((B * M_CAND,), dtype=torch.int32, device=dev)
     n_commit = torch.empty((B,), dtype=torch.int32, device=dev)
     order = torch.empty((B, M_CAND), dtype=torch.int32, device=dev)
 
     # dense fill of every layer's caches from the cached inputs (setup, untimed)
-    log("dense fill")
-    for l in range(L):
-        stc.dcu_selective_layer(layers[l][0], x_prev[l], None, None, kc[l], vc[l], y[l],
-                                max_rows=B * N, workspace=ws)
-    torch.cuda.synchronize()
+    if wl["layers"]:
+        log("dense fill")
+        for l in range(L_):
+            stc.dcu_selective_layer(layers[l][0], x_prev[l], None, None, kc[l], vc[l], y[l],
+                                    max_rows=B * N, workspace=ws)
+        torch.cuda.synchronize()
 
-    n_ev_layer = 2 + len(LAYER_STAGES) + 1
+    stages = list(LAYER_STAGES) if wl["layers"] else []
+    n_ev_layer = 2 + len(stages) + 1 if wl["layers"] else 3
+
+    def rec(e, i):
+        if e is not None and e[i] is not None:
+            e[i].record()
 
     def step(s_prev, s_cur, ev=None):
-        stc.dcu_budget(s_prev, B, L, B_LAYER, out=budgets)
-        for l in range(L):
+        stc.dcu_budget(s_prev, B, L_, B_LAYER, out=budgets)
+        for l in range(L_):
             e = ev[l] if ev is not None else None
-            if e:
-                e[0].record()
+            rec(e, 0)
             stc.dcu_distance(x_cur[l], x_prev[l], dist=dist, mean=s_cur[l])
-            if e:
-                e[1].record()
+            rec(e, 1)
             stc.dcu_select(dist, budgets, l, keys, B_WINDOW, sel_idx=sel_idx[l], sel_count=sel_cnt[l])
-            stc.dcu_selective_layer(layers[l][0], x_cur[l], sel_idx[l], sel_cnt[l], kc[l], vc[l], y[l],
-                                    max_rows=B * N, workspace=ws, events=e[2:] if e else None)
-        e = ev[L] if ev is not None else None
-        if e:
-            e[0].record()
+            if wl["layers"]:
+                le = e[2:] if e is not None and any(x is not None for x in e[2:]) else None
+                stc.dcu_selective_layer(layers[l][0], x_cur[l], sel_idx[l], sel_cnt[l], kc[l], vc[l],
+                                        y[l], max_rows=B * N, workspace=ws, events=le)
+            else:
+                rec(e, 2)
+        if not wl["end"]:
+            return
+        e = ev[L_] if ev is not None else None
+        rec(e, 0)
         stc.dllm_confidence(logits, V, conf=conf, token=tok)
-        if e:
-            e[1].record()
+        rec(e, 1)
         stc.frechet_commit(conf.view(B, M_CAND), DELTA, n_commit=n_commit, order=order)
-        if e:
-            e[2].record()
+        rec(e, 2)
+
+    def make_events(full):
+        """Events of one step: every stage boundary (full), or only the two around the roofline
+        kernel (each recorded event costs device time, so the timed steps carry only those)."""
+        def ev():
+            return torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(L_):
+            if full:
+                per.append([ev() for _ in range(n_ev_layer)])
+            elif wl["layers"]:
+                g = [None] * n_ev_layer
+                gi = 2 + stages.index("gate_up_swiglu")
+                g[gi], g[gi + 1] = ev(), ev()
+                per.append(g)
+            else:
+                per.append([ev(), ev(), None])
+        per.append([ev() for _ in range(3)] if full else [None, None, None])
+        for group in per:  # create the event handles before they are passed to the library
+            for x in group:
+                if x is not None:
+                    x.record()
+        return per
 
     # warm-up: the first step has no previous means (uniform budgets)
     log(f"warmup {args.warmup}")
@@ -260,16 +344,10 @@ def main():
     torch.cuda.synchronize()
 
     # ------------------------------------------------------------------ timed region
+    # K steps with only the roofline kernel's events, then a few instrumented steps with an event
+    # at every stage boundary for the per-stage table
     K = args.steps
-    evs = []
-    for _ in range(K):
-        per = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev_layer)] for _ in range(L)]
-        per.append([torch.cuda.Event(enable_timing=True) for _ in range(3)])
-        evs.append(per)
-    for per in evs:  # create the event handles before they are passed to the library
-        for group in per:
-            for e in group:
-                e.record()
+    evs = [make_events(False) for _ in range(K)]
     torch.cuda.synchronize()
     log(f"timing {K} steps")
     t0 = time.perf_counter()
@@ -279,35 +357,43 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / K * 1e3
+    roof_ms = [0.0] * L_           # roofline kernel time per layer, summed over the timed steps
+    for it in range(K):
+        for l in range(L_):
+            e = evs[it][l]
+            if wl["layers"]:
+                gi = 2 + stages.index("gate_up_swiglu")
+                roof_ms[l] += e[gi].elapsed_time(e[gi + 1])
+            else:
+                roof_ms[l] += e[0].elapsed_time(e[1])
+
+    KI = min(K, 5)
+    ievs = [make_events(True) for _ in range(KI)]
+    torch.cuda.synchronize()
+    log(f"instrumented {KI} steps")
+    for it in range(KI):
+        step(s_buf[cur ^ 1], s_buf[cur], ievs[it])
+        cur ^= 1
+    torch.cuda.synchronize()
 
     counts = sel_cnt.cpu().numpy()            # same selection every step (open loop)
     M_l = counts.sum(axis=1)                   # rows recomputed per layer (whole batch)
     rows_step = int(M_l.sum())
 
-    # per-stage device times (ms), averaged over steps; per layer lists for the GEMM roofline
-    names = ["distance", "select"] + list(LAYER_STAGES)
+    # per-stage device times (ms) of the instrumented steps
+    names = ["distance", "select"] + stages
     stage_ms = {n: 0.0 for n in names}
-    gateup_ms = [0.0] * L
-    for it in range(K):
-        for l in range(L):
-            e = evs[it][l]
+    for it in range(KI):
+        for l in range(L_):
+            e = ievs[it][l]
             for i, n in enumerate(names):
-                t = e[i].elapsed_time(e[i + 1])
-                stage_ms[n] += t
-                if n == "gate_up_swiglu":
-                    gateup_ms[l] += t
-    end_ms = {"confidence": 0.0, "commit": 0.0}
-    for it in range(K):
-        e = evs[it][L]
-        end_ms["confidence"] += e[0].elapsed_time(e[1])
-        end_ms["commit"] += e[1].elapsed_time(e[2])
-
+                stage_ms[n] += e[i].elapsed_time(e[i + 1])
     kernels = {}
     for n in names:
-        per_layer_ms = stage_ms[n] / (K * L)
-        fb = [stage_flops_bytes(int(m))[n] for m in M_l]
-        flops = sum(x.get("flops", 0) for x in fb) / L
-        byts = sum(x.get("bytes", 0) for x in fb) / L
+        per_layer_ms = stage_ms[n] / (KI * L_)
+        fb = [stage_flops_bytes(int(m), B, N)[n] for m in M_l]
+        flops = sum(x.get("flops", 0) for x in fb) / L_
+        byts = sum(x.get("bytes", 0) for x in fb) / L_
         k = {"us_per_layer": round(per_layer_ms * 1e3, 2)}
         if byts:
             k["GBps"] = round(byts / (per_layer_ms * 1e-3) / 1e9, 1)
@@ -316,34 +402,60 @@ def main():
             k["TFLOPps"] = round(flops / (per_layer_ms * 1e-3) / 1e12, 1)
             k["mfma_frac"] = round(k["TFLOPps"] / MFMA_BF16_PEAK_TFLOPS, 3)
         kernels[n] = k
-    for n in end_ms:
-        us = end_ms[n] / K * 1e3
-        kernels[n] = {"us_per_step": round(us, 2)}
-    conf_bytes = B * M_CAND * V * 2
-    kernels["confidence"]["GBps"] = round(conf_bytes / (end_ms["confidence"] / K * 1e-3) / 1e9, 1)
-    kernels["confidence"]["hbm_frac"] = round(kernels["confidence"]["GBps"] / HBM_PEAK_GBS, 3)
+    if wl["end"]:
+        end_ms = {"confidence": 0.0, "commit": 0.0}
+        for it in range(KI):
+            e = ievs[it][L_]
+            end_ms["confidence"] += e[0].elapsed_time(e[1])
+            end_ms["commit"] += e[1].elapsed_time(e[2])
+        for n in end_ms:
+            kernels[n] = {"us_per_step": round(end_ms[n] / KI * 1e3, 2)}
+        conf_bytes = B * M_CAND * V * 2
+        kernels["confidence"]["GBps"] = round(conf_bytes / (end_ms["confidence"] / KI * 1e-3) / 1e9, 1)
+        kernels["confidence"]["hbm_frac"] = round(kernels["confidence"]["GBps"] / HBM_PEAK_GBS, 3)
 
-    # roofline of the dominant kernel: gate/up projection with the SwiGLU epilogue
-    gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l in range(L)) * K
-    gu_time = sum(gateup_ms) * 1e-3
-    achieved = gu_flops / gu_time / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tj = json.load(open(TRAFFIC_FILE))
-            if tj.get("source_sha256") == source_hash():
-                traffic = tj.get("traffic_bytes_per_launch")
-        except Exception:  # pragma: no cover
+    # roofline of the dominant kernel, timed with HIP events on the library's stream
+    if wl["layers"]:
+        gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l in range(L_)) * K
+        gu_time = sum(roof_ms) * 1e-3
+        gu_bytes = (2.0 * F * D * 2) * L_ * K
+        if float(M_l.mean()) >= 312:
+            # MFMA-bound at these row counts: gate/up projection with the SwiGLU epilogue
+            achieved = gu_flops / gu_time / 1e12
             traffic = None
-    roofline = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU)", "bound": "mfma",
-                "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                "algorithmic_flops_per_launch": int(gu_flops / (K * L)),
-                "avg_launch_us": round(gu_time / (K * L) * 1e6, 2)}
+            if args.workload == "step" and os.path.exists(TRAFFIC_FILE):
+                try:
+                    tj = json.load(open(TRAFFIC_FILE))
+                    if tj.get("source_sha256") == source_hash():
+                        traffic = tj.get("traffic_bytes_per_launch")
+                except Exception:  # pragma: no cover
+                    traffic = None
+            roofline = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU)", "bound": "mfma",
+                        "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": traffic, "algorithmic_flops_per_launch": int(gu_flops / (K * L_)),
+                        "avg_launch_us": round(gu_time / (K * L_) * 1e6, 2)}
+        else:
+            # few rows: the projection streams its weights once per layer-step (HBM-bound)
+            achieved = gu_bytes / gu_time / 1e9
+            roofline = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU)", "bound": "hbm",
+                        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": int(gu_bytes / (K * L_)),
+                        "avg_launch_us": round(gu_time / (K * L_) * 1e6, 2)}
+    else:
+        d_ms = sum(roof_ms) / (K * L_)
+        d_bytes = 2.0 * B * N * D * 2 + B * N * 4
+        roofline = {"kernel": "k_distance + k_group_mean (cosine distance and layer mean)", "bound": "hbm",
+                    "achieved": round(d_bytes / (d_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "traffic": None, "algorithmic_bytes_per_launch": int(d_bytes),
+                    "avg_launch_us": round(d_ms * 1e3, 2)}
 
     # ------------------------------------------------------------------ dense recompute, same shape
     dense = None
-    if args.dense_layers > 0:
+    n_dense = min(args.dense_layers, L_) if wl["layers"] else 0
+    if n_dense > 0:
         log("dense layers")
         kd = torch.empty_like(kc[0])
         vd = torch.empty_like(vc[0])
@@ -352,27 +464,48 @@ def main():
                                 workspace=ws)
         torch.cuda.synchronize()
         dev_ev = []
-        for l in range(args.dense_layers):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(len(LAYER_STAGES) + 1)]
+        gi = stages.index("gate_up_swiglu")
+        for l in range(n_dense):
+            # marks only at the start, around the gate/up projection and at the end
+            e = [torch.cuda.Event(enable_timing=True) if i in (0, gi, gi + 1, len(stages)) else None
+                 for i in range(len(stages) + 1)]
             for x in e:
-                x.record()
+                if x is not None:
+                    x.record()
             dev_ev.append(e)
         torch.cuda.synchronize()
-        for l in range(args.dense_layers):
+        for l in range(n_dense):
             stc.dcu_selective_layer(layers[l][0], x_cur[l], None, None, kd, vd, yd, max_rows=B * N,
                                     workspace=ws, events=dev_ev[l])
         torch.cuda.synchronize()
-        d_ms = sum(e[0].elapsed_time(e[-1]) for e in dev_ev) / args.dense_layers
-        d_gu = sum(e[LAYER_STAGES.index("gate_up_swiglu")].elapsed_time(
-            e[LAYER_STAGES.index("gate_up_swiglu") + 1]) for e in dev_ev) / args.dense_layers
-        sel_ms = (stage_ms["distance"] + stage_ms["select"] +
-                  sum(stage_ms[n] for n in LAYER_STAGES)) / (K * L)
+        d_ms = sum(e[0].elapsed_time(e[-1]) for e in dev_ev) / n_dense
+        d_gu = sum(e[gi].elapsed_time(e[gi + 1]) for e in dev_ev) / n_dense
+        # selective layer-step from the timed (uninstrumented) steps, end of step excluded
+        sel_ms = ms_step / L_ - (sum(end_ms.values()) / KI / L_ if wl["end"] else 0.0)
         dense_flops = 2.0 * B * N * (4 * D * D + 3 * D * F) + 4.0 * B * N * N * D
         dense = {"layer_ms": round(d_ms, 3), "selective_layer_step_ms": round(sel_ms, 3),
                  "speedup_selective_vs_dense": round(d_ms / sel_ms, 2),
                  "dense_TFLOPps": round(dense_flops / (d_ms * 1e-3) / 1e12, 1),
                  "dense_gate_up_TFLOPps": round(2.0 * B * N * 2 * F * D / (d_gu * 1e-3) / 1e12, 1),
                  "rows": B * N}
+        # the same dense layer written with PyTorch operators (vendor GEMMs), as a cross-check
+        log("torch dense reference")
+        del kd, vd, yd
+        w0 = layers[0][1]
+        with torch.no_grad():
+            for _ in range(2):
+                torch_dense_layer(w0, x_cur[0], 1e-5)
+            torch.cuda.synchronize()
+            t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            t_ev[0].record()
+            for _ in range(3):
+                torch_dense_layer(w0, x_cur[0], 1e-5)
+            t_ev[1].record()
+            torch.cuda.synchronize()
+        t_ms = t_ev[0].elapsed_time(t_ev[1]) / 3
+        dense["torch_layer_ms"] = round(t_ms, 3)
+        dense["speedup_selective_vs_torch_dense"] = round(t_ms / sel_ms, 2)
+        torch.cuda.empty_cache()
 
     if args.calib_copy:
         log("calibration copy")
@@ -386,11 +519,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        cpu = cpu_baseline(layers, x_cur, x_prev, kc, vc, y, s_buf[cur ^ 1], keys, logits, torch)
+        cpu = cpu_baseline(wl, layers, x_cur, x_prev, kc, vc, y, s_buf[cur ^ 1], keys, logits, torch)
 
     out = {
         "metric": METRIC,
-        "value": round(L / (ms_step * 1e-3), 2),
+        "value": round(L_ / (ms_step * 1e-3), 2),
         "unit": "layer-steps/s",
         "n_gpus": 1,
         "steps": K,
@@ -401,12 +534,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "full 32-layer DCU denoising step + end of step (confidence over "
-                               "[8x256, 126464] logits, Frechet commit delta=0.1); LLaDA-8B-shaped "
-                               "layers, bf16",
-                   "batch": B, "seq_len": N, "layers": L, "d": D, "heads": H, "head_dim": DH,
-                   "ffn": F, "vocab": V, "b_layer": B_LAYER, "b_window": B_WINDOW,
-                   "keys_per_seq": N_KEYS, "drift_rows": 0.3, "parallelism": "single GPU"},
+        "config": {"workload": wl["desc"], "batch": B, "seq_len": N, "layers": L_, "d": D, "heads": H,
+                   "head_dim": DH, "ffn": F, "vocab": V if wl["end"] else None, "b_layer": B_LAYER,
+                   "b_window": B_WINDOW, "keys_per_seq": N_KEYS, "drift_rows": 0.3,
+                   "parallelism": "single GPU"},
         "recomputed_tokens_per_s": round(rows_step / (ms_step * 1e-3), 1),
         "rows_per_step": rows_step,
         "rows_per_layer_min_max": [int(M_l.min()), int(M_l.max())],
@@ -415,13 +546,16 @@ def main():
         "dense": dense,
         "cpu_baseline": cpu,
     }
+    if not wl["layers"]:
+        out["metric"] = "distance+budget+select layer-steps/s at N=1024; % HBM peak"
+        out["recomputed_tokens_per_s"] = None
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(layers, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, torch):
-    """The numpy oracle, untuned, on a bounded sample of the same step: 8 of the 32 layers for the
-    whole batch (distance, select, selective layer) plus the end of step on 1/8 of the candidate
-    rows; scaled to layer-steps/s of the full step (32 layers + full end of step)."""
+def cpu_baseline(wl, layers, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, torch):
+    """The numpy oracle, untuned, on a bounded sample of the same workload: a subset of the layers
+    for the whole batch (distance, select, and the selective layer when the workload has one) plus
+    the end of step on 1/8 of the candidate rows; scaled to layer-steps/s of the whole step."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -432,36 +566,46 @@ def cpu_baseline(layers, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, tor
     from oracle import layer as olayer
     from oracle import select as osel
 
+    B, L_ = wl["B"], wl["L"]
+
     def h16(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    sample_layers = list(range(0, L, 4))
+    if wl["layers"]:
+        sample_layers = list(range(0, L_, 4)) if wl["N"] <= 1024 else [0, 16]
+    else:
+        sample_layers = list(range(L_))
     host = []
     for l in sample_layers:
-        w = {k: h16(v) for k, v in layers[l][1].items()}
-        host.append((w, h16(x_cur[l]), h16(x_prev[l]), h16(kc[l]), h16(vc[l]), h16(y[l])))
+        w = {k: h16(v) for k, v in layers[l][1].items()} if wl["layers"] else None
+        lay = (h16(kc[l]), h16(vc[l]), h16(y[l])) if wl["layers"] else None
+        host.append((w, h16(x_cur[l]), h16(x_prev[l]), lay))
     s_prev = s_prev_dev.cpu().numpy().T.copy()     # [B, L]
     kp = keys.cpu().numpy()
-    lg = h16(logits[: B * M_CAND // 8])
     t0 = time.perf_counter()
-    bud = obud.layer_budget(s_prev, B, L, B_LAYER)
-    for (w, xc, xp, k_, v_, y_), l in zip(host, sample_layers):
+    bud = obud.layer_budget(s_prev, B, L_, wl["b_layer"])
+    for (w, xc, xp, lay), l in zip(host, sample_layers):
         d, _ = odist.distance_and_mean(xc, xp)
         sel, cnt = osel.select(d, bud, l, kp, B_WINDOW)
-        olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, k_, v_, y_)
+        if lay is not None:
+            olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, *lay)
     t_layer = (time.perf_counter() - t0) / len(sample_layers)
-    t1 = time.perf_counter()
-    c, _ = oconf.confidence(lg, V)
-    ofre.frechet_commit(c.reshape(B // 8, M_CAND), None, DELTA)
-    t_end = (time.perf_counter() - t1) * 8
-    t_step = L * t_layer + t_end
+    t_end = 0.0
+    if wl["end"]:
+        lg = h16(logits[: B * M_CAND // 8])
+        t1 = time.perf_counter()
+        c, _ = oconf.confidence(lg, V)
+        ofre.frechet_commit(c.reshape(B // 8, M_CAND), None, DELTA)
+        t_end = (time.perf_counter() - t1) * 8
+    t_step = L_ * t_layer + t_end
     sample_s = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(L / t_step, 4), "unit": "layer-steps/s", "cores": int(threads),
+    what = "distance, select, selective layer" if wl["layers"] else "distance, select"
+    end = " plus confidence/commit on 1/8 of the candidate rows" if wl["end"] else ""
+    return {"value": round(L_ / t_step, 4), "unit": "layer-steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"numpy fp64 oracle on layers {sample_layers} of the batch-8 step (distance, "
-                      f"select, selective layer) plus confidence/commit on 1/8 of the 2048 "
-                      f"candidate rows; scaled to a 32-layer step with full end of step",
+            "sample": f"numpy fp64 oracle on layers {sample_layers} of the batch-{B} step ({what})"
+                      f"{end}; scaled to the whole {L_}-layer step",
             "sample_seconds": round(sample_s, 2),
             "cpu_layer_step_s": round(t_layer, 3)}
 

@@ -175,7 +175,9 @@ int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel
  * (A fixup kernel finishes the tiles whose K range was split over idle workgroups; it exits at
  * once when the projection did not split.)
  * events may be NULL (then this is dcu_selective_layer); otherwise n_events must be at least
- * DCU_LAYER_STAGES + 1 (EINVAL). A failed event record returns DCU_EHIP.
+ * DCU_LAYER_STAGES + 1 (EINVAL), and a NULL entry skips that mark (each recorded event costs a
+ * few microseconds of device time, so a caller timing one stage passes only its two events).
+ * A failed event record returns DCU_EHIP.
  */
 #define DCU_LAYER_STAGES 11
 int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,

@@ -199,9 +199,9 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
                         stream=None, events=None):
     """Recompute the selected rows in place (k_cache, v_cache, y_out are in/out).
 
-    events: optional sequence of len(LAYER_STAGES) + 1 torch.cuda.Event(enable_timing=True);
-    event 0 is recorded before the first kernel and event i after stage i, on the library's
-    stream (dcu_selective_layer_staged)."""
+    events: optional sequence of len(LAYER_STAGES) + 1 torch.cuda.Event(enable_timing=True) or
+    None; event 0 is recorded before the first kernel and event i after stage i, on the library's
+    stream (dcu_selective_layer_staged); a None entry skips that mark."""
     _need(x_in, "x_in", torch.bfloat16)
     B, N, d = x_in.shape
     if d != layer.d:
@@ -227,7 +227,7 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
     else:
         if len(events) < len(LAYER_STAGES) + 1:
             raise ValueError(f"need {len(LAYER_STAGES) + 1} events")
-        arr = (_vp * len(events))(*[_vp(e.cuda_event) for e in events])
+        arr = (_vp * len(events))(*[_vp(e.cuda_event if e is not None else None) for e in events])
         st = load().dcu_selective_layer_staged(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
                                                _p(sel_count), B, N, max_rows, _p(k_cache),
                                                _p(v_cache), _p(y_out), _p(workspace),

@@ -259,7 +259,7 @@ struct GemmArgs {
 // along K into S segments whose fp32 partial tiles go to the workspace; k_gemm_fixup sums them in
 // segment order and applies the epilogue (deterministic, no atomics). S depends on the row count, so
 // it is chosen on the device; kernel and fixup evaluate the same function.
-constexpr int kMaxSplitK = 4;
+constexpr int kMaxSplitK = 16;  // few rows (batch 1) need many segments to fill the chip
 
 struct SplitPlan {
   int full;  // tiles computed whole (ids 0 .. full-1)
@@ -402,6 +402,7 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm) {
         const int r = wm * C::WM + fm * 16 + (lane & 15);
+        if (m_t * C::BM + r >= M) continue;  // rows past M are never read back
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) {
           const int c = wn * C::WN + fn * 16 + (lane >> 4) * 4;
@@ -414,9 +415,10 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
 }
 
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
-// thread and item, kFixupU items per thread and round, with every partial of those items loaded
-// before any is used (memory-level parallelism). Exits at once when the GEMM did not split.
-constexpr int kFixupU = 2;
+// thread and item, kFixupU items per thread and round, with kFixupChunk partials of those items
+// loaded before any is added (memory-level parallelism). Exits at once when the GEMM did not split.
+constexpr int kFixupU = 1;
+constexpr int kFixupChunk = 8;
 
 template <int EPI, class C>
 __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
@@ -434,7 +436,8 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < total;
        i0 += stride * kFixupU) {
     float4 v[kFixupU][NV];
-    int m_u[kFixupU], col_u[kFixupU], nt_u[kFixupU];
+    int m_u[kFixupU], col_u[kFixupU], nt_u[kFixupU], cols_u[kFixupU][NV];
+    const float* pt_u[kFixupU];
     bool ok[kFixupU];
 #pragma unroll
     for (int u = 0; u < kFixupU; ++u) {
@@ -458,24 +461,36 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
       } else {
         cols[0] = c4;
       }
-      const float* pt = g.part + int64_t(ok[u] ? tt : 0) * sp.S * (C::BM * C::BN) + r * C::BN;
-      float4 p[kMaxSplitK][NV];
+      pt_u[u] = g.part + int64_t(ok[u] ? tt : 0) * sp.S * (C::BM * C::BN) + r * C::BN;
+      cols_u[u][0] = cols[0];
+      cols_u[u][NV - 1] = cols[NV - 1];
+    }
+    // partials in segment order, kFixupChunk segments of every item loaded before they are added
+    for (int s0 = 0; s0 < sp.S; s0 += kFixupChunk) {
+      float4 p[kFixupU][kFixupChunk][NV];
 #pragma unroll
-      for (int s2 = 0; s2 < kMaxSplitK; ++s2)
+      for (int u = 0; u < kFixupU; ++u)
 #pragma unroll
-        for (int e = 0; e < NV; ++e)
-          if (ok[u] && s2 < sp.S)
-            p[s2][e] = *reinterpret_cast<const float4*>(pt + int64_t(s2) * (C::BM * C::BN) + cols[e]);
+        for (int j = 0; j < kFixupChunk; ++j)
 #pragma unroll
-      for (int e = 0; e < NV; ++e) {
-        v[u][e] = p[0][e];
+          for (int e = 0; e < NV; ++e)
+            if (ok[u] && s0 + j < sp.S)
+              p[u][j][e] = *reinterpret_cast<const float4*>(
+                  pt_u[u] + int64_t(s0 + j) * (C::BM * C::BN) + cols_u[u][e]);
 #pragma unroll
-        for (int s2 = 1; s2 < kMaxSplitK; ++s2)
-          if (s2 < sp.S) {
-            v[u][e].x += p[s2][e].x; v[u][e].y += p[s2][e].y;
-            v[u][e].z += p[s2][e].z; v[u][e].w += p[s2][e].w;
-          }
-      }
+      for (int u = 0; u < kFixupU; ++u)
+#pragma unroll
+        for (int j = 0; j < kFixupChunk; ++j)
+#pragma unroll
+          for (int e = 0; e < NV; ++e)
+            if (s0 + j < sp.S) {
+              if (s0 + j == 0) {
+                v[u][e] = p[u][j][e];
+              } else {
+                v[u][e].x += p[u][j][e].x; v[u][e].y += p[u][j][e].y;
+                v[u][e].z += p[u][j][e].z; v[u][e].w += p[u][j][e].w;
+              }
+            }
     }
 #pragma unroll
     for (int u = 0; u < kFixupU; ++u) {
@@ -972,7 +987,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   int stage = 0;
   auto mark = [&]() -> bool {
     if (!events) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(events[stage++]), s) == hipSuccess;
+    void* e = events[stage++];  // a NULL entry skips that mark
+    return !e || hipEventRecord(static_cast<hipEvent_t>(e), s) == hipSuccess;
   };
   if (!mark()) return DCU_EHIP;
 
