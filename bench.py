@@ -108,7 +108,7 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, bench_json, steps, cmds
     def rows(d, suffix):
         return list(csv.DictReader(open(glob.glob(os.path.join(d, f"*{suffix}"))[0])))
 
-    tag = "k_gemm<2,"
+    tag = "k_gemm<2>"
     kt = [r for r in rows(ktrace_dir, "_kernel_trace.csv") if tag in r["Kernel_Name"]]
     kt.sort(key=lambda r: int(r["Start_Timestamp"]))
     timed = kt[-steps * L:]

@@ -297,6 +297,17 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT) {
 // is faster on the dense shape in isolation but exceeds the 256 registers per wave with the fused
 // epilogues and spills.)
 using CfgSmall = gemm::Cfg<128, 128, 64, 64, 2, 4>;
+// Up to 64 rows (one or a few sequences) the projections stream their weights; a 64-row tile with
+// three stages keeps twice the weight bytes in flight per CU (two K-tiles per workgroup, two
+// workgroups per CU) for the same LDS budget.
+using CfgSkinny = gemm::Cfg<64, 128, 32, 64, 3, 4>;
+constexpr int kGemmLdsChunks = CfgSmall::STAGES * CfgSmall::CHUNKS > CfgSkinny::STAGES * CfgSkinny::CHUNKS
+                                   ? CfgSmall::STAGES * CfgSmall::CHUNKS
+                                   : CfgSkinny::STAGES * CfgSkinny::CHUNKS;
+static_assert(kGemmLdsChunks * 16 <= 80 * 1024, "two workgroups per CU");
+static_assert(CfgSkinny::BM * CfgSkinny::BN <= CfgSmall::BM * CfgSmall::BN, "partial tile slots");
+// the tile shape follows the device-side row count; kernel and fixup take the same decision
+__device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
 
 template <int EPI, class C>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&acc)[C::FM][C::FN],
@@ -358,13 +369,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
 }
 
 template <int EPI, class C>
-__global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArgs g) {
-  __shared__ u32x4 b0[C::CHUNKS];
-  __shared__ u32x4 b1[C::CHUNKS];
-  __shared__ u32x4 b2[C::STAGES > 2 ? C::CHUNKS : 1];
-  __shared__ u32x4 b3[C::STAGES > 3 ? C::CHUNKS : 1];
-  const int M = g.hdr[kHdrM];
-  if (M <= 0) return;
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem) {
+  static_assert(C::THREADS == 256, "one launch shape");
+  u32x4* b0 = smem;
+  u32x4* b1 = smem + C::CHUNKS;
+  u32x4* b2 = smem + (C::STAGES > 2 ? 2 : 0) * C::CHUNKS;
+  u32x4* b3 = smem + (C::STAGES > 3 ? 3 : 0) * C::CHUNKS;
   using Rows = typename std::conditional<EPI == EPI_SWIGLU, gemm::GateUpRows<C::WN>,
                                          gemm::PlainRows>::type;
   Rows wr;
@@ -414,6 +424,17 @@ __global__ __launch_bounds__(C::THREADS, C::NW == 4 ? 2 : 1) void k_gemm(GemmArg
   }
 }
 
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
+  __shared__ u32x4 smem[kGemmLdsChunks];
+  const int M = g.hdr[kHdrM];
+  if (M <= 0) return;
+  if (use_skinny(M))
+    gemm_body<EPI, CfgSkinny>(g, M, smem);
+  else
+    gemm_body<EPI, CfgSmall>(g, M, smem);
+}
+
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
 // thread and item, kFixupU items per thread and round, with kFixupChunk partials of those items
 // loaded before any is added (memory-level parallelism). Exits at once when the GEMM did not split.
@@ -421,9 +442,7 @@ constexpr int kFixupU = 1;
 constexpr int kFixupChunk = 8;
 
 template <int EPI, class C>
-__global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
-  const int M = g.hdr[kHdrM];
-  if (M <= 0) return;
+__device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) {
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
   const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK);
@@ -528,6 +547,16 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
       }
     }
   }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
+  const int M = g.hdr[kHdrM];
+  if (M <= 0) return;
+  if (use_skinny(M))
+    fixup_body<EPI, CfgSkinny>(g, M, slots);
+  else
+    fixup_body<EPI, CfgSmall>(g, M, slots);
 }
 
 // ------------------------------------------------------------------------------ 4. attention
@@ -827,7 +856,8 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
 }
 
 // merge the S units of every split item, one wave per (item, query row), in split order; exits at
-// once when the plan split nothing
+// once when the plan split nothing. Every (max, sum) pair and partial row of the item is loaded
+// before the merge (lane s holds unit s's pair; the partial rows are read in groups of 4 units).
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH, int attn_grid) {
   const AttnPlan ap = attn_plan(g.hdr[kHdrTq] * g.H, attn_grid, g.N, g.S_max);
   if (ap.rem == 0) return;
@@ -841,19 +871,33 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH, int at
     const int b = g.tile_seq[tile];
     const int r = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile + j;
     if (r >= g.seq_off[b + 1]) continue;
-    float mx = -INFINITY;
-    for (int s2 = 0; s2 < ap.S; ++s2)
-      mx = fmaxf(mx, g.ml[((int64_t(k) * ap.S + s2) * kQTile + j) * 2]);
-    float l = 0.0f;
-    float acc0 = 0.0f, acc1 = 0.0f;
-    for (int s2 = 0; s2 < ap.S; ++s2) {
-      const int64_t slot = (int64_t(k) * ap.S + s2) * kQTile + j;
-      const float* mlp = g.ml + slot * 2;
-      const float f = __builtin_amdgcn_exp2f(mlp[0] - mx);
-      l += mlp[1] * f;
-      const float* op = g.opart + slot * DH;
-      if (lane < DH) acc0 += op[lane] * f;
-      if (lane + 64 < DH) acc1 += op[lane + 64] * f;
+    const int64_t slot0 = int64_t(k) * ap.S * kQTile + j;  // unit s of this row: slot0 + s * kQTile
+    float m_s = -INFINITY, l_s = 0.0f;
+    if (lane < ap.S) {
+      const float2 v = *reinterpret_cast<const float2*>(g.ml + (slot0 + int64_t(lane) * kQTile) * 2);
+      m_s = v.x;
+      l_s = v.y;
+    }
+    const float mx = wave_max(m_s);
+    float l = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
+    for (int s0 = 0; s0 < ap.S; s0 += 4) {
+      float o0[4], o1[4], f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s2 = s0 + u < ap.S ? s0 + u : s0;
+        const float* op = g.opart + (slot0 + int64_t(s2) * kQTile) * DH;
+        o0[u] = lane < DH ? op[lane] : 0.0f;
+        o1[u] = lane + 64 < DH ? op[lane + 64] : 0.0f;
+        f[u] = __shfl(m_s, s2, kWave);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (s0 + u >= ap.S) break;
+        const float w = __builtin_amdgcn_exp2f(f[u] - mx);
+        l += __shfl(l_s, s0 + u, kWave) * w;
+        acc0 += o0[u] * w;
+        acc1 += o1[u] * w;
+      }
     }
     const float inv = 1.0f / l;
     uint16_t* dst = g.o + int64_t(r) * g.d + h * DH;
@@ -922,20 +966,18 @@ int validate(const dcu_layer* w, int B, int N) {
 
 // The persistent projection grids always hold the resident workgroup count, so that the tail of a
 // tile walk can be split over idle slots (the split plan is a function of the device row count).
-template <class C>
 int gemm_slots() {
-  const int per_cu = C::NW == 4 ? 2 : 1;  // LDS: 64 KB (4 waves) or 128 KB (8 waves) per workgroup
-  return per_cu * kCUs;
+  return 2 * kCUs;  // two workgroups per CU (64-72 KB of LDS each)
 }
 
-template <int EPI, class C>
+template <int EPI>
 void launch_gemm(const GemmArgs& ga, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<EPI, C>), dim3(gemm_slots<C>()), dim3(C::THREADS), 0, s, ga);
+  hipLaunchKernelGGL((k_gemm<EPI>), dim3(gemm_slots()), dim3(256), 0, s, ga);
 }
 
-template <int EPI, class C>
+template <int EPI>
 void launch_fixup(const GemmArgs& ga, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_fixup<EPI, C>), dim3(2048), dim3(256), 0, s, ga, gemm_slots<C>());
+  hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, gemm_slots());
 }
 
 
@@ -1024,10 +1066,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.q = P.q;
   ga.kc = static_cast<uint16_t*>(k_cache);
   ga.vc = static_cast<uint16_t*>(v_cache);
-  launch_gemm<EPI_QKV, CfgSmall>(ga, s);
+  launch_gemm<EPI_QKV>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_QKV, CfgSmall>(ga, s);
+  launch_fixup<EPI_QKV>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1070,10 +1112,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.x = x;
   ga.a = P.a;
 
-  launch_gemm<EPI_RESID, CfgSmall>(ga, s);
+  launch_gemm<EPI_RESID>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_RESID, CfgSmall>(ga, s);
+  launch_fixup<EPI_RESID>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1102,10 +1144,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = d;
   ga.Nout = F;
   ga.h = P.h;
-  launch_gemm<EPI_SWIGLU, CfgSmall>(ga, s);
+  launch_gemm<EPI_SWIGLU>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_SWIGLU, CfgSmall>(ga, s);
+  launch_fixup<EPI_SWIGLU>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1116,10 +1158,10 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = F;
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(y_out);
-  launch_gemm<EPI_DOWN, CfgSmall>(ga, s);
+  launch_gemm<EPI_DOWN>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_DOWN, CfgSmall>(ga, s);
+  launch_fixup<EPI_DOWN>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   return DCU_OK;
