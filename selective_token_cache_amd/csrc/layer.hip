@@ -267,9 +267,19 @@ struct SplitPlan {
   int S;
 };
 
-__host__ __device__ inline SplitPlan plan_split(int T, int G, int KT) {
+__host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, bool streaming = false) {
   SplitPlan p{T, 0, 1};
   if (T <= 0) return p;
+  if (streaming) {
+    // weight streaming (few rows): the time is the weight bytes over the bandwidth once enough
+    // workgroups stream, so use the fewest segments that still keep the units within one round
+    // (every segment adds a partial tile written and read back)
+    int S = G / T;
+    S = S < kMaxSplitK ? S : kMaxSplitK;
+    while (S > 1 && KT / S < 8) --S;
+    if (S > 1) p = SplitPlan{0, T, S};
+    return p;
+  }
   if (T < G) {
     // every tile: pick S minimising rounds / S with at most 2 rounds of units
     float best = 1.0f;
@@ -300,7 +310,7 @@ using CfgSmall = gemm::Cfg<128, 128, 64, 64, 2, 4>;
 // Up to 64 rows (one or a few sequences) the projections stream their weights; a 64-row tile with
 // three stages keeps twice the weight bytes in flight per CU (two K-tiles per workgroup, two
 // workgroups per CU) for the same LDS budget.
-using CfgSkinny = gemm::Cfg<64, 128, 32, 64, 3, 4>;
+using CfgSkinny = gemm::Cfg<64, 64, 32, 32, 4, 4>;
 constexpr int kGemmLdsChunks = CfgSmall::STAGES * CfgSmall::CHUNKS > CfgSkinny::STAGES * CfgSkinny::CHUNKS
                                    ? CfgSmall::STAGES * CfgSmall::CHUNKS
                                    : CfgSkinny::STAGES * CfgSkinny::CHUNKS;
@@ -385,7 +395,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
   const int KT = g.K / C::BK;
-  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT);
+  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, std::is_same<C, CfgSkinny>::value);
   const int units = sp.full + sp.rem * sp.S;
   int lin, zero;
   for (int round = 0; gemm::next_tile(round, units, units, &lin, &zero); ++round) {
@@ -445,7 +455,7 @@ template <int EPI, class C>
 __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) {
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
-  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK);
+  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, std::is_same<C, CfgSkinny>::value);
   if (sp.rem == 0) return;
   constexpr int OUTC = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;  // output columns per tile
   constexpr int Q = C::BM * OUTC / 4;                          // float4 groups per tile
