@@ -234,11 +234,24 @@ __device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C:
   __builtin_amdgcn_s_barrier();
 }
 
-// Persistent tile walk: the round-th tile of this workgroup, remapped XCD-major.
+// Persistent tile walk: the round-th tile of this workgroup, remapped XCD-major (workgroup i runs
+// on XCD i mod 8; each XCD takes a contiguous run of tiles, so the M-tiles that share a weight tile
+// share that XCD's L2). A partial last round is spread evenly over the 8 XCDs (XCD x takes
+// rem/8 tiles, one more for x < rem mod 8) instead of filling the first XCDs and idling the rest.
 __device__ __forceinline__ bool next_tile(int round, int total, int MT, int* m_t, int* n_t) {
   const int G = gridDim.x, per_xcd = G >> 3;
-  const int tile = round * G + (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= total) return false;
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int base = round * G;
+  if (base >= total) return false;
+  const int rem = total - base;
+  int tile;
+  if (rem >= G) {
+    tile = base + x * per_xcd + j;
+  } else {
+    const int q = rem >> 3, r = rem & 7;
+    if (j >= q + (x < r ? 1 : 0)) return false;
+    tile = base + x * q + (x < r ? x : r) + j;
+  }
   *m_t = tile % MT;
   *n_t = tile / MT;
   return true;
