@@ -234,6 +234,94 @@ __device__ __forceinline__ void tile_mainloop(typename C::acc_t (&acc)[C::FM][C:
   __builtin_amdgcn_s_barrier();
 }
 
+// Two-buffer main loop with early refill. A K-tile's fragments are all read into registers right
+// after the barrier that makes the tile visible; a second barrier (after lgkmcnt(0)) then frees its
+// buffer, which is refilled at once with K-tile kt+2 while the MFMAs run. Each DMA thus has two
+// K-tiles of compute to land instead of one, with the same two buffers.
+template <class C, class WRows>
+__device__ __forceinline__ void tile_mainloop_er(typename C::acc_t (&acc)[C::FM][C::FN],
+                                                 const uint16_t* A, int M, int K, int m0, int n_t,
+                                                 const WRows& wr, u32x4* b0, u32x4* b1,
+                                                 int kt0 = 0, int kt1 = -1) {
+  static_assert(C::STAGES == 2 && C::MF == 16, "two buffers, 16x16x32 fragments");
+  static_assert(C::NQ < 64, "vmcnt range");
+  constexpr int KS = C::BK / 32;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+  const int KT = (kt1 < 0 ? K / C::BK : kt1) - kt0;
+  const uint16_t* src[C::NQ];
+#pragma unroll
+  for (int i = 0; i < C::NQ; ++i) {
+    const int q = i * C::NW + wid;
+    const int row = q * C::ROWS_PER_DMA + lane / C::RC;
+    const int pc = lane % C::RC;
+    const int c = C::RC == 8 ? (pc ^ (row & 7)) : (pc ^ ((row >> 1) & 3));
+    const uint16_t* base;
+    if (row < C::BM) {
+      int ar = m0 + row;
+      ar = ar < M ? ar : M - 1;
+      base = A + int64_t(ar) * K;
+    } else {
+      base = wr.template row<C::BN>(n_t, row - C::BM, K);
+    }
+    src[i] = base + c * 8 + kt0 * C::BK;
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = typename C::acc_t{};
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  auto issue = [&](auto sidx, int kt) {
+    constexpr int S = decltype(sidx)::value;
+    u32x4* buf = S == 0 ? b0 : b1;
+    const int kc = kt < KT ? kt : KT - 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int q = i * C::NW + wid_s;
+      dma16(static_cast<const void*>(src[i] + kc * C::BK),
+            uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(buf + q * 64))));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto iter = [&](auto sidx, int kt) {
+    constexpr int S = decltype(sidx)::value;
+    const u32x4* buf = S == 0 ? b0 : b1;
+    wait_vm_lgkm0<C::NQ>();         // K-tile kt landed (kt+1 may still be in flight)
+    __builtin_amdgcn_s_barrier();   // ... for every wave
+    asm volatile("" ::: "memory");  // the LDS reads below stay after the barrier
+    u32x4 fw[KS][C::FN], fx[KS][C::FM];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 4 + (lane >> 4);
+#pragma unroll
+      for (int f = 0; f < C::FN; ++f)
+        fw[ks][f] = buf[swz<C::RC>(C::BM + wn * C::WN + f * 16 + (lane & 15), c)];
+#pragma unroll
+      for (int f = 0; f < C::FM; ++f) fx[ks][f] = buf[swz<C::RC>(wm * C::WM + f * 16 + (lane & 15), c)];
+    }
+    wait_vm_lgkm0<C::NQ>();         // this wave's reads of the buffer are done
+    __builtin_amdgcn_s_barrier();   // ... every wave's: refill it with K-tile kt+2
+    issue(sidx, kt + 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma(fw[ks][j], fx[ks][i], acc[i][j]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  issue(I0{}, 0);
+  issue(I1{}, 1);
+  for (int kt = 0; kt < KT; kt += 2) {
+    iter(I0{}, kt);
+    if (kt + 1 < KT) iter(I1{}, kt + 1); else break;
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
 // Persistent tile walk: the round-th tile of this workgroup, remapped XCD-major (workgroup i runs
 // on XCD i mod 8; each XCD takes a contiguous run of tiles, so the M-tiles that share a weight tile
 // share that XCD's L2). A partial last round is spread evenly over the 8 XCDs (XCD x takes

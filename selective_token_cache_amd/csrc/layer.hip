@@ -267,9 +267,14 @@ struct SplitPlan {
   int S;
 };
 
-__host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, bool streaming = false) {
+enum SplitMode { kSplitTail = 0, kSplitStreaming = 1, kSplitFewTiles = 2 };
+
+__host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode = kSplitTail) {
   SplitPlan p{T, 0, 1};
   if (T <= 0) return p;
+  const bool streaming = mode == kSplitStreaming;
+  // early-refill main loop: tiles run whole unless there are fewer tiles than CUs
+  if (mode == kSplitFewTiles && 2 * T >= G) return p;
   if (streaming) {
     // weight streaming (few rows): the time is the weight bytes over the bandwidth once enough
     // workgroups stream, so use the fewest segments that still keep the units within one round
@@ -318,6 +323,19 @@ static_assert(kGemmLdsChunks * 16 <= 80 * 1024, "two workgroups per CU");
 static_assert(CfgSkinny::BM * CfgSkinny::BN <= CfgSmall::BM * CfgSmall::BN, "partial tile slots");
 // the tile shape follows the device-side row count; kernel and fixup take the same decision
 __device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
+// Main loop per projection. Gate/up (~3.4 rounds of 512 tiles at ~1.1k rows) keeps two busy
+// workgroups per CU and runs the plain loop. QKV, output and down (1-1.7 rounds) run the
+// early-refill loop, whose DMAs have two K-tiles of latency, with their tiles whole: measured at
+// batch 8, N = 1024, output 58.0 + 17.8 (split fixup) -> 60.4 + 6.8 us, down and QKV even.
+template <int EPI, class C>
+constexpr bool early_refill() {
+  return (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_DOWN) && std::is_same<C, CfgSmall>::value;
+}
+template <int EPI, class C>
+constexpr int split_mode() {
+  return std::is_same<C, CfgSkinny>::value ? kSplitStreaming
+                                           : (early_refill<EPI, C>() ? kSplitFewTiles : kSplitTail);
+}
 
 template <int EPI, class C>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&acc)[C::FM][C::FN],
@@ -395,7 +413,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
   const int KT = g.K / C::BK;
-  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, std::is_same<C, CfgSkinny>::value);
+  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, split_mode<EPI, C>());
   const int units = sp.full + sp.rem * sp.S;
   int lin, zero;
   for (int round = 0; gemm::next_tile(round, units, units, &lin, &zero); ++round) {
@@ -411,7 +429,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
     }
     const int m_t = tile % MT, n_t = tile / MT;  // consecutive tiles share the weight tile
     gemm::f32x4 acc[C::FM][C::FN];
-    gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
+    if constexpr (early_refill<EPI, C>())
+      gemm::tile_mainloop_er<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, kt0, kt1);
+    else
+      gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
     if (lin < sp.full) {
       gemm_epilogue<EPI, C>(g, acc, M, m_t * C::BM, n_t);
     } else {
@@ -455,7 +476,7 @@ template <int EPI, class C>
 __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) {
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
-  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, std::is_same<C, CfgSkinny>::value);
+  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode<EPI, C>());
   if (sp.rem == 0) return;
   constexpr int OUTC = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;  // output columns per tile
   constexpr int Q = C::BM * OUTC / 4;                          // float4 groups per tile
