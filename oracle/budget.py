@@ -5,7 +5,7 @@ B^{t,l} = (B_layer * LayerNum) * s^{t+1,l} / sum_k s^{t+1,k}: the total budget T
 split across layers in proportion to the previous step's layer means (the page's step t+1 is the
 previous step because its step index counts down).
 
-The page gives a real-valued share. Readings (listed in the design doc):
+The page gives a real-valued share. Readings:
 * integer budgets by floor plus largest remainder, ties to the lower layer, in IEEE fp64 with the
   fixed operation order below, so that sum_l b_l == T exactly;
 * with no previous step, or when every previous mean is 0, each layer gets B_layer.

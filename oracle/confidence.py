@@ -4,7 +4,7 @@ Follows "Fast-dLLM++" reading notes, Key designs / overall framework: after the 
 masked position takes the argmax of its marginal prediction and that argmax's probability as its
 confidence c_i.
 
-Readings (listed in DESIGN.md): temperature-1 softmax over the full vocabulary; no sampling noise;
+Readings: temperature-1 softmax over the full vocabulary; no sampling noise;
 the argmax is the lowest index among equal maxima; c = 1 / sum_v exp(z_v - max z) in fp64.
 """
 from __future__ import annotations

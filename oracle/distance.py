@@ -6,7 +6,7 @@ Follows "Dynamic-dLLM" reading notes, Key design 1 (DCU):
   d_i = 1 - <x_i^t, x_i^{t+1}> / (||x_i^t|| ||x_i^{t+1}||)   (the d_i^{t,l} equation);
 * layer dynamics s = (1/N) sum_i d_i over all N positions (the s^{t,l} definition).
 
-Readings where the page is silent (listed in the design doc):
+Readings where the page is silent:
 * bitwise-identical rows give exactly 0; if exactly one row has zero norm the distance is 1; two
   zero-norm rows give 0;
 * the exact value is clamped to [0, 2] and rounded once to fp32 (RNE);

@@ -9,7 +9,7 @@ Follows "Fast-dLLM++: Frechet Profile Decoding" reading notes, Key designs:
   factor rule (n+1)(1 - c_(n)) < f with f = 1 - delta), B_n = sum_{j<n} (c_(j) - c_(n)), and
   G_n = F_n + B_n whenever L_n > 0.
 
-Readings (listed in DESIGN.md): ties in c are ordered by candidate slot ascending; m = 0 commits 0;
+Readings: ties in c are ordered by candidate slot ascending; m = 0 commits 0;
 delta must be >= 0; sums are fp64 in sorted order (exact whenever every c is an fp32 value >= 2^-17
 and m <= 8192, because every term is then a multiple of 2^-40 and every partial sum is below 2^13).
 """

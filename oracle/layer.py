@@ -6,7 +6,7 @@ tokens are recomputed, all others reuse their cached values. The layer is a bidi
 projection, attention of the selected queries over every cached key/value, an output projection and
 a SwiGLU feed-forward block.
 
-The pages do not fix the layer internals. Reading used here (listed in DESIGN.md; "parity unpinned"
+The pages do not fix the layer internals. Reading used here ("parity unpinned"
 by the pages, pinned by the tests as an implementation of this reading):
 * pre-norm residual block with RMSNorm (gain vectors, eps given), no rotary embedding, no attention
   mask, softmax scale 1/sqrt(head_dim);

@@ -7,7 +7,7 @@ Follows "Dynamic-dLLM" reading notes:
   window of fixed size B_window is always recomputed (the U^{t,l} union equation), and the remaining
   budget is spent outside the window.
 
-Readings (listed in DESIGN.md):
+Readings:
 * the window holds exactly B_window positions, [p - floor(B_window/2), p - floor(B_window/2) +
   B_window - 1], clipped to [0, N) (the page's inclusive bracket [p - B/2, p + B/2] would hold
   B + 1; ``literal_window=True`` switches to that form for sensitivity checks only);

@@ -14,7 +14,7 @@ Order of operations per step (see the per-module docstrings for the passages eac
 makes the "stuck in the mud" effect of Key design 2 in the Dynamic-dLLM notes observable.
 
 The initial cache fill is one dense pass (every row selected) over each layer's cached input; the
-pages do not describe the initial fill, so this is a reading (listed in the design doc).
+pages do not describe the initial fill, so this is a reading.
 """
 from __future__ import annotations
 

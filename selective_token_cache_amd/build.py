@@ -26,7 +26,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", shutil.which("g++") or "g++")
 
-# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated (build flags)
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 are generated
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

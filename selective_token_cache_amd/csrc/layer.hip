@@ -615,8 +615,20 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
-constexpr int kKB = 64;         // keys per block
-constexpr int kAttnStages = 2;  // LDS stages of (K, V) blocks: 64 KB at head_dim 128, 2 WGs per CU
+#ifndef DCU_ATTN_KB
+#define DCU_ATTN_KB 64
+#endif
+#ifndef DCU_ATTN_STAGES
+#define DCU_ATTN_STAGES 2
+#endif
+#ifndef DCU_ATTN_WGS
+#define DCU_ATTN_WGS 2
+#endif
+constexpr int kKB = 64;                      // key-range granularity of split units
+constexpr int kAttnKB = DCU_ATTN_KB;         // keys per block (32 or 64; 64 at head_dim 32)
+constexpr int kAttnStages = DCU_ATTN_STAGES; // LDS stages of (K, V) blocks
+constexpr int kAttnWgs = DCU_ATTN_WGS;       // workgroups per CU the registers are budgeted for
+static_assert(kAttnKB == 32 || kAttnKB == 64, "key block");
 
 // Work plan of the attention grid (G persistent workgroups, two per CU) for the device-side
 // query-tile count. Items are (query tile, head) pairs. When there are fewer items than CUs
@@ -626,7 +638,7 @@ constexpr int kAttnStages = 2;  // LDS stages of (K, V) blocks: 64 KB at head_di
 // the short units and the merge cost more than the half-empty round, whose workgroups run alone
 // on their CUs.) A split unit writes its unnormalised fp32 output and (max, sum) to a unit-indexed
 // slot; k_attn_combine merges an item's S units in split order. Split units: items * S < G + items.
-constexpr int kAttnMaxUnits = 4 * 256;  // 2 * (2 workgroups per CU * 256 CUs)
+constexpr int kAttnMaxUnits = 2 * kAttnWgs * 256;  // 2 * (attention workgroups per CU * 256 CUs)
 
 struct AttnPlan {
   int full, rem, S, kps;
@@ -666,9 +678,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs g) {
+__global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
+  constexpr int KB = DH == 32 ? 64 : kAttnKB;  // keys per block
+  constexpr int kKF = KB / 16;                // 16-key fragments per block
   constexpr int CH = DH / 8;            // 16-byte chunks per head row
-  constexpr int BLK = kKB * CH;         // chunks per K (or V) block
+  constexpr int BLK = KB * CH;         // chunks per K (or V) block
   constexpr int NQ = BLK / 64 / 4;      // DMA instructions per wave per block, per operand
   constexpr int ST = kAttnStages;
   static_assert(NQ >= 1, "block size");
@@ -712,7 +726,7 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
     // whole items cover every key; split units their range
     const int kbeg = split * ap.kps;
     const int kend = w < ap.full ? g.N : min(g.N, kbeg + ap.kps);
-    const int nblk = (kend - kbeg + kKB - 1) / kKB;
+    const int nblk = (kend - kbeg + KB - 1) / KB;
     // this wave's 16 queries; lane column `col` is its query
     int qr = r0 + wid * 16 + col;
     const bool qvalid = qr < rend;
@@ -732,14 +746,14 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
     int64_t doff[NQ];
 #pragma unroll
     for (int i = 0; i < NQ; ++i) doff[i] = int64_t(kbeg + drow[i]) * g.d + dcol[i] * 8;
-    const int64_t blk_step = int64_t(kKB) * g.d;
+    const int64_t blk_step = int64_t(KB) * g.d;
 
     auto issue = [&](auto sidx, int j) {
       constexpr int S = decltype(sidx)::value;
       u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
       u32x4* vb = S == 0 ? v0 : (S == 1 ? v1 : v2);
       const int jj = j < nblk ? j : nblk - 1;
-      const bool full = kbeg + (jj + 1) * kKB <= kend;
+      const bool full = kbeg + (jj + 1) * KB <= kend;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
@@ -747,7 +761,7 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
         if (full) {
           off = head_base + doff[i] + jj * blk_step;
         } else {
-          int key = kbeg + jj * kKB + drow[i];
+          int key = kbeg + jj * KB + drow[i];
           key = key < kend ? key : kend - 1;
           off = head_base + int64_t(key) * g.d + dcol[i] * 8;
         }
@@ -763,11 +777,11 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
       constexpr int S = decltype(sidx)::value;
       const u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
       const uint16_t* vh = reinterpret_cast<const uint16_t*>(S == 0 ? v0 : (S == 1 ? v1 : v2));
-      const int kb0 = kbeg + j * kKB;
+      const int kb0 = kbeg + j * KB;
       // S^T for 64 keys x 16 queries: 4 fragments (keys 16f + 4*grp + i)
-      f32x4 s[4];
+      f32x4 s[kKF];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < kKF; ++f) {
         s[f] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int key = f * 16 + col;
 #pragma unroll
@@ -776,16 +790,16 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
       }
       // raw scores; the scale log2(e)/sqrt(dh) > 0 is applied inside exp2 (fma), and only the
       // ragged last block masks keys past the end
-      if (kb0 + kKB > kend) {
+      if (kb0 + KB > kend) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < kKF; ++f)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (kb0 + f * 16 + grp * 4 + i >= kend) s[f][i] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
+      for (int f = 0; f < kKF; ++f)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[f][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -804,9 +818,9 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
         for (int df = 0; df < DH / 16; ++df) acc_o[df] *= alpha;
       }
       float psum = 0.0f;
-      uint32_t pk[4][2];
+      uint32_t pk[kKF][2];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < kKF; ++f) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -820,7 +834,7 @@ __global__ __launch_bounds__(256, kAttnStages == 2 ? 2 : 1) void k_attn(AttnArgs
       // O^T += V^T P^T over two 32-key chunks; MFMA k index 8*grp + j maps to key
       // 32c + 4*grp + j (j < 4) and 32c + 16 + 4*grp + (j - 4) (j >= 4)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < KB / 32; ++c) {
         const u32x4 pb = u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]};
 #pragma unroll
         for (int df = 0; df < DH / 16; ++df) {
@@ -1121,8 +1135,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.d = d;
   aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;  // key ranges of >= 128 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
-  const int attn_blocks = 2 * kCUs;  // persistent; the plan depends on the device row count
-  static_assert(2 * (2 * kCUs) <= kAttnMaxUnits, "attention split slots");
+  const int attn_blocks = kAttnWgs * kCUs;  // persistent; the plan depends on the device row count
+  static_assert(2 * (kAttnWgs * kCUs) <= kAttnMaxUnits, "attention split slots");
   if (DH == 128)
     hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
   else if (DH == 64)

@@ -3,7 +3,8 @@ routines (scaled_dot_product_attention, rms_norm, silu) and closed forms.
 
 What the layer must satisfy comes from the Dynamic-dLLM notes, Key design 1 (only the selected
 tokens are recomputed, the rest reuse cached values); that a full selection reproduces the dense
-layer is the method's own consistency requirement. The layer internals are this build's reading."""
+layer is the method's own consistency requirement. The layer internals follow the reading stated in the
+oracle's layer module."""
 import math
 
 import numpy as np
