@@ -615,14 +615,17 @@ struct AttnArgs {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
+// 32-key blocks, two stages (32 KB of LDS at head_dim 128) and four workgroups per CU: measured
+// 53.9 / 108.3 us per layer at batch 8, N = 1024 / 2048, against 59.3 / 115.3 for 64-key blocks at
+// two workgroups per CU and 55.7 / 112.8 for 32-key blocks with three stages at three per CU
 #ifndef DCU_ATTN_KB
-#define DCU_ATTN_KB 64
+#define DCU_ATTN_KB 32
 #endif
 #ifndef DCU_ATTN_STAGES
 #define DCU_ATTN_STAGES 2
 #endif
 #ifndef DCU_ATTN_WGS
-#define DCU_ATTN_WGS 2
+#define DCU_ATTN_WGS 4
 #endif
 constexpr int kKB = 64;                      // key-range granularity of split units
 constexpr int kAttnKB = DCU_ATTN_KB;         // keys per block (32 or 64; 64 at head_dim 32)
