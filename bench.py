@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--workload", default="step", choices=sorted(WORKLOADS))
     ap.add_argument("--dense-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-rows", type=int, default=0,
+                    help="row bound passed to the layer calls (default: B * min(N, L * b_layer + window))")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also launch a plain 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -280,6 +282,9 @@ def main():
                                     max_rows=B * N, workspace=ws)
         torch.cuda.synchronize()
 
+    # host-side bound on the selected rows of one layer call: a sequence's budget for one layer is
+    # at most its whole step budget L * b_layer, plus the window, and never more than N
+    max_rows = args.max_rows if args.max_rows > 0 else B * min(N, L_ * B_LAYER + B_WINDOW)
     stages = list(LAYER_STAGES) if wl["layers"] else []
     n_ev_layer = 2 + len(stages) + 1 if wl["layers"] else 3
 
@@ -298,7 +303,7 @@ def main():
             if wl["layers"]:
                 le = e[2:] if e is not None and any(x is not None for x in e[2:]) else None
                 stc.dcu_selective_layer(layers[l][0], x_cur[l], sel_idx[l], sel_cnt[l], kc[l], vc[l],
-                                        y[l], max_rows=B * N, workspace=ws, events=le)
+                                        y[l], max_rows=max_rows, workspace=ws, events=le)
             else:
                 rec(e, 2)
         if not wl["end"]:
@@ -536,7 +541,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl["desc"], "batch": B, "seq_len": N, "layers": L_, "d": D, "heads": H,
                    "head_dim": DH, "ffn": F, "vocab": V if wl["end"] else None, "b_layer": B_LAYER,
-                   "b_window": B_WINDOW, "keys_per_seq": N_KEYS, "drift_rows": 0.3,
+                   "b_window": B_WINDOW, "max_rows": max_rows if wl["layers"] else None,
+                   "keys_per_seq": N_KEYS, "drift_rows": 0.3,
                    "parallelism": "single GPU"},
         "recomputed_tokens_per_s": round(rows_step / (ms_step * 1e-3), 1),
         "rows_per_step": rows_step,

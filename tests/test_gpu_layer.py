@@ -112,6 +112,25 @@ def test_selective_layer_small_shapes(shape, B, N, counts):
     _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
 
 
+@pytest.mark.parametrize("shape,B,N,counts,max_rows", [
+    # ragged weight tiles (QKV 960, FFN 448, output 320 rows), no split
+    (synth.LayerShape(d=320, n_heads=5, head_dim=64, ffn=448), 2, 100, [30, 23], 60),
+    # split K on every projection, one row
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 1, 256, [1], 1),
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 3, 90, [17, 40, 7], 64),
+])
+def test_selective_layer_at_most_64_rows(shape, B, N, counts, max_rows):
+    """A tight caller bound max_rows <= 64: workspace and launch grids sized for at most 64 rows,
+    every projection in one 64-row tile, split along K where the weight tiles are few."""
+    _log(f"layer <=64 rows d={shape.d} F={shape.ffn} B={B} N={N} max_rows={max_rows}")
+    case = Case(shape, B, N, seed=shape.d + N + 1)
+    sel, cnt = _random_selection(case.g, B, N, counts)
+    (got, got2) = case.run_gpu(sel, cnt, max_rows=max_rows, reps=2)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
+
+
 def test_dense_mode_small():
     shape = synth.LayerShape(d=256, n_heads=2, head_dim=128, ffn=320)
     case = Case(shape, 2, 150, seed=7)
@@ -149,7 +168,11 @@ def test_full_size_single_sequence_64_rows():
     (got, got2) = case.run_gpu(sel, cnt, reps=2)
     for a, b in zip(got, got2):
         assert np.array_equal(a, b)
-    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, 1, 1024))
+    ref = case.run_oracle(sel, cnt)
+    _compare(case, got, ref, _rows(sel, cnt, 1, 1024))
+    # the same call with the caller's tight bound max_rows = 64 (workspace and grids sized for it)
+    (got64,) = case.run_gpu(sel, cnt, max_rows=64)
+    _compare(case, got64, ref, _rows(sel, cnt, 1, 1024))
 
 
 def test_full_size_batched_sampled():
