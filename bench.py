@@ -251,8 +251,11 @@ def main():
     for l in range(L_):
         if wl["layers"]:
             w = wd.layer_weights(D, F, 0.02, CFG, l, device=dev)
+            # the layer keeps its own blocked copy; row-major weights stay only for layer 0
+            # (the PyTorch dense reference)
             layers.append((stc.Layer(D, H, DH, F, 1e-5, w["w_qkv"], w["w_o"], w["w_gate"], w["w_up"],
-                                     w["w_down"], w["g_attn"], w["g_ffn"]), w))
+                                     w["w_down"], w["g_attn"], w["g_ffn"]), w if l == 0 else None))
+            del w
             kc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
             vc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
             y.append(torch.empty((B, N, D), dtype=torch.bfloat16, device=dev))

@@ -111,7 +111,26 @@ int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t lay
                int32_t* sel_idx, int32_t* sel_count, void* stream);
 
 /*
- * One pre-norm transformer layer (bf16 weights, [out, in] row-major):
+ * dcu_pack_weights -- write one projection matrix in the blocked layout the layer reads.
+ * (A data layout of this library, not an operation of the method: the projections of a layer are
+ * the matrices of the pre-norm transformer layer below.)
+ * w      [rows, cols] bf16 row-major: an [out, in] projection matrix. Not modified.
+ * out    rows * cols bf16, caller-owned, must not overlap w. Block (g, t) holds rows
+ *        16g .. 16g+15 and columns 64t .. 64t+63 at element offset (g * (cols/64) + t) * 1024;
+ *        inside a block, columns 64t+8c .. 64t+8c+7 of row 16g+r sit at element offset
+ *        (16c + r) * 8. A pure permutation (no arithmetic); the device buffers must stay valid
+ *        until the work on `stream` completes.
+ * Errors: EINVAL on NULL pointers or rows, cols <= 0; EUNSUPPORTED if rows % 16 != 0,
+ *         cols % 64 != 0, rows * cols >= 2^40, or a pointer not 16-byte aligned.
+ */
+int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void* out, void* stream);
+
+/* dcu_layer.weight_layout: the only layout the layer accepts (matrices from dcu_pack_weights) */
+#define DCU_WEIGHTS_BLOCKED 1
+
+/*
+ * One pre-norm transformer layer (bf16 weights; W[out, in] below means the [out, in] matrix
+ * written in the blocked layout of dcu_pack_weights):
  *   xn = RMSNorm(x; g_attn), [q|k|v] = xn W_qkv^T, o = softmax(q K^T / sqrt(head_dim)) V per head
  *   over all N cached rows (no mask), a = x + o W_o^T, an = RMSNorm(a; g_ffn),
  *   y = a + (silu(an W_gate^T) * (an W_up^T)) W_down^T.
@@ -122,13 +141,14 @@ typedef struct {
   int32_t head_dim;   /* 32, 64 or 128                                */
   int32_t ffn;        /* FFN width F                                  */
   float rms_eps;
-  const void* w_qkv;  /* bf16 [3d, d]: rows Wq | Wk | Wv              */
-  const void* w_o;    /* bf16 [d, d]                                  */
-  const void* w_gate; /* bf16 [F, d]                                  */
-  const void* w_up;   /* bf16 [F, d]                                  */
-  const void* w_down; /* bf16 [d, F]                                  */
+  const void* w_qkv;  /* bf16 [3d, d] blocked: rows Wq | Wk | Wv      */
+  const void* w_o;    /* bf16 [d, d] blocked                          */
+  const void* w_gate; /* bf16 [F, d] blocked                          */
+  const void* w_up;   /* bf16 [F, d] blocked                          */
+  const void* w_down; /* bf16 [d, F] blocked                          */
   const void* g_attn; /* bf16 [d] RMSNorm gain before attention       */
   const void* g_ffn;  /* bf16 [d] RMSNorm gain before the FFN         */
+  int32_t weight_layout; /* must be DCU_WEIGHTS_BLOCKED                */
 } dcu_layer;
 
 /* Workspace bytes dcu_selective_layer needs for these shapes (max_rows <= 0 means B*N). */
@@ -154,8 +174,8 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  *           split-K partial tiles of one call.
  * Results are bitwise reproducible for a given device: every reduction runs in a fixed order.
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
- *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if head_dim not in {32, 64, 128}, d
- *         or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte
+ *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if weight_layout is not
+ *         DCU_WEIGHTS_BLOCKED, head_dim not in {32, 64, 128}, d or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte
  *         aligned;
  *         EWORKSPACE if the workspace is too small or not 256-byte aligned.
  */

@@ -33,7 +33,11 @@ class LayerDesc(ctypes.Structure):
     """Mirror of dcu_layer in include/dcu.h."""
     _fields_ = [("d", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn", _i32),
                 ("rms_eps", ctypes.c_float), ("w_qkv", _vp), ("w_o", _vp), ("w_gate", _vp),
-                ("w_up", _vp), ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp)]
+                ("w_up", _vp), ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp),
+                ("weight_layout", _i32)]
+
+
+WEIGHTS_BLOCKED = 1  # DCU_WEIGHTS_BLOCKED
 
 
 _lib = None
@@ -45,6 +49,7 @@ EXPORTS = {
     "dcu_distance": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "dcu_select": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp]),
+    "dcu_pack_weights": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "dcu_selective_layer_workspace": (ctypes.c_size_t,
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
@@ -171,8 +176,24 @@ def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: t
     return sel_idx, sel_count
 
 
+def dcu_pack_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The blocked layout of a row-major [rows, cols] bf16 projection matrix (a new tensor of the
+    same shape unless `out` is given), written by the library's permutation kernel."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be a 2-D [rows, cols] matrix")
+    if out is None:
+        out = torch.empty_like(w)
+    _need(out, "out", torch.bfloat16, tuple(w.shape))
+    _check("dcu_pack_weights",
+           load().dcu_pack_weights(_p(w), w.shape[0], w.shape[1], _p(out), _stream(stream)))
+    return out
+
+
 class Layer:
-    """Holds the device weights of one layer and the matching dcu_layer descriptor."""
+    """Holds the device weights of one layer and the matching dcu_layer descriptor. The five
+    projection matrices are given row-major ([out, in]) and copied once into the library's blocked
+    layout (dcu_pack_weights, on the current stream); the caller's tensors are not kept."""
 
     def __init__(self, d, n_heads, head_dim, ffn, eps, w_qkv, w_o, w_gate, w_up, w_down, g_attn,
                  g_ffn):
@@ -181,9 +202,11 @@ class Layer:
                                ("w_down", w_down, (d, ffn)), ("g_attn", g_attn, (d,)),
                                ("g_ffn", g_ffn, (d,))]:
             _need(t, name, torch.bfloat16, shape)
-        self.tensors = (w_qkv, w_o, w_gate, w_up, w_down, g_attn, g_ffn)
+        packed = [dcu_pack_weights(t) for t in (w_qkv, w_o, w_gate, w_up, w_down)]
+        self.tensors = (*packed, g_attn, g_ffn)
         self.d, self.n_heads, self.head_dim, self.ffn, self.eps = d, n_heads, head_dim, ffn, eps
-        self.desc = LayerDesc(d, n_heads, head_dim, ffn, float(eps), *[_p(t) for t in self.tensors])
+        self.desc = LayerDesc(d, n_heads, head_dim, ffn, float(eps), *[_p(t) for t in self.tensors],
+                              WEIGHTS_BLOCKED)
 
     def workspace_bytes(self, B: int, N: int, max_rows: int = 0) -> int:
         return int(load().dcu_selective_layer_workspace(ctypes.byref(self.desc), B, N, max_rows))

@@ -238,8 +238,8 @@ enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3 };
 
 struct GemmArgs {
   const uint16_t* A;    // [M, K] compacted rows (workspace)
-  const uint16_t* W;    // [Nout, K]
-  const uint16_t* W2;   // SwiGLU: up weights [Nout, K]; W holds the gate weights
+  const uint16_t* W;    // [Nout, K] blocked (see gemm.h)
+  const uint16_t* W2;   // SwiGLU: up weights [Nout, K] blocked; W holds the gate weights
   int K, Nout;          // Nout: W rows (SwiGLU: F)
   const int* hdr;
   const int* rowmap;
@@ -403,13 +403,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   u32x4* b1 = smem + C::CHUNKS;
   u32x4* b2 = smem + (C::STAGES > 2 ? 2 : 0) * C::CHUNKS;
   u32x4* b3 = smem + (C::STAGES > 3 ? 3 : 0) * C::CHUNKS;
-  using Rows = typename std::conditional<EPI == EPI_SWIGLU, gemm::GateUpRows<C::WN>,
-                                         gemm::PlainRows>::type;
-  Rows wr;
+  using Blocks = typename std::conditional<EPI == EPI_SWIGLU, gemm::GateUpBlocks<C::WN>,
+                                           gemm::PlainBlocks>::type;
+  Blocks wr;
   if constexpr (EPI == EPI_SWIGLU)
-    wr = Rows{g.W, g.W2, g.Nout};
+    wr = Blocks{g.W, g.W2, g.Nout, g.K / C::BK};
   else
-    wr = Rows{g.W, g.Nout};
+    wr = Blocks{g.W, g.Nout, g.K / C::BK};
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
   const int KT = g.K / C::BK;
@@ -1000,6 +1000,7 @@ int validate(const dcu_layer* w, int B, int N) {
   if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
     return DCU_EINVAL;
   if (w->d <= 0 || w->n_heads <= 0 || w->head_dim <= 0 || w->ffn <= 0) return DCU_EINVAL;
+  if (w->weight_layout != DCU_WEIGHTS_BLOCKED) return DCU_EUNSUPPORTED;
   if (int64_t(w->n_heads) * w->head_dim != w->d) return DCU_EINVAL;
   if (!(w->rms_eps >= 0.0f)) return DCU_EINVAL;
   if (w->head_dim != 32 && w->head_dim != 64 && w->head_dim != 128) return DCU_EUNSUPPORTED;
@@ -1028,10 +1029,42 @@ void launch_fixup(const GemmArgs& ga, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, gemm_slots());
 }
 
+// Row-major [rows, cols] -> blocked layout (gemm.h): one 16-byte chunk per thread, reads coalesced
+// along the rows; a block's 128 chunks are written by the 8 rows x 16 chunk columns that own them.
+__global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ w, int64_t rows,
+                                                      int64_t cols, u32x4* __restrict__ out) {
+  const int64_t cpr = cols / 8;  // chunks per row
+  const int64_t n = rows * cpr;
+  const int64_t kt_n = cols / 64;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = i / cpr, ch = i - r * cpr;
+    const int64_t g = r >> 4, kt = ch >> 3;
+    const int rr = int(r & 15), c = int(ch & 7);
+    out[(g * kt_n + kt) * 128 + c * 16 + rr] = w[i];
+  }
+}
+
 
 
 }  // namespace
 }  // namespace dcu
+
+extern "C" int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void* out,
+                                void* stream) {
+  if (!w || !out || rows <= 0 || cols <= 0) return DCU_EINVAL;
+  if (rows % 16 != 0 || cols % 64 != 0) return DCU_EUNSUPPORTED;
+  if (int64_t(rows) * cols >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
+  if (!dcu_aligned16(w) || !dcu_aligned16(out)) return DCU_EUNSUPPORTED;
+  const int64_t chunks = int64_t(rows) * cols / 8;
+  const int64_t want = (chunks + 255) / 256;
+  const unsigned grid = unsigned(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(dcu::k_pack_weights, dim3(grid), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const dcu::u32x4*>(w),
+                     int64_t(rows), int64_t(cols), static_cast<dcu::u32x4*>(out));
+  DCU_LAUNCH_CHECK();
+  return DCU_OK;
+}
 
 extern "C" size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N,
                                                 int32_t max_rows) {

@@ -94,3 +94,44 @@ def test_confidence_and_commit_validation():
     assert L.frechet_commit(FAKE, None, 2, 16, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 0, 16, 0.1, FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 2, 8193, 0.1, FAKE, FAKE, None) == _lib.EUNSUPPORTED
+
+
+def test_pack_weights_validation():
+    L = stc.load()
+    assert L.dcu_pack_weights(None, 16, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_weights(FAKE, 16, 64, None, None) == _lib.EINVAL
+    assert L.dcu_pack_weights(FAKE, 0, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_weights(FAKE, 24, 64, FAKE, None) == _lib.EUNSUPPORTED   # rows % 16
+    assert L.dcu_pack_weights(FAKE, 16, 96, FAKE, None) == _lib.EUNSUPPORTED   # cols % 64
+    odd = ctypes.c_void_p(256 + 8)
+    assert L.dcu_pack_weights(odd, 16, 64, FAKE, None) == _lib.EUNSUPPORTED
+
+
+def _desc(**kw):
+    a = dict(d=256, n_heads=4, head_dim=64, ffn=512, eps=1e-5, layout=_lib.WEIGHTS_BLOCKED)
+    a.update(kw)
+    return _lib.LayerDesc(a["d"], a["n_heads"], a["head_dim"], a["ffn"], a["eps"],
+                          *([FAKE] * 7), a["layout"])
+
+
+def test_layer_validation():
+    L = stc.load()
+    ws = L.dcu_selective_layer_workspace
+
+    def call(desc, B=2, N=64, sel=None, cnt=None):
+        return L.dcu_selective_layer(ctypes.byref(desc), FAKE, sel, cnt, B, N, 0, FAKE, FAKE, FAKE,
+                                     FAKE, 1 << 40, None)
+
+    assert ws(ctypes.byref(_desc()), 2, 64, 0) > 0
+    assert ws(ctypes.byref(_desc(layout=0)), 2, 64, 0) == 0
+    assert call(_desc(layout=0)) == _lib.EUNSUPPORTED              # row-major weights claimed
+    assert call(_desc(d=250)) == _lib.EINVAL                       # d != n_heads * head_dim
+    assert call(_desc(d=192, n_heads=2, head_dim=96)) == _lib.EUNSUPPORTED   # head_dim 96
+    assert call(_desc(ffn=500)) == _lib.EUNSUPPORTED              # ffn % 64
+    assert call(_desc(eps=-1.0)) == _lib.EINVAL
+    assert call(_desc(), B=0) == _lib.EINVAL
+    assert call(_desc(), N=70000) == _lib.EUNSUPPORTED
+    assert call(_desc(), sel=FAKE) == _lib.EINVAL                  # only one of sel_idx / sel_count
+    # workspace smaller than the query says
+    assert L.dcu_selective_layer(ctypes.byref(_desc()), FAKE, None, None, 2, 64, 0, FAKE, FAKE, FAKE,
+                                 FAKE, 16, None) == _lib.EWORKSPACE

@@ -58,6 +58,19 @@ class Case:
                                       self.kc, self.vc, self.y)
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 64), (48, 192), (3 * 4096, 4096)])
+def test_pack_weights_layout(rows, cols):
+    """dcu_pack_weights against the layout its header states, bit for bit: block (g, t) of rows
+    16g.. and columns 64t.. at (g * cols/64 + t) * 1024, columns 64t+8c..+7 of row 16g+r at
+    (16c + r) * 8 inside it."""
+    _log(f"pack {rows} x {cols}")
+    g = np.random.default_rng(rows + cols)
+    w = g.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16)
+    got = host_bf16(stc.dcu_pack_weights(dev_bf16(w)))
+    want = w.reshape(rows // 16, 16, cols // 64, 8, 8).transpose(0, 2, 3, 1, 4).reshape(rows, cols)
+    assert np.array_equal(got.reshape(rows, cols), want)
+
+
 def _rows(sel, cnt, B, N):
     if sel is None:
         return [np.arange(N) for _ in range(B)]
