@@ -265,16 +265,30 @@ struct SplitPlan {
   int full;  // tiles computed whole (ids 0 .. full-1)
   int rem;   // tail tiles (ids full .. full+rem-1), each in S segments
   int S;
+  // CU-paired placement (one round): workgroups i and i + G/2 share a CU (the dispatcher fills
+  // every CU once before it places a second workgroup: workgroup j of an XCD shares its CU with
+  // j + G/16); the first G/2 workgroups take the full = G/2 whole tiles, one per CU, and the second
+  // G/2 the rem * S <= G/2 segments of the other tiles, so every CU gets the same work
+  bool paired;
 };
 
 enum SplitMode { kSplitTail = 0, kSplitStreaming = 1, kSplitFewTiles = 2 };
 
 __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode = kSplitTail) {
-  SplitPlan p{T, 0, 1};
+  SplitPlan p{T, 0, 1, false};
   if (T <= 0) return p;
   const bool streaming = mode == kSplitStreaming;
-  // early-refill main loop: tiles run whole unless there are fewer tiles than CUs
-  if (mode == kSplitFewTiles && 2 * T >= G) return p;
+  // early-refill main loop: tiles run whole unless there are fewer tiles than CUs; between one and
+  // two tiles per CU, one whole tile per CU and the rest cut in segments for the CUs' second slots
+  if (mode == kSplitFewTiles && 2 * T >= G) {
+    const int C = G / 2, rem = T - C;
+    if (rem <= 0 || rem >= C || (G & 15) != 0) return p;
+    int S = C / rem;
+    S = S < kMaxSplitK ? S : kMaxSplitK;
+    while (S > 1 && KT / S < 8) --S;
+    if (S > 1) p = SplitPlan{C, rem, S, true};
+    return p;
+  }
   if (streaming) {
     // weight streaming (few rows): the time is the weight bytes over the bandwidth once enough
     // workgroups stream, so use the fewest segments that still keep the units within one round
@@ -282,7 +296,7 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode =
     int S = G / T;
     S = S < kMaxSplitK ? S : kMaxSplitK;
     while (S > 1 && KT / S < 8) --S;
-    if (S > 1) p = SplitPlan{0, T, S};
+    if (S > 1) p = SplitPlan{0, T, S, false};
     return p;
   }
   if (T < G) {
@@ -296,7 +310,7 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode =
         p.S = S;
       }
     }
-    if (p.S > 1) p = SplitPlan{0, T, p.S};
+    if (p.S > 1) p = SplitPlan{0, T, p.S, false};
     return p;
   }
   const int rem = T % G;
@@ -304,7 +318,7 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode =
   int S = G / rem;
   S = S < kMaxSplitK ? S : kMaxSplitK;
   while (S > 1 && KT / S < 8) --S;
-  if (S > 1) p = SplitPlan{T - rem, rem, S};
+  if (S > 1) p = SplitPlan{T - rem, rem, S, false};
   return p;
 }
 
@@ -416,7 +430,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, split_mode<EPI, C>());
   const int units = sp.full + sp.rem * sp.S;
   int lin, zero;
-  for (int round = 0; gemm::next_tile(round, units, units, &lin, &zero); ++round) {
+  for (int round = 0;; ++round) {
+    if (sp.paired) {
+      if (round > 0) break;
+      const int per = gridDim.x >> 4, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+      if (j < per) {
+        lin = x * per + j;  // whole tile
+      } else {
+        const int v = x * per + (j - per);
+        if (v >= sp.rem * sp.S) break;
+        lin = sp.full + v;  // segment v % S of tail tile v / S
+      }
+    } else if (!gemm::next_tile(round, units, units, &lin, &zero)) {
+      break;
+    }
     int tile, s = 0, kt0 = 0, kt1 = KT;
     if (lin < sp.full) {
       tile = lin;

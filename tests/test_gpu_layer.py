@@ -188,16 +188,22 @@ def test_full_size_single_sequence_64_rows():
     _compare(case, got64, ref, _rows(sel, cnt, 1, 1024))
 
 
-def test_full_size_batched_sampled():
-    """Batch 8, N=1024, LLaDA-8B shapes, ~150 rows per sequence; the oracle recomputes one
+@pytest.mark.parametrize("counts,b", [
+    # 1041 rows: 9 row tiles, the output and down projections (288 tiles) run one whole tile per CU
+    # plus 32 tiles in 8 K-segments
+    ([150, 90, 200, 64, 128, 170, 99, 140], 2),
+    # 1250 rows (320 tiles: 64 tiles in 4 segments) and 1400 rows (352 tiles: 96 in 2)
+    ([160, 170, 150, 180, 155, 140, 165, 130], 5),
+    ([180, 175, 170, 185, 176, 168, 172, 174], 7),
+])
+def test_full_size_batched_sampled(counts, b):
+    """Batch 8, N=1024, LLaDA-8B shapes, ~130-200 rows per sequence; the oracle recomputes one
     sequence completely (its rows depend only on that sequence's cache)."""
-    _log("layer full size batch 8")
+    _log(f"layer full size batch 8, {sum(counts)} rows")
     shape = synth.LLADA8B
-    case = Case(shape, 8, 1024, seed=4)
-    counts = [150, 90, 200, 64, 128, 170, 99, 140]
+    case = Case(shape, 8, 1024, seed=4 + b)
     sel, cnt = _random_selection(case.g, 8, 1024, counts)
     (got,) = case.run_gpu(sel, cnt)
-    b = 2
     ref = olayer.selective_layer(case.w, shape.n_heads, shape.head_dim, shape.eps,
                                  case.x[b:b + 1], sel[b:b + 1], cnt[b:b + 1], case.kc[b:b + 1],
                                  case.vc[b:b + 1], case.y[b:b + 1])
