@@ -109,6 +109,7 @@ def _random_selection(g, B, N, counts):
 
 @pytest.mark.parametrize("shape,B,N,counts", [
     (synth.TINY, 1, 64, [20]),                                                   # tiny fp32 config shapes
+    (synth.TINY, 2, 64, [20, 41]),                                               # one K-tile, 2 sequences
     (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 3, 200, [130, 1, 0]),
     (synth.LayerShape(d=512, n_heads=4, head_dim=128, ffn=768), 2, 300, [64, 257]),
     (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 4, 77, [77, 5, 33, 64]),
