@@ -265,10 +265,10 @@ struct SplitPlan {
   int full;  // tiles computed whole (ids 0 .. full-1)
   int rem;   // tail tiles (ids full .. full+rem-1), each in S segments
   int S;
-  // CU-paired placement (one round): workgroups i and i + G/2 share a CU (the dispatcher fills
-  // every CU once before it places a second workgroup: workgroup j of an XCD shares its CU with
-  // j + G/16); the first G/2 workgroups take the full = G/2 whole tiles, one per CU, and the second
-  // G/2 the rem * S <= G/2 segments of the other tiles, so every CU gets the same work
+  // CU-paired last round: workgroup j of an XCD shares its CU with workgroup j + G/16 (the
+  // dispatcher fills every CU once before it places a second workgroup). After (full - G/2) / G
+  // rounds of whole tiles, the first G/2 workgroups take the last G/2 whole tiles, one per CU, and
+  // the second G/2 the rem * S <= G/2 segments of the other tiles, so every CU gets the same work
   bool paired;
 };
 
@@ -281,12 +281,14 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode =
   // early-refill main loop: tiles run whole unless there are fewer tiles than CUs; between one and
   // two tiles per CU, one whole tile per CU and the rest cut in segments for the CUs' second slots
   if (mode == kSplitFewTiles && 2 * T >= G) {
-    const int C = G / 2, rem = T - C;
+    // the last round (T mod G tiles, or G when T is a multiple of G) decides: between one and two
+    // tiles per CU, the CU-paired placement; otherwise whole tiles
+    const int C = G / 2, last = T % G == 0 ? G : T % G, rem = last - C;
     if (rem <= 0 || rem >= C || (G & 15) != 0) return p;
     int S = C / rem;
     S = S < kMaxSplitK ? S : kMaxSplitK;
     while (S > 1 && KT / S < 8) --S;
-    if (S > 1) p = SplitPlan{C, rem, S, true};
+    if (S > 1) p = SplitPlan{T - rem, rem, S, true};
     return p;
   }
   if (streaming) {
@@ -432,14 +434,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   int lin, zero;
   for (int round = 0;; ++round) {
     if (sp.paired) {
-      if (round > 0) break;
-      const int per = gridDim.x >> 4, x = blockIdx.x & 7, j = blockIdx.x >> 3;
-      if (j < per) {
-        lin = x * per + j;  // whole tile
+      const int f0 = sp.full - (gridDim.x >> 1);  // tiles of the full rounds
+      if (round * int(gridDim.x) < f0) {
+        gemm::next_tile(round, f0, f0, &lin, &zero);
       } else {
-        const int v = x * per + (j - per);
-        if (v >= sp.rem * sp.S) break;
-        lin = sp.full + v;  // segment v % S of tail tile v / S
+        if (round * int(gridDim.x) > f0) break;
+        const int per = gridDim.x >> 4, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        if (j < per) {
+          lin = f0 + x * per + j;  // whole tile
+        } else {
+          const int v = x * per + (j - per);
+          if (v >= sp.rem * sp.S) break;
+          lin = sp.full + v;  // segment v % S of tail tile v / S
+        }
       }
     } else if (!gemm::next_tile(round, units, units, &lin, &zero)) {
       break;
