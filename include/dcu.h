@@ -125,7 +125,23 @@ int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t lay
  */
 int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void* out, void* stream);
 
-/* dcu_layer.weight_layout: the only layout the layer accepts (matrices from dcu_pack_weights) */
+/*
+ * dcu_pack_gate_up -- the gate and up matrices of the SwiGLU FFN as one blocked matrix.
+ * (A data layout of this library, as dcu_pack_weights.)
+ * w_gate, w_up  [F, d] bf16 row-major each. Not modified.
+ * out    2 * F * d bf16, caller-owned, overlapping neither input: the [2F, d] matrix whose 16-row
+ *        groups alternate gate group g, up group g (rows 32g .. 32g+15 = gate rows 16g .. 16g+15,
+ *        rows 32g+16 .. 32g+31 = up rows 16g .. 16g+15), written in the blocked layout of
+ *        dcu_pack_weights. (The gate and up rows of the same outputs sit next to each other, so the
+ *        FFN's weight stream is one contiguous range per tile.)
+ * Errors: EINVAL on NULL pointers or F, d <= 0; EUNSUPPORTED if F % 16 != 0, d % 64 != 0,
+ *         2 * F * d >= 2^40, or a pointer not 16-byte aligned.
+ */
+int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d, void* out,
+                     void* stream);
+
+/* dcu_layer.weight_layout: the only layout the layer accepts (matrices from dcu_pack_weights and
+ * dcu_pack_gate_up) */
 #define DCU_WEIGHTS_BLOCKED 1
 
 /*
@@ -143,8 +159,7 @@ typedef struct {
   float rms_eps;
   const void* w_qkv;  /* bf16 [3d, d] blocked: rows Wq | Wk | Wv      */
   const void* w_o;    /* bf16 [d, d] blocked                          */
-  const void* w_gate; /* bf16 [F, d] blocked                          */
-  const void* w_up;   /* bf16 [F, d] blocked                          */
+  const void* w_gate_up; /* bf16 [2F, d]: gate and up, dcu_pack_gate_up */
   const void* w_down; /* bf16 [d, F] blocked                          */
   const void* g_attn; /* bf16 [d] RMSNorm gain before attention       */
   const void* g_ffn;  /* bf16 [d] RMSNorm gain before the FFN         */

@@ -32,9 +32,8 @@ class DcuError(RuntimeError):
 class LayerDesc(ctypes.Structure):
     """Mirror of dcu_layer in include/dcu.h."""
     _fields_ = [("d", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn", _i32),
-                ("rms_eps", ctypes.c_float), ("w_qkv", _vp), ("w_o", _vp), ("w_gate", _vp),
-                ("w_up", _vp), ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp),
-                ("weight_layout", _i32)]
+                ("rms_eps", ctypes.c_float), ("w_qkv", _vp), ("w_o", _vp), ("w_gate_up", _vp),
+                ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp), ("weight_layout", _i32)]
 
 
 WEIGHTS_BLOCKED = 1  # DCU_WEIGHTS_BLOCKED
@@ -50,6 +49,7 @@ EXPORTS = {
     "dcu_select": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp]),
     "dcu_pack_weights": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
+    "dcu_pack_gate_up": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "dcu_selective_layer_workspace": (ctypes.c_size_t,
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
@@ -190,10 +190,27 @@ def dcu_pack_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=No
     return out
 
 
+def dcu_pack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """The fused blocked gate/up matrix [2F, d] of two row-major [F, d] bf16 matrices."""
+    _need(w_gate, "w_gate", torch.bfloat16)
+    if w_gate.dim() != 2:
+        raise ValueError("w_gate must be a 2-D [F, d] matrix")
+    _need(w_up, "w_up", torch.bfloat16, tuple(w_gate.shape))
+    F, d = w_gate.shape
+    if out is None:
+        out = torch.empty((2 * F, d), dtype=torch.bfloat16, device=w_gate.device)
+    _need(out, "out", torch.bfloat16, (2 * F, d))
+    _check("dcu_pack_gate_up", load().dcu_pack_gate_up(_p(w_gate), _p(w_up), F, d, _p(out),
+                                                       _stream(stream)))
+    return out
+
+
 class Layer:
     """Holds the device weights of one layer and the matching dcu_layer descriptor. The five
     projection matrices are given row-major ([out, in]) and copied once into the library's blocked
-    layout (dcu_pack_weights, on the current stream); the caller's tensors are not kept."""
+    layout (dcu_pack_weights; gate and up fused by dcu_pack_gate_up; on the current stream); the
+    caller's tensors are not kept."""
 
     def __init__(self, d, n_heads, head_dim, ffn, eps, w_qkv, w_o, w_gate, w_up, w_down, g_attn,
                  g_ffn):
@@ -202,7 +219,8 @@ class Layer:
                                ("w_down", w_down, (d, ffn)), ("g_attn", g_attn, (d,)),
                                ("g_ffn", g_ffn, (d,))]:
             _need(t, name, torch.bfloat16, shape)
-        packed = [dcu_pack_weights(t) for t in (w_qkv, w_o, w_gate, w_up, w_down)]
+        packed = [dcu_pack_weights(w_qkv), dcu_pack_weights(w_o), dcu_pack_gate_up(w_gate, w_up),
+                  dcu_pack_weights(w_down)]
         self.tensors = (*packed, g_attn, g_ffn)
         self.d, self.n_heads, self.head_dim, self.ffn, self.eps = d, n_heads, head_dim, ffn, eps
         self.desc = LayerDesc(d, n_heads, head_dim, ffn, float(eps), *[_p(t) for t in self.tensors],

@@ -106,19 +106,20 @@ struct PlainBlocks {
 };
 
 // Gate/up interleave: each wave's WN tile rows are WN/2 gate rows followed by the WN/2 up rows of
-// the same output columns, so matching gate and up accumulators land in the same lane.
+// the same output columns, so matching gate and up accumulators land in the same lane. W is the
+// fused gate/up matrix: its 16-row groups alternate gate group g (group 2g) and up group g (2g+1).
 template <int WN>
 struct GateUpBlocks {
   static_assert((WN / 2) % 16 == 0, "gate and up halves of whole blocks");
-  const uint16_t* Wg;
-  const uint16_t* Wu;
+  const uint16_t* W;
   int F;
   int KT;
   template <int BN>
   __device__ __forceinline__ const uint16_t* block(int n_t, int jb) const {
     const int tr = jb * 16, wn = tr / WN, within = tr % WN;
     const int j = n_t * (BN / 2) + wn * (WN / 2) + (within % (WN / 2));
-    return (within < WN / 2 ? Wg : Wu) + int64_t(j / 16) * KT * kBlockElems;
+    const int grp = 2 * (j / 16) + (within < WN / 2 ? 0 : 1);
+    return W + int64_t(grp) * KT * kBlockElems;
   }
   template <int BN>
   __device__ __forceinline__ int tiles() const { return F / (BN / 2); }

@@ -238,8 +238,7 @@ enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3 };
 
 struct GemmArgs {
   const uint16_t* A;    // [M, K] compacted rows (workspace)
-  const uint16_t* W;    // [Nout, K] blocked (see gemm.h)
-  const uint16_t* W2;   // SwiGLU: up weights [Nout, K] blocked; W holds the gate weights
+  const uint16_t* W;    // [Nout, K] blocked (see gemm.h); SwiGLU: the fused gate/up [2 Nout, K]
   int K, Nout;          // Nout: W rows (SwiGLU: F)
   const int* hdr;
   const int* rowmap;
@@ -423,7 +422,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
                                            gemm::PlainBlocks>::type;
   Blocks wr;
   if constexpr (EPI == EPI_SWIGLU)
-    wr = Blocks{g.W, g.W2, g.Nout, g.K / C::BK};
+    wr = Blocks{g.W, g.Nout, g.K / C::BK};
   else
     wr = Blocks{g.W, g.Nout, g.K / C::BK};
   const int MT = (M + C::BM - 1) / C::BM;
@@ -1031,7 +1030,7 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
 
 int validate(const dcu_layer* w, int B, int N) {
   if (!w || B <= 0 || N <= 0) return DCU_EINVAL;
-  if (!w->w_qkv || !w->w_o || !w->w_gate || !w->w_up || !w->w_down || !w->g_attn || !w->g_ffn)
+  if (!w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->g_attn || !w->g_ffn)
     return DCU_EINVAL;
   if (w->d <= 0 || w->n_heads <= 0 || w->head_dim <= 0 || w->ffn <= 0) return DCU_EINVAL;
   if (w->weight_layout != DCU_WEIGHTS_BLOCKED) return DCU_EUNSUPPORTED;
@@ -1040,7 +1039,7 @@ int validate(const dcu_layer* w, int B, int N) {
   if (w->head_dim != 32 && w->head_dim != 64 && w->head_dim != 128) return DCU_EUNSUPPORTED;
   if (w->d % 64 != 0 || w->ffn % 64 != 0) return DCU_EUNSUPPORTED;
   if (N > 65536 || int64_t(B) * N > (int64_t(1) << 28) || B > kMaxSeqs) return DCU_EUNSUPPORTED;
-  const void* ps[] = {w->w_qkv, w->w_o, w->w_gate, w->w_up, w->w_down, w->g_attn, w->g_ffn};
+  const void* ps[] = {w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->g_attn, w->g_ffn};
   for (const void* p : ps)
     if (!dcu_aligned16(p)) return DCU_EUNSUPPORTED;
   return DCU_OK;
@@ -1064,22 +1063,37 @@ void launch_fixup(const GemmArgs& ga, hipStream_t s) {
 }
 
 // Row-major [rows, cols] -> blocked layout (gemm.h): one 16-byte chunk per thread, reads coalesced
-// along the rows; a block's 128 chunks are written by the 8 rows x 16 chunk columns that own them.
-__global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ w, int64_t rows,
+// along the rows. With a second source b (the up matrix), the 16-row groups of a and b alternate
+// in the output (a's group g -> group 2g, b's group g -> group 2g + 1).
+__global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ a,
+                                                      const u32x4* __restrict__ b, int64_t rows,
                                                       int64_t cols, u32x4* __restrict__ out) {
   const int64_t cpr = cols / 8;  // chunks per row
-  const int64_t n = rows * cpr;
+  const int64_t n = rows * cpr;  // chunks per source
   const int64_t kt_n = cols / 64;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+  const int nsrc = b ? 2 : 1;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n * nsrc;
        i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t r = i / cpr, ch = i - r * cpr;
-    const int64_t g = r >> 4, kt = ch >> 3;
+    const int m = i < n ? 0 : 1;
+    const int64_t k = i - m * n;
+    const int64_t r = k / cpr, ch = k - r * cpr;
+    const int64_t g = (r >> 4) * nsrc + m, kt = ch >> 3;
     const int rr = int(r & 15), c = int(ch & 7);
-    out[(g * kt_n + kt) * 128 + c * 16 + rr] = w[i];
+    out[(g * kt_n + kt) * 128 + c * 16 + rr] = (m ? b : a)[k];
   }
 }
 
-
+int launch_pack(const void* a, const void* b, int64_t rows, int64_t cols, void* out,
+                void* stream) {
+  const int64_t chunks = rows * cols / 8 * (b ? 2 : 1);
+  const int64_t want = (chunks + 255) / 256;
+  const unsigned grid = unsigned(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(k_pack_weights, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), rows, cols,
+                     static_cast<u32x4*>(out));
+  DCU_LAUNCH_CHECK();
+  return DCU_OK;
+}
 
 }  // namespace
 }  // namespace dcu
@@ -1090,14 +1104,17 @@ extern "C" int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void*
   if (rows % 16 != 0 || cols % 64 != 0) return DCU_EUNSUPPORTED;
   if (int64_t(rows) * cols >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
   if (!dcu_aligned16(w) || !dcu_aligned16(out)) return DCU_EUNSUPPORTED;
-  const int64_t chunks = int64_t(rows) * cols / 8;
-  const int64_t want = (chunks + 255) / 256;
-  const unsigned grid = unsigned(want < 8192 ? want : 8192);
-  hipLaunchKernelGGL(dcu::k_pack_weights, dim3(grid), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const dcu::u32x4*>(w),
-                     int64_t(rows), int64_t(cols), static_cast<dcu::u32x4*>(out));
-  DCU_LAUNCH_CHECK();
-  return DCU_OK;
+  return dcu::launch_pack(w, nullptr, rows, cols, out, stream);
+}
+
+extern "C" int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d,
+                                void* out, void* stream) {
+  if (!w_gate || !w_up || !out || F <= 0 || d <= 0) return DCU_EINVAL;
+  if (F % 16 != 0 || d % 64 != 0) return DCU_EUNSUPPORTED;
+  if (2 * int64_t(F) * d >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
+  if (!dcu_aligned16(w_gate) || !dcu_aligned16(w_up) || !dcu_aligned16(out))
+    return DCU_EUNSUPPORTED;
+  return dcu::launch_pack(w_gate, w_up, F, d, out, stream);
 }
 
 extern "C" size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N,
@@ -1254,8 +1271,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
 
   // gate and up together, SwiGLU epilogue -> h
   ga.A = P.xn;
-  ga.W = static_cast<const uint16_t*>(w->w_gate);
-  ga.W2 = static_cast<const uint16_t*>(w->w_up);
+  ga.W = static_cast<const uint16_t*>(w->w_gate_up);
   ga.K = d;
   ga.Nout = F;
   ga.h = P.h;
@@ -1269,7 +1285,6 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   // down projection + residual, scattered back into y_out
   ga.A = P.h;
   ga.W = static_cast<const uint16_t*>(w->w_down);
-  ga.W2 = nullptr;
   ga.K = F;
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(y_out);

@@ -107,11 +107,19 @@ def test_pack_weights_validation():
     assert L.dcu_pack_weights(odd, 16, 64, FAKE, None) == _lib.EUNSUPPORTED
 
 
+def test_pack_gate_up_validation():
+    L = stc.load()
+    assert L.dcu_pack_gate_up(FAKE, None, 16, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_gate_up(FAKE, FAKE, 0, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_gate_up(FAKE, FAKE, 8, 64, FAKE, None) == _lib.EUNSUPPORTED    # F % 16
+    assert L.dcu_pack_gate_up(FAKE, FAKE, 16, 32, FAKE, None) == _lib.EUNSUPPORTED   # d % 64
+
+
 def _desc(**kw):
     a = dict(d=256, n_heads=4, head_dim=64, ffn=512, eps=1e-5, layout=_lib.WEIGHTS_BLOCKED)
     a.update(kw)
     return _lib.LayerDesc(a["d"], a["n_heads"], a["head_dim"], a["ffn"], a["eps"],
-                          *([FAKE] * 7), a["layout"])
+                          *([FAKE] * 6), a["layout"])
 
 
 def test_layer_validation():

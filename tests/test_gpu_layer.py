@@ -71,6 +71,20 @@ def test_pack_weights_layout(rows, cols):
     assert np.array_equal(got.reshape(rows, cols), want)
 
 
+@pytest.mark.parametrize("F,d", [(16, 64), (48, 128), (12288, 4096)])
+def test_pack_gate_up_layout(F, d):
+    """dcu_pack_gate_up against its header: the [2F, d] matrix with alternating 16-row groups of
+    gate and up, in the blocked layout (checked through the same block formula as above)."""
+    _log(f"pack gate/up {F} x {d}")
+    g = np.random.default_rng(F + d)
+    wg = g.integers(0, 1 << 16, size=(F, d), dtype=np.uint16)
+    wu = g.integers(0, 1 << 16, size=(F, d), dtype=np.uint16)
+    got = host_bf16(stc.dcu_pack_gate_up(dev_bf16(wg), dev_bf16(wu)))
+    inter = np.stack([wg.reshape(F // 16, 16, d), wu.reshape(F // 16, 16, d)], axis=1).reshape(2 * F, d)
+    want = inter.reshape(2 * F // 16, 16, d // 64, 8, 8).transpose(0, 2, 3, 1, 4).reshape(2 * F, d)
+    assert np.array_equal(got.reshape(2 * F, d), want)
+
+
 def _rows(sel, cnt, B, N):
     if sel is None:
         return [np.arange(N) for _ in range(B)]
