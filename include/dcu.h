@@ -103,12 +103,16 @@ int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype, int64_t G
  *           candidates C = {i not in W : dist_i > 0} ranked by (dist desc, position asc).
  *           Entries past sel_count[b] are set to -1.
  * sel_count [B] int32 out.
+ * mean      [B] fp32 out, or NULL: the layer dynamics s of each sequence (Key design 1), bit for
+ *           bit what dcu_distance writes to its `mean` for the same dist (same fp64 sums, same
+ *           order), so a step can take s here and call dcu_distance with mean = NULL (one launch
+ *           fewer per layer).
  * Errors: EINVAL on NULL pointers, B, N, L <= 0, P < 0, b_window < 0, layer outside [0, L);
  *         EUNSUPPORTED if N > 8192.
  */
 int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t layer,
                const int32_t* key_pos, int32_t P, int32_t B, int32_t N, int32_t b_window,
-               int32_t* sel_idx, int32_t* sel_count, void* stream);
+               int32_t* sel_idx, int32_t* sel_count, float* mean, void* stream);
 
 /*
  * dcu_pack_weights -- write one projection matrix in the blocked layout the layer reads.

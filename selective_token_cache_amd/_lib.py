@@ -47,7 +47,7 @@ EXPORTS = {
     "dcu_budget": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "dcu_distance": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "dcu_select": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
-                                  _vp]),
+                                  _vp, _vp]),
     "dcu_pack_weights": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "dcu_pack_gate_up": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "dcu_selective_layer_workspace": (ctypes.c_size_t,
@@ -152,8 +152,9 @@ def dcu_distance(x_cur: torch.Tensor, x_prev: torch.Tensor, dist=None, mean=None
 
 
 def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: torch.Tensor | None,
-               b_window: int, sel_idx=None, sel_count=None, stream=None):
-    """dist [B, N] fp32, budgets [B, L] int32, key_pos [B, P] int32 -> (sel_idx [B, N], sel_count [B])."""
+               b_window: int, sel_idx=None, sel_count=None, mean=None, stream=None):
+    """dist [B, N] fp32, budgets [B, L] int32, key_pos [B, P] int32 -> (sel_idx [B, N], sel_count [B]).
+    mean: optional [B] fp32 out, the layer mean of dist per sequence (as dcu_distance's)."""
     _need(dist, "dist", torch.float32)
     B, N = dist.shape
     _need(budgets, "budgets", torch.int32)
@@ -170,8 +171,10 @@ def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: t
     sel_count = torch.empty((B,), dtype=torch.int32, device=dist.device) if sel_count is None else sel_count
     _need(sel_idx, "sel_idx", torch.int32, (B, N))
     _need(sel_count, "sel_count", torch.int32, (B,))
+    if mean is not None:
+        _need(mean, "mean", torch.float32, (B,))
     st = load().dcu_select(_p(dist), _p(budgets), L, layer, _p(key_pos) if P else None, P, B, N,
-                           b_window, _p(sel_idx), _p(sel_count), _stream(stream))
+                           b_window, _p(sel_idx), _p(sel_count), _p(mean), _stream(stream))
     _check("dcu_select", st)
     return sel_idx, sel_count
 

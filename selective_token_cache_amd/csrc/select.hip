@@ -27,7 +27,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
                                                      int layer, const int32_t* __restrict__ key_pos,
                                                      int P, int N, int b_window,
                                                      int32_t* __restrict__ sel_idx,
-                                                     int32_t* __restrict__ sel_count) {
+                                                     int32_t* __restrict__ sel_count,
+                                                     float* __restrict__ mean) {
   __shared__ int hist[256];
   __shared__ int scan_lds[17];
   __shared__ uint32_t s_prefix;
@@ -67,7 +68,20 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
       }
     }
   }
+  // optional layer mean, formed exactly as dcu_distance forms it (256 threads with fixed strides,
+  // fp64, wave sums, then (w0 + w1) + (w2 + w3)); its loads overlap the ones above, and the barrier
+  // of the block sum below publishes the wave partials
+  __shared__ double mpart[4];
+  if (mean) {
+    double acc = 0.0;
+    if (t < 256)
+      for (int i = t; i < N; i += 256) acc += double(d[i]);
+    acc = wave_sum(acc);
+    if (t < 256 && (t & (kWave - 1)) == 0) mpart[t / kWave] = acc;
+  }
   const int nC = block_sum_int(ncand, scan_lds);
+  if (mean && t == 0)
+    mean[b] = float(((mpart[0] + mpart[1]) + (mpart[2] + mpart[3])) / double(N));
   int budget = budgets[int64_t(b) * L + layer];
   budget = budget < 0 ? 0 : budget;
   const int k = budget < nC ? budget : nC;
@@ -161,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
 
 extern "C" int dcu_select(const float* dist, const int32_t* budgets, int32_t L, int32_t layer,
                           const int32_t* key_pos, int32_t P, int32_t B, int32_t N,
-                          int32_t b_window, int32_t* sel_idx, int32_t* sel_count, void* stream) {
+                          int32_t b_window, int32_t* sel_idx, int32_t* sel_count, float* mean,
+                          void* stream) {
   if (!dist || !budgets || !sel_idx || !sel_count) return DCU_EINVAL;
   if (B <= 0 || N <= 0 || L <= 0 || P < 0 || b_window < 0) return DCU_EINVAL;
   if (layer < 0 || layer >= L) return DCU_EINVAL;
@@ -169,7 +184,7 @@ extern "C" int dcu_select(const float* dist, const int32_t* budgets, int32_t L, 
   if (N > dcu::kThreads * dcu::kMaxE) return DCU_EUNSUPPORTED;
   hipLaunchKernelGGL(dcu::k_select, dim3(unsigned(B)), dim3(dcu::kThreads), 0,
                      static_cast<hipStream_t>(stream), dist, budgets, int(L), int(layer), key_pos,
-                     int(P), int(N), int(b_window), sel_idx, sel_count);
+                     int(P), int(N), int(b_window), sel_idx, sel_count, mean);
   DCU_LAUNCH_CHECK();
   return DCU_OK;
 }

@@ -72,7 +72,7 @@ def test_select_validation():
     def call(**kw):
         a = dict(args, **kw)
         return L.dcu_select(a["dist"], a["budgets"], a["L"], a["layer"], a["key_pos"], a["P"],
-                            a["B"], a["N"], a["bw"], a["sel"], a["cnt"], None)
+                            a["B"], a["N"], a["bw"], a["sel"], a["cnt"], None, None)
 
     assert call(layer=4) == _lib.EINVAL
     assert call(layer=-1) == _lib.EINVAL

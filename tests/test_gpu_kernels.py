@@ -127,7 +127,12 @@ def test_budget_bit_exact():
 # ----------------------------------------------------------------------------- select
 def _check_select(d, budgets, layer, keys, bw):
     sel, cnt = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw)
-    sel2, cnt2 = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw)
+    mean = torch.empty((d.shape[0],), dtype=torch.float32, device="cuda")
+    sel2, cnt2 = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw,
+                                mean=mean)
+    # the optional layer mean: the fp64 sum of the fp32 distances over N
+    ref_mean = d.astype(np.float64).mean(axis=1)
+    assert np.allclose(mean.cpu().numpy(), ref_mean, rtol=1e-6, atol=0)
     B, N = d.shape
     kp = keys if keys is not None else np.zeros((B, 0), np.int32)
     rs, rc = osel.select(d, budgets, layer, kp, bw)
@@ -181,9 +186,12 @@ def test_select_on_drift_distances():
     bud_h = budgets.cpu().numpy()
     assert np.array_equal(bud_h, obud.layer_budget(mean.cpu().numpy().reshape(1, L), 1, L, 32))
     for l in range(L):
-        sel, cnt = stc.dcu_select(dist[l:l + 1].contiguous(), budgets, l, dk, 32)
+        m = torch.empty((1,), dtype=torch.float32, device="cuda")
+        sel, cnt = stc.dcu_select(dist[l:l + 1].contiguous(), budgets, l, dk, 32, mean=m)
         rs, rc = osel.select(dist_h[l:l + 1], bud_h, l, keys, 32)
         assert np.array_equal(sel.cpu().numpy(), rs) and np.array_equal(cnt.cpu().numpy(), rc)
+        # the select kernel's layer mean is dcu_distance's, bit for bit
+        assert m.cpu().numpy().view(np.uint32)[0] == mean.cpu().numpy()[l:l + 1].view(np.uint32)[0]
 
 
 # ----------------------------------------------------------------------------- confidence
