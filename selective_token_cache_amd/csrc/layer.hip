@@ -1057,8 +1057,18 @@ void launch_gemm(const GemmArgs& ga, hipStream_t s) {
   hipLaunchKernelGGL((k_gemm<EPI>), dim3(gemm_slots()), dim3(256), 0, s, ga);
 }
 
+// The fixup is launched unless the host can tell that the projection will not split: with a row
+// capacity of at most 64, every device row count takes the 64 x 64 tiles with one row tile, so the
+// split plan is the same for all of them.
 template <int EPI>
-void launch_fixup(const GemmArgs& ga, hipStream_t s) {
+void launch_fixup(const GemmArgs& ga, hipStream_t s, int M_cap) {
+  if (M_cap <= CfgSkinny::BM) {
+    const int NT = EPI == EPI_SWIGLU ? ga.Nout / (CfgSkinny::BN / 2)
+                                     : (ga.Nout + CfgSkinny::BN - 1) / CfgSkinny::BN;
+    const SplitPlan sp = plan_split(NT, gemm_slots(), ga.K / CfgSkinny::BK,
+                                    split_mode<EPI, CfgSkinny>());
+    if (sp.rem == 0) return;
+  }
   hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, gemm_slots());
 }
 
@@ -1201,7 +1211,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   launch_gemm<EPI_QKV>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_QKV>(ga, s);
+  launch_fixup<EPI_QKV>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1247,7 +1257,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   launch_gemm<EPI_RESID>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_RESID>(ga, s);
+  launch_fixup<EPI_RESID>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1278,7 +1288,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   launch_gemm<EPI_SWIGLU>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_SWIGLU>(ga, s);
+  launch_fixup<EPI_SWIGLU>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
@@ -1291,7 +1301,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   launch_gemm<EPI_DOWN>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_DOWN>(ga, s);
+  launch_fixup<EPI_DOWN>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   return DCU_OK;
