@@ -530,7 +530,15 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
-        cpu = cpu_baseline(wl, layers, x_cur, x_prev, kc, vc, y, s_buf[cur ^ 1], keys, logits, torch)
+
+        def weights_of(l):
+            # row-major weights of layer l: kept for layer 0, regenerated (same seeds) otherwise
+            if layers[l][1] is not None:
+                return layers[l][1]
+            return wd.layer_weights(D, F, 0.02, CFG, l, device=dev)
+
+        cpu = cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_buf[cur ^ 1], keys, logits,
+                           torch)
 
     out = {
         "metric": METRIC,
@@ -564,7 +572,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, layers, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, torch):
+def cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, torch):
     """The numpy oracle, untuned, on a bounded sample of the same workload: a subset of the layers
     for the whole batch (distance, select, and the selective layer when the workload has one) plus
     the end of step on 1/8 of the candidate rows; scaled to layer-steps/s of the whole step."""
@@ -589,7 +597,7 @@ def cpu_baseline(wl, layers, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits,
         sample_layers = list(range(L_))
     host = []
     for l in sample_layers:
-        w = {k: h16(v) for k, v in layers[l][1].items()} if wl["layers"] else None
+        w = {k: h16(v) for k, v in weights_of(l).items()} if wl["layers"] else None
         lay = (h16(kc[l]), h16(vc[l]), h16(y[l])) if wl["layers"] else None
         host.append((w, h16(x_cur[l]), h16(x_prev[l]), lay))
     s_prev = s_prev_dev.cpu().numpy().T.copy()     # [B, L]
