@@ -9,6 +9,13 @@ Follows "Fast-dLLM++: Frechet Profile Decoding" reading notes, Key designs:
   factor rule (n+1)(1 - c_(n)) < f with f = 1 - delta), B_n = sum_{j<n} (c_(j) - c_(n)), and
   G_n = F_n + B_n whenever L_n > 0.
 
+The two rules the page compares against (its motivation section, Fast-dLLM's confidence-aware
+parallel decoding): the threshold rule commits every candidate with c_i >= tau independently, and
+the factor rule accepts the top n candidates when (n+1)(1 - c_(n)) < f. Readings: both commit at
+least one candidate when there is one (the progress guarantee the page states for n*), the factor
+rule takes the largest such n (its left side never decreases with n, so that is the accepted
+prefix), and c_i >= tau is inclusive.
+
 Readings: ties in c are ordered by candidate slot ascending; m = 0 commits 0;
 delta must be >= 0; sums are fp64 in sorted order (exact whenever every c is an fp32 value >= 2^-17
 and m <= 8192, because every term is then a multiple of 2^-40 and every partial sum is below 2^13).
@@ -81,11 +88,52 @@ def heterogeneity_bonus(c_sorted: np.ndarray) -> np.ndarray:
     return out
 
 
-def factor_count(c: np.ndarray, delta: float) -> int:
-    """Matched factor rule: largest n with (n+1)(1 - c_(n)) < 1 - delta, else 1 (0 if m = 0)."""
+def factor_commit_count(c: np.ndarray, f: float) -> int:
+    """Factor rule: largest n with (n+1)(1 - c_(n)) < f (fp64), else 1 (0 if m = 0)."""
     _, cs = sort_profile(c)
     if len(cs) == 0:
         return 0
-    n = np.arange(1, len(cs) + 1, dtype=np.float64)
-    ok = np.nonzero((n + 1) * (1.0 - cs) < 1.0 - delta)[0]
-    return int(ok[-1]) + 1 if ok.size else 1
+    n_star = 1
+    for i in range(len(cs)):
+        n = i + 1
+        if (n + 1.0) * (1.0 - float(cs[i])) < f:
+            n_star = n
+    return n_star
+
+
+def factor_count(c: np.ndarray, delta: float) -> int:
+    """Matched factor rule of Corollary 4.4: the factor rule with f = 1 - delta."""
+    return factor_commit_count(c, 1.0 - delta)
+
+
+def threshold_commit_count(c: np.ndarray, tau: float) -> int:
+    """Threshold rule: the number of candidates with c_i >= tau (fp64 compare), at least 1
+    (0 if m = 0). They are the first entries of the (c desc, slot asc) order."""
+    c = np.asarray(c, np.float32)
+    if c.shape[0] == 0:
+        return 0
+    k = sum(1 for v in c if float(v) >= tau)
+    return max(k, 1)
+
+
+RULES = ("frechet", "factor", "threshold")
+
+
+def commit(conf: np.ndarray, m_valid: np.ndarray | None, rule: str, param: float):
+    """Batched commit under one rule: conf [B, m] -> (n_commit [B], order [B, m]); param is delta
+    (frechet), f (factor) or tau (threshold). The order is the same for every rule."""
+    if rule not in RULES:
+        raise ValueError(rule)
+    if rule == "frechet":
+        return frechet_commit(conf, m_valid, param)
+    conf = np.asarray(conf, np.float32)
+    B, m = conf.shape
+    n = np.zeros(B, np.int32)
+    order = np.full((B, m), -1, np.int32)
+    for b in range(B):
+        mv = m if m_valid is None else int(m_valid[b])
+        ob, _ = sort_profile(conf[b, :mv])
+        order[b, :mv] = ob
+        n[b] = (factor_commit_count(conf[b, :mv], param) if rule == "factor"
+                else threshold_commit_count(conf[b, :mv], param))
+    return n, order

@@ -172,3 +172,56 @@ def test_theorem_4_1_brute_force_on_tiny_joint_distributions():
                         assert PS[t] < best
                 assert best >= L - 1e-12
     assert certified > 500
+
+
+# --- the comparison rules (Fast-dLLM threshold and factor rules; the page's motivation section) ----
+def test_threshold_and_factor_rules_on_the_page_profile():
+    c = np.array([0.99, 0.95, 0.82, 0.78, 0.74], np.float32)
+    # threshold: every candidate with c >= tau (inclusive), at least one
+    assert of.threshold_commit_count(c, 0.9) == 2
+    assert of.threshold_commit_count(c, float(np.float32(0.82))) == 3
+    assert of.threshold_commit_count(c, 0.999) == 1
+    assert of.threshold_commit_count(c, 0.0) == 5
+    # factor f = 0.75 (the matched factor of delta = 0.25): 2*0.01, 3*0.05, 4*0.18 < 0.75 <= 5*0.22,
+    # the three candidates the page says the factor rule flattens to c_(3)
+    assert of.factor_commit_count(c, 0.75) == 3
+    assert of.factor_commit_count(c, 0.0) == 1
+    assert of.factor_commit_count(np.zeros(0, np.float32), 0.75) == 0
+    assert of.threshold_commit_count(np.zeros(0, np.float32), 0.9) == 0
+
+
+def test_factor_and_threshold_rules_exact_on_random_profiles():
+    g = np.random.default_rng(11)
+    for trial in range(200):
+        m = int(g.integers(1, 40))
+        c = g.uniform(0, 1, m).astype(np.float32)
+        if trial % 3 == 0:
+            c[g.integers(0, m, m // 2)] = c[0]            # ties
+        f = float(Fraction(int(g.integers(0, 2 ** 20)), 2 ** 19))   # dyadic: exact in fp64
+        tau = float(np.float32(g.uniform(0, 1)))
+        cs = sorted((Fraction(float(v)) for v in c), reverse=True)
+        want_f = max([n for n in range(1, m + 1) if (n + 1) * (1 - cs[n - 1]) < Fraction(f)],
+                     default=1)
+        assert of.factor_commit_count(c, f) == want_f
+        k = sum(1 for v in cs if v >= Fraction(tau))
+        assert of.threshold_commit_count(c, tau) == max(k, 1)
+        # the threshold set is a prefix of the sorted order
+        order, srt = of.sort_profile(c)
+        assert all(srt[:k] >= tau) and all(srt[k:] < tau)
+
+
+def test_batched_commit_rules():
+    g = np.random.default_rng(5)
+    conf = g.uniform(0.3, 1.0, (4, 16)).astype(np.float32)
+    mv = np.array([16, 3, 0, 9], np.int32)
+    for rule, p in [("frechet", 0.1), ("factor", 0.9), ("threshold", 0.8)]:
+        n, order = of.commit(conf, mv, rule, p)
+        assert n[2] == 0 and np.all(order[2] == -1)
+        assert np.all(order[1, 3:] == -1) and sorted(order[1, :3].tolist()) == [0, 1, 2]
+        for b in (0, 1, 3):
+            ref = {"frechet": lambda c: of.commit_count(c, p)[0],
+                   "factor": lambda c: of.factor_commit_count(c, p),
+                   "threshold": lambda c: of.threshold_commit_count(c, p)}[rule](conf[b, :mv[b]])
+            assert n[b] == ref
+    with pytest.raises(ValueError):
+        of.commit(conf, mv, "greedy", 0.1)
