@@ -425,6 +425,33 @@ def main():
         kernels["confidence"]["GBps"] = round(conf_bytes / (end_ms["confidence"] / KI * 1e-3) / 1e9, 1)
         kernels["confidence"]["hbm_frac"] = round(kernels["confidence"]["GBps"] / HBM_PEAK_GBS, 3)
 
+    # the commit rules compared on the same confidences (the last step's): tokens committed per
+    # sequence and device time per call, Frechet at the step's delta and the page's default, the
+    # matched factor rule f = 1 - delta, and the threshold rule tau = 0.9
+    commit_rules = None
+    if wl["end"]:
+        c2 = conf.view(B, M_CAND)
+        commit_rules = {}
+        for name, rule, param in [("frechet_delta_0.1", "frechet", DELTA),
+                                  ("factor_f_0.9", "factor", 1.0 - DELTA),
+                                  ("frechet_delta_0.25", "frechet", 0.25),
+                                  ("factor_f_0.75", "factor", 0.75),
+                                  ("threshold_tau_0.9", "threshold", 0.9)]:
+            nc = torch.empty((B,), dtype=torch.int32, device=dev)
+            oc = torch.empty((B, M_CAND), dtype=torch.int32, device=dev)
+            stc.dllm_commit(c2, rule, param, n_commit=nc, order=oc)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                stc.dllm_commit(c2, rule, param, n_commit=nc, order=oc)
+            e1.record()
+            torch.cuda.synchronize()
+            commit_rules[name] = {"tokens_per_seq": round(float(nc.float().mean()), 2),
+                                  "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
+
     # roofline of the dominant kernel, timed with HIP events on the library's stream
     if wl["layers"]:
         gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l in range(L_)) * K
@@ -562,6 +589,7 @@ def main():
         "rows_per_step": rows_step,
         "rows_per_layer_min_max": [int(M_l.min()), int(M_l.max())],
         "kernels": kernels,
+        "commit_rules": commit_rules,
         "roofline": roofline,
         "dense": dense,
         "cpu_baseline": cpu,

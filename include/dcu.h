@@ -12,6 +12,8 @@
  *                        with K/V and output rows scattered back into caller-owned caches
  *   dllm_confidence      per-position softmax confidence and argmax over the vocabulary
  *   frechet_commit       sort, prefix sum and the Frechet margin rule -> how many positions commit
+ *   dllm_commit          the same with the factor or threshold rule instead (rule comparison)
+ *   dcu_pack_weights, dcu_pack_gate_up   the projections' blocked weight layout (set-up, not a step)
  *
  * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
  * Acceleration of Diffusion LLM" (reading notes), Key designs 1-2; "Fast-dLLM++: Frechet Profile
@@ -257,6 +259,25 @@ int dllm_confidence(const void* logits, int32_t dtype, int64_t R, int64_t V, int
  */
 int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m, double delta,
                    int32_t* n_commit, int32_t* order, void* stream);
+
+/*
+ * dllm_commit -- frechet_commit under a choice of rule, for comparing the rules on the same step.
+ * Fast-dLLM++ notes, motivation (the two rules of Fast-dLLM's confidence-aware parallel decoding,
+ * which the Frechet rule generalises) and Key designs 1-2:
+ *   DCU_COMMIT_FRECHET    param = delta >= 0: exactly frechet_commit;
+ *   DCU_COMMIT_FACTOR     param = f: n* = max{n : (n+1)(1 - c_(n)) < f} (fp64), else 1;
+ *   DCU_COMMIT_THRESHOLD  param = tau: every candidate with c_i >= tau (fp64), at least 1; these
+ *                         are the first n* entries of `order`.
+ * Arguments, outputs (order is the same for every rule; n_commit is 0 for a row without
+ * candidates) and limits as frechet_commit.
+ * Errors: EINVAL on NULL conf/n_commit/order, B <= 0, m <= 0, an unknown rule, a NaN or infinite
+ *         param, or delta < 0; EUNSUPPORTED if m > 8192.
+ */
+#define DCU_COMMIT_FRECHET 0
+#define DCU_COMMIT_FACTOR 1
+#define DCU_COMMIT_THRESHOLD 2
+int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m, int32_t rule,
+                double param, int32_t* n_commit, int32_t* order, void* stream);
 
 #ifdef __cplusplus
 }

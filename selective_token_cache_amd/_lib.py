@@ -60,6 +60,7 @@ EXPORTS = {
                                     ctypes.POINTER(_vp), _i32]),
     "dllm_confidence": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
+    "dllm_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
 }
 
 
@@ -312,4 +313,27 @@ def frechet_commit(conf: torch.Tensor, delta: float, m_valid: torch.Tensor | Non
     st = load().frechet_commit(_p(conf), _p(m_valid), B, m, float(delta), _p(n_commit), _p(order),
                                _stream(stream))
     _check("frechet_commit", st)
+    return n_commit, order
+
+
+COMMIT_RULES = {"frechet": 0, "factor": 1, "threshold": 2}  # DCU_COMMIT_*
+
+
+def dllm_commit(conf: torch.Tensor, rule: str, param: float, m_valid: torch.Tensor | None = None,
+                n_commit=None, order=None, stream=None):
+    """conf [B, m] fp32 -> n_commit [B] int32, order [B, m] int32 under rule 'frechet' (param =
+    delta), 'factor' (param = f) or 'threshold' (param = tau)."""
+    if rule not in COMMIT_RULES:
+        raise ValueError(f"rule must be one of {sorted(COMMIT_RULES)}")
+    _need(conf, "conf", torch.float32)
+    B, m = conf.shape
+    if m_valid is not None:
+        _need(m_valid, "m_valid", torch.int32, (B,))
+    n_commit = torch.empty((B,), dtype=torch.int32, device=conf.device) if n_commit is None else n_commit
+    order = torch.empty((B, m), dtype=torch.int32, device=conf.device) if order is None else order
+    _need(n_commit, "n_commit", torch.int32, (B,))
+    _need(order, "order", torch.int32, (B, m))
+    st = load().dllm_commit(_p(conf), _p(m_valid), B, m, COMMIT_RULES[rule], float(param),
+                            _p(n_commit), _p(order), _stream(stream))
+    _check("dllm_commit", st)
     return n_commit, order

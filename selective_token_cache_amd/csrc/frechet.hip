@@ -11,6 +11,9 @@
 //     sum is below 2^13, so the sums are exact in any order and a parallel block scan equals the
 //     sequential sum bit for bit. Otherwise one thread takes the sequential sum in sorted order;
 //  3. each n evaluates G_n > delta; n* is the block-wide maximum such n (no monotonicity assumed).
+// The same kernel applies the two rules that page compares against (its motivation section): the
+// factor rule, n* = max{n : (n+1)(1 - c_(n)) < f}, and the threshold rule, every candidate with
+// c_i >= tau (a prefix of the sorted order); both in fp64, both commit at least one candidate.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -40,8 +43,10 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v) {
 
 __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ conf,
                                                       const int32_t* __restrict__ m_valid, int m,
-                                                      double delta, int32_t* __restrict__ n_commit,
+                                                      int rule, double param,
+                                                      int32_t* __restrict__ n_commit,
                                                       int32_t* __restrict__ order) {
+  const double delta = param;
   extern __shared__ uint64_t keys[];  // P2 entries
   __shared__ double wsum[kThreads / kWave];
   __shared__ int s_flag[17];
@@ -100,7 +105,17 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
     return double(__uint_as_float(u));
   };
   int best = 0;
-  if (nbad == 0) {
+  if (rule != DCU_COMMIT_FRECHET) {
+    // per-candidate tests, no sums: (n+1)(1 - c_(n)) < f, or c_(n) >= tau
+    for (int e = 0; e < E; ++e) {
+      const int i = i0 + e;
+      if (i >= mv) break;
+      const double cn = value_at(i);
+      const bool ok = rule == DCU_COMMIT_FACTOR ? (double(i + 2) * (1.0 - cn) < param)
+                                                : (cn >= param);
+      if (ok) best = i + 1;
+    }
+  } else if (nbad == 0) {
     double loc = 0.0;
     for (int e = 0; e < E; ++e) {
       const int i = i0 + e;
@@ -147,10 +162,14 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
 }  // namespace
 }  // namespace dcu
 
-extern "C" int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m,
-                              double delta, int32_t* n_commit, int32_t* order, void* stream) {
+extern "C" int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m,
+                           int32_t rule, double param, int32_t* n_commit, int32_t* order,
+                           void* stream) {
   if (!conf || !n_commit || !order || B <= 0 || m <= 0) return DCU_EINVAL;
-  if (!(delta >= 0.0)) return DCU_EINVAL;  // also rejects NaN
+  if (rule != DCU_COMMIT_FRECHET && rule != DCU_COMMIT_FACTOR && rule != DCU_COMMIT_THRESHOLD)
+    return DCU_EINVAL;
+  if (param != param || param - param != 0.0) return DCU_EINVAL;  // NaN or infinite
+  if (rule == DCU_COMMIT_FRECHET && !(param >= 0.0)) return DCU_EINVAL;
   if (m > dcu::kMaxM) return DCU_EUNSUPPORTED;
   int P2 = 1;
   while (P2 < m) P2 <<= 1;
@@ -159,8 +178,14 @@ extern "C" int frechet_commit(const float* conf, const int32_t* m_valid, int32_t
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
     return DCU_EHIP;
   hipLaunchKernelGGL(dcu::k_frechet, dim3(unsigned(B)), dim3(dcu::kThreads), lds,
-                     static_cast<hipStream_t>(stream), conf, m_valid, int(m), delta, n_commit,
-                     order);
+                     static_cast<hipStream_t>(stream), conf, m_valid, int(m), int(rule), param,
+                     n_commit, order);
   DCU_LAUNCH_CHECK();
   return DCU_OK;
+}
+
+extern "C" int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m,
+                              double delta, int32_t* n_commit, int32_t* order, void* stream) {
+  if (!(delta >= 0.0)) return DCU_EINVAL;  // also rejects NaN
+  return dllm_commit(conf, m_valid, B, m, DCU_COMMIT_FRECHET, delta, n_commit, order, stream);
 }

@@ -94,6 +94,12 @@ def test_confidence_and_commit_validation():
     assert L.frechet_commit(FAKE, None, 2, 16, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 0, 16, 0.1, FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 2, 8193, 0.1, FAKE, FAKE, None) == _lib.EUNSUPPORTED
+    assert L.dllm_commit(FAKE, None, 2, 16, 3, 0.5, FAKE, FAKE, None) == _lib.EINVAL      # rule
+    assert L.dllm_commit(FAKE, None, 2, 16, 1, float("inf"), FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit(FAKE, None, 2, 16, 2, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit(FAKE, None, 2, 16, 0, -0.1, FAKE, FAKE, None) == _lib.EINVAL     # delta < 0
+    assert L.dllm_commit(FAKE, None, 2, 8193, 1, 0.9, FAKE, FAKE, None) == _lib.EUNSUPPORTED
+    assert L.dllm_commit(None, None, 2, 16, 1, 0.9, FAKE, FAKE, None) == _lib.EINVAL
 
 
 def test_pack_weights_validation():

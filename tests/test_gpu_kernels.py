@@ -274,6 +274,37 @@ def test_commit_outside_exactness_precondition_uses_sequential_sums():
     _check_commit(c, 0.1)
 
 
+def _check_rule(c, rule, param, m_valid=None):
+    n, order = stc.dllm_commit(dev(c), rule, param, dev(m_valid) if m_valid is not None else None)
+    rn, ro = ofre.commit(c, m_valid, rule, param)
+    assert np.array_equal(n.cpu().numpy(), rn), (rule, param)
+    assert np.array_equal(order.cpu().numpy(), ro)
+    return n.cpu().numpy()
+
+
+@pytest.mark.parametrize("m", [1, 5, 256, 1000, 8192])
+def test_commit_rules_bit_exact(m):
+    """dllm_commit under the Frechet, factor and threshold rules against the oracle, bit for bit;
+    on the same profiles Frechet(delta) >= factor(1 - delta) (Corollary 4.4)."""
+    _log(f"commit rules m={m}")
+    g = synth.rng(906, m)
+    c = (1 - g.uniform(0, 0.3, (6, m)) ** 2).astype(np.float32)
+    c[1] = g.uniform(0, 1, m)
+    c[2] = np.float32(0.9)                                   # all tied, equal to tau below
+    if m >= 5:
+        c[3, :5] = [0.99, 0.95, 0.82, 0.78, 0.74]
+    mv = np.array([m, m, m, min(m, 5), m // 2, 0], np.int32)
+    for delta in [0.0, 0.1, 0.25]:
+        nf = _check_rule(c, "frechet", delta, mv)
+        nc = _check_rule(c, "factor", 1.0 - delta, mv)
+        assert np.all(nf >= nc)
+    for f in [0.0, 0.5, 0.75, 2.0]:
+        _check_rule(c, "factor", f, mv)
+    for tau in [0.0, 0.5, float(np.float32(0.9)), 0.95, 1.5]:
+        _check_rule(c, "threshold", tau)
+        _check_rule(c, "threshold", tau, mv)
+
+
 def test_confidence_then_commit_full_end_of_step():
     """End of step at full size: confidence over [8 x 256, 126464] logits, then commit with
     delta = 0.1; the commit must agree exactly with the oracle rule applied to the GPU confidences
