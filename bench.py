@@ -44,6 +44,7 @@ L = 32
 D, H, DH, F = 4096, 32, 128, 12288
 V, M_CAND = 126464, 256
 B_WINDOW, DELTA = 32, 0.1
+APD_ALPHA, APD_BETA = 0.1, 0.1
 
 # name -> shape of the run; sigma(l) is the drift of layer l's inputs
 WORKLOADS = {
@@ -452,6 +453,47 @@ def main():
             commit_rules[name] = {"tokens_per_seq": round(float(nc.float().mean()), 2),
                                   "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
 
+    # adaptive parallel decoding on the same positions: the previous step's logits are this step's
+    # with N(0, 0.3^2) noise; thresholds start at 0.9 (alpha = beta = 0.1: the page leaves them
+    # open); one call streams both [B*256, V] logit matrices
+    apd = None
+    if wl["end"]:
+        R = B * M_CAND
+        zprev = wd.drifted_logits(logits, 0.3, CFG)
+        tau = torch.empty((R,), dtype=torch.float32, device=dev)
+        zmax = torch.empty((R,), dtype=torch.float32, device=dev)
+        ca = torch.empty((R,), dtype=torch.float32, device=dev)
+        ta = torch.empty((R,), dtype=torch.int32, device=dev)
+        hh = torch.empty((R,), dtype=torch.float32, device=dev)
+
+        def apd_pair():
+            tau.fill_(0.9)
+            stc.dllm_apd(zprev, None, V, APD_ALPHA, APD_BETA, tau, zmax, conf=ca, token=ta)
+            stc.dllm_apd(logits, zprev, V, APD_ALPHA, APD_BETA, tau, zmax, conf=ca, token=ta,
+                         h_instab=hh)
+
+        apd_pair()
+        nc, _ = stc.dllm_commit(ca.view(B, M_CAND), "tau", tau=tau.view(B, M_CAND))
+        torch.cuda.synchronize()
+        toks = float(nc.float().mean())
+        h_mean = float(hh.mean())
+        reps = 10
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            stc.dllm_apd(logits, zprev, V, APD_ALPHA, APD_BETA, tau, zmax, conf=ca, token=ta)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        apd_bytes = 2.0 * R * V * 2
+        apd = {"kernel": "k_apd (concentration, instability, thresholds; two logit matrices)",
+               "us_per_call": round(us, 2), "GBps": round(apd_bytes / (us * 1e-6) / 1e9, 1),
+               "hbm_frac": round(apd_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+               "alpha": APD_ALPHA, "beta": APD_BETA, "tau0": 0.9,
+               "tokens_per_seq": round(toks, 2), "mean_instability": round(h_mean, 4)}
+        del zprev
+
     # roofline of the dominant kernel, timed with HIP events on the library's stream
     if wl["layers"]:
         gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l in range(L_)) * K
@@ -590,6 +632,7 @@ def main():
         "rows_per_layer_min_max": [int(M_l.min()), int(M_l.max())],
         "kernels": kernels,
         "commit_rules": commit_rules,
+        "apd": apd,
         "roofline": roofline,
         "dense": dense,
         "cpu_baseline": cpu,

@@ -12,7 +12,8 @@
  *                        with K/V and output rows scattered back into caller-owned caches
  *   dllm_confidence      per-position softmax confidence and argmax over the vocabulary
  *   frechet_commit       sort, prefix sum and the Frechet margin rule -> how many positions commit
- *   dllm_commit          the same with the factor or threshold rule instead (rule comparison)
+ *   dllm_commit          the same with the factor, threshold or per-position threshold rule
+ *   dllm_apd             adaptive-parallel-decoding signals and per-position thresholds
  *   dcu_pack_weights, dcu_pack_gate_up   the projections' blocked weight layout (set-up, not a step)
  *
  * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
@@ -267,17 +268,49 @@ int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t
  *   DCU_COMMIT_FRECHET    param = delta >= 0: exactly frechet_commit;
  *   DCU_COMMIT_FACTOR     param = f: n* = max{n : (n+1)(1 - c_(n)) < f} (fp64), else 1;
  *   DCU_COMMIT_THRESHOLD  param = tau: every candidate with c_i >= tau (fp64), at least 1; these
- *                         are the first n* entries of `order`.
- * Arguments, outputs (order is the same for every rule; n_commit is 0 for a row without
- * candidates) and limits as frechet_commit.
+ *                         are the first n* entries of `order`;
+ *   DCU_COMMIT_TAU        per-candidate thresholds tau [B, m] fp32 (adaptive parallel decoding,
+ *                         Dynamic-dLLM notes Key design 3, from dllm_apd): every candidate with
+ *                         c_i >= tau_i commits (fp32 compare), at least 1 (the most confident);
+ *                         `order` lists the passing candidates first, then the others, each group
+ *                         by (conf desc, slot asc); param is ignored.
+ * tau is read only for DCU_COMMIT_TAU (NULL otherwise). Other arguments, outputs (n_commit is 0 for
+ * a row without candidates; for the first three rules order is frechet_commit's) and limits as
+ * frechet_commit.
  * Errors: EINVAL on NULL conf/n_commit/order, B <= 0, m <= 0, an unknown rule, a NaN or infinite
- *         param, or delta < 0; EUNSUPPORTED if m > 8192.
+ *         param, delta < 0, or DCU_COMMIT_TAU without tau; EUNSUPPORTED if m > 8192.
  */
 #define DCU_COMMIT_FRECHET 0
 #define DCU_COMMIT_FACTOR 1
 #define DCU_COMMIT_THRESHOLD 2
+#define DCU_COMMIT_TAU 3
 int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m, int32_t rule,
-                double param, int32_t* n_commit, int32_t* order, void* stream);
+                double param, const float* tau, int32_t* n_commit, int32_t* order, void* stream);
+
+/*
+ * dllm_apd -- adaptive-parallel-decoding signals and per-position thresholds of one step.
+ * Dynamic-dLLM notes, Key design 3: with z the softmax distribution (temperature 1) of a position,
+ * concentration c = 1 - max_{v != argmax} z_v, temporal instability H = 1 - cos(z^t, z^{t+1})
+ * against the previous step's distribution, and tau^t = tau^{t+1} - alpha c + beta H.
+ *
+ * logits       [R, ld] of dtype DCU_BF16 or DCU_F32, this step; the first V columns are used.
+ * logits_prev  the same positions' logits of the previous step (same shape and dtype), or NULL at
+ *              the first step (then H = 0).
+ * alpha, beta  >= 0 (the page leaves them open).
+ * tau          [R] fp32 in/out: tau^{t+1} in (initialise near 0.9), tau^t out.
+ * zmax         [R] fp32 in/out: in, the previous step's row max of logits_prev (read only when
+ *              logits_prev is given; it is what this call wrote last step); out, this step's.
+ * conf, token  [R] out: the largest probability and its (lowest) index, as dllm_confidence.
+ * c_conc, h_instab  [R] fp32 out, or NULL: c and H.
+ * Sums of exponentials are fp32 per 8 terms, fp64 across them; the cosine uses
+ * D / sqrt(Q P) with D = sum e q, Q = sum e^2, P = sum q^2 (e, q the unnormalised softmax terms).
+ * Errors: EINVAL on NULL logits/tau/zmax/conf/token, R <= 0, V <= 0, ld < V, a bad dtype, alpha
+ *         or beta negative, NaN or infinite; EUNSUPPORTED if ld is not a multiple of 8 (bf16) or
+ *         4 (fp32), a pointer is not 16-byte aligned, or V > 2^31 - 17.
+ */
+int dllm_apd(const void* logits, const void* logits_prev, int32_t dtype, int64_t R, int64_t V,
+             int64_t ld, float alpha, float beta, float* tau, float* zmax, float* conf,
+             int32_t* token, float* c_conc, float* h_instab, void* stream);
 
 #ifdef __cplusplus
 }

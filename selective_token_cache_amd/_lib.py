@@ -60,7 +60,10 @@ EXPORTS = {
                                     ctypes.POINTER(_vp), _i32]),
     "dllm_confidence": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
-    "dllm_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
+    "dllm_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp,
+                                   _vp]),
+    "dllm_apd": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -316,24 +319,57 @@ def frechet_commit(conf: torch.Tensor, delta: float, m_valid: torch.Tensor | Non
     return n_commit, order
 
 
-COMMIT_RULES = {"frechet": 0, "factor": 1, "threshold": 2}  # DCU_COMMIT_*
+COMMIT_RULES = {"frechet": 0, "factor": 1, "threshold": 2, "tau": 3}  # DCU_COMMIT_*
 
 
-def dllm_commit(conf: torch.Tensor, rule: str, param: float, m_valid: torch.Tensor | None = None,
-                n_commit=None, order=None, stream=None):
+def dllm_commit(conf: torch.Tensor, rule: str, param: float = 0.0, m_valid: torch.Tensor | None = None,
+                tau: torch.Tensor | None = None, n_commit=None, order=None, stream=None):
     """conf [B, m] fp32 -> n_commit [B] int32, order [B, m] int32 under rule 'frechet' (param =
-    delta), 'factor' (param = f) or 'threshold' (param = tau)."""
+    delta), 'factor' (param = f), 'threshold' (param = tau) or 'tau' (per-candidate thresholds
+    tau [B, m] fp32)."""
     if rule not in COMMIT_RULES:
         raise ValueError(f"rule must be one of {sorted(COMMIT_RULES)}")
     _need(conf, "conf", torch.float32)
     B, m = conf.shape
+    if rule == "tau":
+        _need(tau, "tau", torch.float32, (B, m))
+    else:
+        tau = None
     if m_valid is not None:
         _need(m_valid, "m_valid", torch.int32, (B,))
     n_commit = torch.empty((B,), dtype=torch.int32, device=conf.device) if n_commit is None else n_commit
     order = torch.empty((B, m), dtype=torch.int32, device=conf.device) if order is None else order
     _need(n_commit, "n_commit", torch.int32, (B,))
     _need(order, "order", torch.int32, (B, m))
-    st = load().dllm_commit(_p(conf), _p(m_valid), B, m, COMMIT_RULES[rule], float(param),
+    st = load().dllm_commit(_p(conf), _p(m_valid), B, m, COMMIT_RULES[rule], float(param), _p(tau),
                             _p(n_commit), _p(order), _stream(stream))
     _check("dllm_commit", st)
     return n_commit, order
+
+
+def dllm_apd(logits: torch.Tensor, logits_prev: torch.Tensor | None, V: int, alpha: float,
+             beta: float, tau: torch.Tensor, zmax: torch.Tensor, conf=None, token=None,
+             c_conc=None, h_instab=None, stream=None):
+    """logits [R, ld] (bf16 or fp32) of this step, logits_prev the previous step's or None; tau and
+    zmax [R] fp32 state updated in place -> (conf [R], token [R], c [R] or None, H [R] or None)."""
+    _need(logits, "logits")
+    if logits.dim() != 2 or logits.dtype not in _DT:
+        raise ValueError("logits must be [R, ld] bf16 or fp32")
+    R, ld = logits.shape
+    if logits_prev is not None:
+        _need(logits_prev, "logits_prev", logits.dtype, (R, ld))
+    _need(tau, "tau", torch.float32, (R,))
+    _need(zmax, "zmax", torch.float32, (R,))
+    dev_ = logits.device
+    conf = torch.empty((R,), dtype=torch.float32, device=dev_) if conf is None else conf
+    token = torch.empty((R,), dtype=torch.int32, device=dev_) if token is None else token
+    _need(conf, "conf", torch.float32, (R,))
+    _need(token, "token", torch.int32, (R,))
+    for name, t in (("c_conc", c_conc), ("h_instab", h_instab)):
+        if t is not None:
+            _need(t, name, torch.float32, (R,))
+    st = load().dllm_apd(_p(logits), _p(logits_prev), _DT[logits.dtype], R, V, ld, float(alpha),
+                         float(beta), _p(tau), _p(zmax), _p(conf), _p(token), _p(c_conc),
+                         _p(h_instab), _stream(stream))
+    _check("dllm_apd", st)
+    return conf, token, c_conc, h_instab

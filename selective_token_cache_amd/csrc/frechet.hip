@@ -14,6 +14,8 @@
 // The same kernel applies the two rules that page compares against (its motivation section): the
 // factor rule, n* = max{n : (n+1)(1 - c_(n)) < f}, and the threshold rule, every candidate with
 // c_i >= tau (a prefix of the sorted order); both in fp64, both commit at least one candidate.
+// With per-candidate thresholds (adaptive parallel decoding, Dynamic-dLLM notes Key design 3) every
+// candidate with c_i >= tau_i commits (fp32 compare); those lead the order, at least one commits.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -44,9 +46,15 @@ __device__ __forceinline__ double wave_incl_scan_f64(double v) {
 __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ conf,
                                                       const int32_t* __restrict__ m_valid, int m,
                                                       int rule, double param,
+                                                      const float* __restrict__ tau,
                                                       int32_t* __restrict__ n_commit,
                                                       int32_t* __restrict__ order) {
   const double delta = param;
+  // per-candidate thresholds: the pass flag is the key's top bit (passing candidates sort first),
+  // the confidence bits sit below it and the slot in the low 31 bits
+  const bool per_tau = rule == DCU_COMMIT_TAU;
+  const int vshift = per_tau ? 31 : 32;
+  const uint64_t slot_mask = per_tau ? 0x7fffffffull : 0xffffffffull;
   extern __shared__ uint64_t keys[];  // P2 entries
   __shared__ double wsum[kThreads / kWave];
   __shared__ int s_flag[17];
@@ -65,18 +73,25 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
   int P2 = 1;
   while (P2 < mv) P2 <<= 1;
   // load keys and test the exactness precondition
-  int bad = 0;
+  int bad = 0, npass = 0;
   for (int i = t; i < P2; i += kThreads) {
     if (i < mv) {
       const float v = c[i];
       const float av = fabsf(v);
       bad |= !(v == 0.0f || (av >= 0x1p-17f && av <= 1.0f));
-      keys[i] = (uint64_t(desc_key(v)) << 32) | uint32_t(i);
+      uint64_t k = (uint64_t(desc_key(v)) << vshift) | uint32_t(i);
+      if (per_tau) {
+        const bool pass = v >= tau[int64_t(b) * m + i];
+        npass += pass ? 1 : 0;
+        k |= uint64_t(pass ? 0 : 1) << 63;
+      }
+      keys[i] = k;
     } else {
       keys[i] = ~uint64_t(0);
     }
   }
   const int nbad = block_sum_int(bad, s_flag);
+  const int n_pass = per_tau ? block_sum_int(npass, s_flag) : 0;
   // bitonic sort, ascending keys
   for (int k = 2; k <= P2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -99,13 +114,15 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
   const int i0 = t * E;
   // value of sorted entry i (inverse of desc_key)
   auto value_at = [&](int i) -> double {
-    const uint32_t dk = uint32_t(keys[i] >> 32);
+    const uint32_t dk = uint32_t(keys[i] >> vshift);
     uint32_t u = ~dk;
     u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
     return double(__uint_as_float(u));
   };
   int best = 0;
-  if (rule != DCU_COMMIT_FRECHET) {
+  if (per_tau) {
+    best = n_pass;  // the passing candidates lead the order
+  } else if (rule != DCU_COMMIT_FRECHET) {
     // per-candidate tests, no sums: (n+1)(1 - c_(n)) < f, or c_(n) >= tau
     for (int e = 0; e < E; ++e) {
       const int i = i0 + e;
@@ -156,18 +173,20 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
     for (int w = 0; w < kThreads / kWave; ++w) bst = s_best[w] > bst ? s_best[w] : bst;
     n_commit[b] = bst > 0 ? bst : 1;
   }
-  for (int i = t; i < m; i += kThreads) ord[i] = i < mv ? int32_t(uint32_t(keys[i])) : -1;
+  for (int i = t; i < m; i += kThreads) ord[i] = i < mv ? int32_t(keys[i] & slot_mask) : -1;
 }
 
 }  // namespace
 }  // namespace dcu
 
 extern "C" int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m,
-                           int32_t rule, double param, int32_t* n_commit, int32_t* order,
-                           void* stream) {
+                           int32_t rule, double param, const float* tau, int32_t* n_commit,
+                           int32_t* order, void* stream) {
   if (!conf || !n_commit || !order || B <= 0 || m <= 0) return DCU_EINVAL;
-  if (rule != DCU_COMMIT_FRECHET && rule != DCU_COMMIT_FACTOR && rule != DCU_COMMIT_THRESHOLD)
+  if (rule != DCU_COMMIT_FRECHET && rule != DCU_COMMIT_FACTOR && rule != DCU_COMMIT_THRESHOLD &&
+      rule != DCU_COMMIT_TAU)
     return DCU_EINVAL;
+  if (rule == DCU_COMMIT_TAU && !tau) return DCU_EINVAL;
   if (param != param || param - param != 0.0) return DCU_EINVAL;  // NaN or infinite
   if (rule == DCU_COMMIT_FRECHET && !(param >= 0.0)) return DCU_EINVAL;
   if (m > dcu::kMaxM) return DCU_EUNSUPPORTED;
@@ -179,7 +198,7 @@ extern "C" int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B,
     return DCU_EHIP;
   hipLaunchKernelGGL(dcu::k_frechet, dim3(unsigned(B)), dim3(dcu::kThreads), lds,
                      static_cast<hipStream_t>(stream), conf, m_valid, int(m), int(rule), param,
-                     n_commit, order);
+                     rule == DCU_COMMIT_TAU ? tau : nullptr, n_commit, order);
   DCU_LAUNCH_CHECK();
   return DCU_OK;
 }
@@ -187,5 +206,6 @@ extern "C" int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B,
 extern "C" int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m,
                               double delta, int32_t* n_commit, int32_t* order, void* stream) {
   if (!(delta >= 0.0)) return DCU_EINVAL;  // also rejects NaN
-  return dllm_commit(conf, m_valid, B, m, DCU_COMMIT_FRECHET, delta, n_commit, order, stream);
+  return dllm_commit(conf, m_valid, B, m, DCU_COMMIT_FRECHET, delta, nullptr, n_commit, order,
+                     stream);
 }

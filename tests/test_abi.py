@@ -94,12 +94,32 @@ def test_confidence_and_commit_validation():
     assert L.frechet_commit(FAKE, None, 2, 16, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 0, 16, 0.1, FAKE, FAKE, None) == _lib.EINVAL
     assert L.frechet_commit(FAKE, None, 2, 8193, 0.1, FAKE, FAKE, None) == _lib.EUNSUPPORTED
-    assert L.dllm_commit(FAKE, None, 2, 16, 3, 0.5, FAKE, FAKE, None) == _lib.EINVAL      # rule
-    assert L.dllm_commit(FAKE, None, 2, 16, 1, float("inf"), FAKE, FAKE, None) == _lib.EINVAL
-    assert L.dllm_commit(FAKE, None, 2, 16, 2, float("nan"), FAKE, FAKE, None) == _lib.EINVAL
-    assert L.dllm_commit(FAKE, None, 2, 16, 0, -0.1, FAKE, FAKE, None) == _lib.EINVAL     # delta < 0
-    assert L.dllm_commit(FAKE, None, 2, 8193, 1, 0.9, FAKE, FAKE, None) == _lib.EUNSUPPORTED
-    assert L.dllm_commit(None, None, 2, 16, 1, 0.9, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit(FAKE, None, 2, 16, 4, 0.5, None, FAKE, FAKE, None) == _lib.EINVAL  # rule
+    assert L.dllm_commit(FAKE, None, 2, 16, 1, float("inf"), None, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit(FAKE, None, 2, 16, 2, float("nan"), None, FAKE, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit(FAKE, None, 2, 16, 0, -0.1, None, FAKE, FAKE, None) == _lib.EINVAL  # delta
+    assert L.dllm_commit(FAKE, None, 2, 16, 3, 0.0, None, FAKE, FAKE, None) == _lib.EINVAL   # no tau
+    assert L.dllm_commit(FAKE, None, 2, 8193, 1, 0.9, None, FAKE, FAKE, None) == _lib.EUNSUPPORTED
+    assert L.dllm_commit(None, None, 2, 16, 1, 0.9, None, FAKE, FAKE, None) == _lib.EINVAL
+
+
+def test_apd_validation():
+    L = stc.load()
+
+    def call(logits=FAKE, R=4, V=10, ld=16, alpha=0.1, beta=0.1, tau=FAKE, dtype=1):
+        return L.dllm_apd(logits, None, dtype, R, V, ld, alpha, beta, tau, FAKE, FAKE, FAKE, None,
+                          None, None)
+
+    assert call(logits=None) == _lib.EINVAL
+    assert call(tau=None) == _lib.EINVAL
+    assert call(R=0) == _lib.EINVAL
+    assert call(ld=8) == _lib.EINVAL                 # ld < V
+    assert call(alpha=-0.1) == _lib.EINVAL
+    assert call(beta=float("nan")) == _lib.EINVAL
+    assert call(dtype=5) == _lib.EINVAL
+    assert call(ld=12) == _lib.EUNSUPPORTED           # bf16 rows not a whole number of 16-B chunks
+    odd = ctypes.c_void_p(256 + 4)
+    assert call(logits=odd) == _lib.EUNSUPPORTED
 
 
 def test_pack_weights_validation():

@@ -317,3 +317,79 @@ def test_confidence_then_commit_full_end_of_step():
     rn, ro = ofre.frechet_commit(ch, None, 0.1)
     assert np.array_equal(n.cpu().numpy(), rn)
     assert np.array_equal(order.cpu().numpy(), ro)
+
+
+# ----------------------------------------------------------------------------- APD (next row f2)
+from oracle import apd as oapd  # noqa: E402
+
+
+def _apd_case(g, R, V, bf16):
+    z, _ = synth.planted_logits(g, R, V, bf16=bf16)
+    zp, _ = synth.planted_logits(g, R, V, bf16=bf16)
+    if R > 3:
+        zp[1] = z[1]                               # an unchanged distribution: H = 0
+        vals = synth.bf16_to_f32(z[2]) if bf16 else z[2]
+        z[2, 3 % V] = z[2, int(np.argmax(vals))]   # a tie at the top (same bit pattern)
+    # rows padded to whole 16-byte chunks with large values that must be ignored (columns >= V)
+    ld = -(-V // (8 if bf16 else 4)) * (8 if bf16 else 4)
+    big = synth.f32_to_bf16(np.array([30.0], np.float32))[0] if bf16 else np.float32(30.0)
+    pad = lambda a: np.concatenate([a, np.full((R, ld - V), big, a.dtype)], axis=1)  # noqa: E731
+    return pad(z), pad(zp)
+
+
+@pytest.mark.parametrize("R,V,bf16", [(9, 1, False), (16, 5, True), (37, 1000, True),
+                                      (12, 1003, False), (4, 126464, True)])
+def test_apd_signals_and_thresholds(R, V, bf16):
+    """dllm_apd over two consecutive steps against the oracle: confidence, argmax, concentration,
+    instability and the threshold update; the row max it keeps feeds the next step."""
+    _log(f"apd R={R} V={V} bf16={bf16}")
+    g = synth.rng(907, R, V)
+    z1, z2 = _apd_case(g, R, V, bf16)
+    to_dev = dev_bf16 if bf16 else dev
+    alpha, beta = 0.1, 0.2
+    tau = torch.full((R,), 0.9, dtype=torch.float32, device="cuda")
+    zmax = torch.empty((R,), dtype=torch.float32, device="cuda")
+    c1 = torch.empty_like(tau)
+    h1 = torch.empty_like(tau)
+    # step 1: no previous distribution (H = 0)
+    conf, tok, _, _ = stc.dllm_apd(to_dev(z1), None, V, alpha, beta, tau, zmax, c_conc=c1, h_instab=h1)
+    pm, rt, rc, rh = oapd.signals(z1, None, V)
+    assert np.array_equal(tok.cpu().numpy(), rt)
+    assert_rel(conf.cpu().numpy(), pm)
+    assert np.allclose(c1.cpu().numpy(), rc, rtol=0, atol=2e-6)
+    assert np.all(h1.cpu().numpy() == 0)
+    tau_ref = oapd.update_threshold(np.full(R, 0.9, np.float32), rc, rh, alpha, beta)
+    assert np.allclose(tau.cpu().numpy(), tau_ref, rtol=0, atol=1e-6)
+    zv = synth.bf16_to_f32(z1[:, :V]) if bf16 else z1[:, :V]
+    assert np.array_equal(zmax.cpu().numpy(), zv.max(axis=1))
+    # step 2: the previous logits and the row max kept by step 1
+    tau_prev = tau.cpu().numpy().copy()
+    conf, tok, _, _ = stc.dllm_apd(to_dev(z2), to_dev(z1), V, alpha, beta, tau, zmax, c_conc=c1,
+                                   h_instab=h1)
+    pm, rt, rc, rh = oapd.signals(z2, z1, V)
+    assert np.array_equal(tok.cpu().numpy(), rt)
+    assert_rel(conf.cpu().numpy(), pm)
+    assert np.allclose(c1.cpu().numpy(), rc, rtol=0, atol=2e-6)
+    assert np.allclose(h1.cpu().numpy(), rh, rtol=0, atol=1e-5)
+    assert np.allclose(tau.cpu().numpy(), oapd.update_threshold(tau_prev, rc, rh, alpha, beta),
+                       rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("m", [1, 7, 256, 2048])
+def test_commit_per_position_thresholds(m):
+    """dllm_commit with per-candidate thresholds against the oracle's unmask rule, bit for bit
+    (same conf and tau on both sides)."""
+    g = synth.rng(908, m)
+    B = 5
+    conf = g.uniform(0.3, 1.0, (B, m)).astype(np.float32)
+    conf[1, ::3] = conf[1, 0]                          # ties
+    tau = g.uniform(0.5, 1.0, (B, m)).astype(np.float32)
+    tau[2] = 2.0                                        # nothing passes: the most confident commits
+    tau[3, : m // 2] = conf[3, : m // 2]                # passes on equality
+    mv = np.array([m, m, m, m // 2, 0], np.int32)
+    for mvalid in (None, mv):
+        n, order = stc.dllm_commit(dev(conf), "tau", m_valid=dev(mvalid) if mvalid is not None else None,
+                                   tau=dev(tau))
+        rn, ro = oapd.unmask(conf, tau, mvalid)
+        assert np.array_equal(n.cpu().numpy(), rn)
+        assert np.array_equal(order.cpu().numpy(), ro)

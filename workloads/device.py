@@ -68,6 +68,13 @@ def planted_logits(R: int, V: int, cfg: int, lo: float = 2.0, hi: float = 12.0, 
     return z.to(torch.bfloat16)
 
 
+def drifted_logits(z: torch.Tensor, sigma: float, cfg: int) -> torch.Tensor:
+    """The same positions' logits one step earlier: z + N(0, sigma^2) per entry, bf16."""
+    g = gen(cfg, 21, device=z.device)
+    n = torch.randn(z.shape, generator=g, device=z.device, dtype=torch.float32)
+    return (z.float() + sigma * n).to(torch.bfloat16)
+
+
 def key_positions(B: int, P: int, lo: int, hi: int, cfg: int, device="cuda") -> torch.Tensor:
     g = gen(cfg, 30, device="cpu")
     out = torch.stack([torch.randperm(hi - lo, generator=g)[:P] + lo for _ in range(B)])
