@@ -453,6 +453,34 @@ def main():
             commit_rules[name] = {"tokens_per_seq": round(float(nc.float().mean()), 2),
                                   "us_per_call": round(e0.elapsed_time(e1) / reps * 1e3, 2)}
 
+    # the V-feature distance (Value vectors recomputed for every row, compared with the V cache)
+    # against the input distance the step uses, on layer 0
+    vfeat = None
+    if wl["layers"]:
+        v_new = torch.empty((B, N, D), dtype=torch.bfloat16, device=dev)
+        vcache = vc[0].view(B, N, D)
+
+        def timed(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e3
+
+        t_vf = timed(lambda: stc.dcu_v_features(layers[0][0], x_cur[0], v_out=v_new, workspace=ws))
+        t_vd = timed(lambda: stc.dcu_distance(v_new, vcache, dist=dist, want_mean=False))
+        t_xd = timed(lambda: stc.dcu_distance(x_cur[0], x_prev[0], dist=dist, want_mean=False))
+        vfeat = {"v_features_us": round(t_vf, 2), "v_distance_us": round(t_vd, 2),
+                 "input_distance_us": round(t_xd, 2),
+                 "v_proxy_over_input_proxy": round((t_vf + t_vd) / t_xd, 2),
+                 "v_features_TFLOPps": round(2.0 * B * N * D * D / (t_vf * 1e-6) / 1e12, 1)}
+        del v_new
+
     # adaptive parallel decoding on the same positions: the previous step's logits are this step's
     # with N(0, 0.3^2) noise; thresholds start at 0.9 (alpha = beta = 0.1: the page leaves them
     # open); one call streams both [B*256, V] logit matrices
@@ -633,6 +661,7 @@ def main():
         "kernels": kernels,
         "commit_rules": commit_rules,
         "apd": apd,
+        "v_feature_distance": vfeat,
         "roofline": roofline,
         "dense": dense,
         "cpu_baseline": cpu,

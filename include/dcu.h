@@ -207,6 +207,19 @@ int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel
                         size_t workspace_bytes, void* stream);
 
 /*
+ * dcu_v_features -- the Value vectors of every row of a layer, for the V-feature distance.
+ * (The alternative distance feature of the dLLM-Cache design the Dynamic-dLLM notes compare their
+ * input proxy against: the cosine distance is taken between this step's Value vectors, recomputed
+ * for all N rows, and the cached ones; apply dcu_distance to v_out and the V cache.)
+ * v_out = RMSNorm(x; g_attn) W_v^T for all B*N rows, [B, N, d] bf16 (the V-cache row layout), with
+ * W_v the rows 2d .. 3d-1 of the layer's blocked W_qkv.
+ * workspace  at least dcu_selective_layer_workspace(w, B, N, B*N) bytes, 256-byte aligned.
+ * Errors: as dcu_selective_layer (layer shape, alignment, workspace).
+ */
+int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, int32_t N, void* v_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * dcu_selective_layer_staged -- dcu_selective_layer with per-stage timing marks, for measurement.
  * Identical work and results; additionally records the caller-created hipEvent_t events[0] before
  * the first kernel and events[i] after stage i on `stream`, for the DCU_LAYER_STAGES stages

@@ -94,3 +94,13 @@ def selective_layer(w: dict, n_heads: int, head_dim: int, eps: float, x_in: np.n
         kc[b], vc[b], yo[b] = selective_layer_seq(w64, n_heads, head_dim, eps, x[b], rows,
                                                   kc[b], vc[b], yo[b])
     return kc, vc, yo
+
+
+def v_features(w: dict, eps: float, x: np.ndarray) -> np.ndarray:
+    """Value vectors of every row (the V-feature distance's input, dLLM-Cache style): [B, N, d]
+    fp64 = RMSNorm(x; g_attn) W_v^T, W_v the last d rows of W_qkv."""
+    w64 = weights64(w)
+    d = w64["w_o"].shape[0]
+    x64 = as64(x)
+    xn = rmsnorm(x64, w64["g_attn"], eps)
+    return xn @ w64["w_qkv"][2 * d:3 * d].T

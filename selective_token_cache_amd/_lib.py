@@ -54,6 +54,8 @@ EXPORTS = {
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
                                            _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "dcu_v_features": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
+                                      ctypes.c_size_t, _vp]),
     "dcu_selective_layer_staged": (ctypes.c_int,
                                    [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp,
@@ -373,3 +375,22 @@ def dllm_apd(logits: torch.Tensor, logits_prev: torch.Tensor | None, V: int, alp
                          _p(h_instab), _stream(stream))
     _check("dllm_apd", st)
     return conf, token, c_conc, h_instab
+
+
+def dcu_v_features(layer: Layer, x_in: torch.Tensor, v_out=None, workspace=None, stream=None):
+    """Value vectors of every row: x_in [B, N, d] bf16 -> v_out [B, N, d] bf16 (the V-cache row
+    layout), RMSNorm(x; g_attn) W_v^T."""
+    _need(x_in, "x_in", torch.bfloat16)
+    B, N, d = x_in.shape
+    if d != layer.d:
+        raise ValueError("x_in width does not match the layer")
+    v_out = torch.empty_like(x_in) if v_out is None else v_out
+    _need(v_out, "v_out", torch.bfloat16, (B, N, d))
+    need = layer.workspace_bytes(B, N, B * N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+    _need(workspace, "workspace", torch.uint8)
+    st = load().dcu_v_features(ctypes.byref(layer.desc), _p(x_in), B, N, _p(v_out), _p(workspace),
+                               workspace.numel(), _stream(stream))
+    _check("dcu_v_features", st)
+    return v_out

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ a
 }
 
 // ------------------------------------------------------------------------------ 3/5/7/8. GEMM
-enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3 };
+enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3, EPI_VPROJ = 4 };
 
 struct GemmArgs {
   const uint16_t* A;    // [M, K] compacted rows (workspace)
@@ -249,7 +249,7 @@ struct GemmArgs {
   const uint16_t* x;    // RESID: residual rows (global, via rowmap)
   float* a;             // RESID: out; DOWN: residual in
   uint16_t* h;          // SWIGLU: out [M, F]
-  uint16_t* y;          // DOWN: scatter target
+  uint16_t* y;          // DOWN: scatter target; VPROJ: V rows out (via the row map)
   float* part;          // split tail partial tiles [2 * grid, BM * BN] fp32
 };
 
@@ -344,7 +344,8 @@ __device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
 // batch 8, N = 1024, output 58.0 + 17.8 (split fixup) -> 60.4 + 6.8 us, down and QKV even.
 template <int EPI, class C>
 constexpr bool early_refill() {
-  return (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_DOWN) && std::is_same<C, CfgSmall>::value;
+  return (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_DOWN || EPI == EPI_VPROJ) &&
+         std::is_same<C, CfgSmall>::value;
 }
 template <int EPI, class C>
 constexpr int split_mode() {
@@ -399,6 +400,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
           o.z = bf_lo(xr.y) + v[2];
           o.w = bf_hi(xr.y) + v[3];
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
+        } else if constexpr (EPI == EPI_VPROJ) {
+          uint2 st;
+          st.x = pack_bf2(v[0], v[1]);
+          st.y = pack_bf2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
         } else {  // EPI_DOWN
           const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
           uint2 st;
@@ -601,6 +607,11 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
               make_float4(bf_lo(xr.x) + w.x, bf_hi(xr.x) + w.y, bf_lo(xr.y) + w.z, bf_hi(xr.y) + w.w);
+        } else if constexpr (EPI == EPI_VPROJ) {
+          uint2 st;
+          st.x = pack_bf2(w.x, w.y);
+          st.y = pack_bf2(w.z, w.w);
+          *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
         } else {  // EPI_DOWN
           const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
           uint2 st;
@@ -1304,6 +1315,63 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   launch_fixup<EPI_DOWN>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
+  return DCU_OK;
+}
+
+extern "C" int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, int32_t N,
+                              void* v_out, void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dcu;
+  int st = validate(w, B, N);
+  if (st != DCU_OK) return st;
+  if (!x_in || !v_out) return DCU_EINVAL;
+  if (!dcu_aligned16(x_in) || !dcu_aligned16(v_out)) return DCU_EUNSUPPORTED;
+  const Layout L = make_layout(w, B, N, 0);
+  if (!workspace || workspace_bytes < L.total) return DCU_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DCU_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Ptrs P{};
+  P.hdr = reinterpret_cast<int*>(ws + L.hdr);
+  P.seq_off = reinterpret_cast<int*>(ws + L.seq_off);
+  P.tile_off = reinterpret_cast<int*>(ws + L.tile_off);
+  P.tile_seq = reinterpret_cast<int*>(ws + L.tile_seq);
+  P.rowmap = reinterpret_cast<int*>(ws + L.rowmap);
+  P.xn = reinterpret_cast<uint16_t*>(ws + L.xn);
+  const int d = w->d;
+  // every row: RMSNorm with the attention gain (the projection input of the layer)
+  const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
+  {
+    const uint16_t* x = static_cast<const uint16_t*>(x_in);
+    const uint16_t* ga_ = static_cast<const uint16_t*>(w->g_attn);
+#define DCU_GATHER(NC)                                                                        \
+  hipLaunchKernelGGL(k_gather_rmsnorm<NC>, dim3(norm_blocks), dim3(256), 0, s, x, nullptr,    \
+                     nullptr, int(B), int(N), L.M_cap, ga_, d, w->rms_eps, P.xn, P)
+    switch (rms_nc(d, false)) {
+      case 1: DCU_GATHER(1); break;
+      case 2: DCU_GATHER(2); break;
+      case 4: DCU_GATHER(4); break;
+      case 8: DCU_GATHER(8); break;
+      case 16: DCU_GATHER(16); break;
+      default: DCU_GATHER(0); break;
+    }
+#undef DCU_GATHER
+  }
+  DCU_LAUNCH_CHECK();
+  // V = xn W_v^T: the W_v rows (2d .. 3d-1) of the blocked W_qkv are its row groups from 2d/16 on
+  GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(ws + L.part);
+  ga.hdr = P.hdr;
+  ga.rowmap = P.rowmap;
+  ga.d = d;
+  ga.A = P.xn;
+  ga.W = static_cast<const uint16_t*>(w->w_qkv) + int64_t(2 * d / 16) * (d / 64) * gemm::kBlockElems;
+  ga.K = d;
+  ga.Nout = d;
+  ga.y = static_cast<uint16_t*>(v_out);
+  launch_gemm<EPI_VPROJ>(ga, s);
+  DCU_LAUNCH_CHECK();
+  launch_fixup<EPI_VPROJ>(ga, s, L.M_cap);
+  DCU_LAUNCH_CHECK();
   return DCU_OK;
 }
 

@@ -252,3 +252,36 @@ def test_full_size_batch8_n2048_sampled():
         keep = np.setdiff1d(np.arange(2048), sel[bb, :cnt[bb]])
         assert np.array_equal(got[2][bb, keep], case.y[bb, keep])
         assert np.array_equal(got[0][bb, keep], case.kc[bb, keep])
+
+
+@pytest.mark.parametrize("shape,B,N", [
+    (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 2, 100),
+    (synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=192), 1, 37),
+    (synth.LLADA8B, 1, 1024),
+])
+def test_v_features_and_v_distance(shape, B, N):
+    """dcu_v_features (RMSNorm + the W_v rows of the blocked W_qkv, every row) against the oracle,
+    then the V-feature distance: dcu_distance on the new Value vectors and the V cache, and the
+    selection it drives, on the same GPU inputs as the oracle's."""
+    from oracle import distance as odist
+    from oracle import select as osel
+    _log(f"v features d={shape.d} B={B} N={N}")
+    case = Case(shape, B, N, seed=shape.d + N + 5)
+    L = case.layer()
+    v = stc.dcu_v_features(L, dev_bf16(case.x))
+    torch.cuda.synchronize()
+    got = synth.bf16_to_f32(host_bf16(v)).reshape(B * N, shape.d)
+    ref = olayer.v_features(case.w, shape.eps, case.x).reshape(B * N, shape.d)
+    e = rel_l2(got, ref)
+    _log(f"  rel-L2 V {e:.2e}")
+    assert e <= TOL
+    vc = dev_bf16(case.vc).view(B, N, shape.d)
+    dist, mean = stc.dcu_distance(v, vc)
+    vh = host_bf16(v)
+    rd, rm = odist.distance_and_mean(vh, case.vc.reshape(B, N, shape.d))
+    assert np.allclose(dist.cpu().numpy(), rd, rtol=1e-5, atol=1e-6)
+    budgets = np.full((B, 1), 16, np.int32)
+    keys = np.full((B, 1), N // 2, np.int32)
+    sel, cnt = stc.dcu_select(dist, dev(budgets), 0, dev(keys), 8)
+    rs, rc = osel.select(dist.cpu().numpy(), budgets, 0, keys, 8)
+    assert np.array_equal(cnt.cpu().numpy(), rc) and np.array_equal(sel.cpu().numpy(), rs)

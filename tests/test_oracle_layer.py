@@ -179,3 +179,19 @@ def test_batched_form_and_bf16_inputs():
                                             shape.eps, ol.as64(x[b]), rows, kc[b], kc[b].copy(),
                                             np.zeros((12, shape.d)))
         assert np.array_equal(y[b], ry)
+
+
+def test_v_features_closed_form():
+    """With the V block of W_qkv the identity, unit gains and eps = 0, the Value vectors are the
+    RMS-normalised inputs: unit mean square and proportional to x row by row."""
+    g = np.random.default_rng(12)
+    d, B, N = 64, 2, 9
+    x = g.normal(0, 3, (B, N, d)).astype(np.float32)
+    w = {"w_qkv": np.zeros((3 * d, d), np.float32), "w_o": np.zeros((d, d), np.float32),
+         "g_attn": np.ones(d, np.float32)}
+    w["w_qkv"][2 * d:] = np.eye(d, dtype=np.float32)
+    w["w_qkv"][:d] = 5.0                                     # the Q and K rows must not leak in
+    v = ol.v_features(w, 0.0, x)
+    assert np.allclose(np.mean(v * v, axis=-1), 1.0, rtol=1e-12)
+    ratio = v / x
+    assert np.allclose(ratio, ratio[..., :1], rtol=1e-12)
