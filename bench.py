@@ -221,6 +221,7 @@ def main():
     ap.add_argument("--workload", default="step", choices=sorted(WORKLOADS))
     ap.add_argument("--dense-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--max-rows", type=int, default=0,
                     help="row bound passed to the layer calls (default: B * min(N, L * b_layer + window))")
     ap.add_argument("--calib-copy", action="store_true",
@@ -637,6 +638,30 @@ def main():
         cpu = cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_buf[cur ^ 1], keys, logits,
                            torch)
 
+    # the same step replayed from a HIP graph (two steps captured, so the layer-mean buffers
+    # alternate as in the eager loop): the library only enqueues kernels, so a whole step captures
+    graph = None
+    if not args.no_graph:
+        try:
+            gph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(gph):
+                step(s_buf[cur ^ 1], s_buf[cur])
+                step(s_buf[cur], s_buf[cur ^ 1])
+            gph.replay()
+            torch.cuda.synchronize()
+            reps = max(1, K // 2)
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                gph.replay()
+            torch.cuda.synchronize()
+            ms_graph = (time.perf_counter() - t0) / (2 * reps) * 1e3
+            graph = {"ms_per_step": round(ms_graph, 3), "layer_steps_per_s": round(L_ / (ms_graph * 1e-3), 2),
+                     "speedup_vs_eager": round(ms_step / ms_graph, 3)}
+            del gph
+        except Exception as exc:  # capture is an optional measurement
+            graph = {"error": str(exc)[:200]}
+
     out = {
         "metric": METRIC,
         "value": round(L_ / (ms_step * 1e-3), 2),
@@ -662,6 +687,7 @@ def main():
         "commit_rules": commit_rules,
         "apd": apd,
         "v_feature_distance": vfeat,
+        "graph": graph,
         "roofline": roofline,
         "dense": dense,
         "cpu_baseline": cpu,
