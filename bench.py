@@ -58,6 +58,11 @@ WORKLOADS = {
     "layer-b1": dict(B=1, N=1024, L=1, b_layer=32, n_keys=1, key_lo=512, cfg=3, layers=True, end=False,
                      sigma=lambda l: 0.01 * (1 + 31 / 8),
                      desc="one selective LLaDA-8B-shaped layer, batch 1, N=1024, budget 32 + window 32"),
+    "step-closed": dict(B=8, N=1024, L=32, b_layer=32, n_keys=4, key_lo=512, cfg=5, layers=True,
+                        end=True, closed=True, sigma=lambda l: 0.01 * (1 + l / 8),
+                        desc="closed-loop 32-layer DCU step + end of step, batch 8, N=1024: layer l+1 "
+                             "reads layer l's output, distances of layers >= 1 on the scattered rows "
+                             "only (with the cache roll), commits give the next step's key positions"),
     "layer-b8-n2048": dict(B=8, N=2048, L=32, b_layer=64, n_keys=4, key_lo=1024, cfg=4, layers=True,
                            end=False, sigma=lambda l: 0.01 * (1 + l / 8),
                            desc="32-layer DCU step without its end, batch 8, N=2048, B_layer=64, "
@@ -279,10 +284,18 @@ def main():
     n_commit = torch.empty((B,), dtype=torch.int32, device=dev)
     order = torch.empty((B, M_CAND), dtype=torch.int32, device=dev)
 
-    # dense fill of every layer's caches from the cached inputs (setup, untimed)
+    closed = wl.get("closed", False)
+    # candidate slot j of a sequence is position 512 + j (the first 256 generated positions)
+    slot_pos = (torch.arange(M_CAND, dtype=torch.int32, device=dev) + N // 2).repeat(B, 1).contiguous()
+
+    # dense fill of every layer's caches from the cached inputs (setup, untimed); in closed loop the
+    # chain runs from the first layer's cached input and each later layer's cached input is a copy
+    # of the previous layer's output
     if wl["layers"]:
         log("dense fill")
         for l in range(L_):
+            if closed and l > 0:
+                x_prev[l].copy_(y[l - 1])
             stc.dcu_selective_layer(layers[l][0], x_prev[l], None, None, kc[l], vc[l], y[l],
                                     max_rows=B * N, workspace=ws)
         torch.cuda.synchronize()
@@ -302,7 +315,12 @@ def main():
         for l in range(L_):
             e = ev[l] if ev is not None else None
             rec(e, 0)
-            stc.dcu_distance(x_cur[l], x_prev[l], dist=dist, want_mean=False)
+            if closed and l > 0:
+                # only the rows layer l-1 scattered can have moved; rolls them into the cache
+                stc.dcu_distance_rows(y[l - 1], x_prev[l], sel_idx[l - 1], sel_cnt[l - 1], dist=dist,
+                                      roll=True)
+            else:
+                stc.dcu_distance(x_cur[l], x_prev[l], dist=dist, want_mean=False)
             rec(e, 1)
             # the layer mean s_l (next step's budget input) comes from the select kernel, which
             # reads every distance of the sequence anyway (one launch fewer per layer)
@@ -310,7 +328,8 @@ def main():
                            mean=s_cur[l])
             if wl["layers"]:
                 le = e[2:] if e is not None and any(x is not None for x in e[2:]) else None
-                stc.dcu_selective_layer(layers[l][0], x_cur[l], sel_idx[l], sel_cnt[l], kc[l], vc[l],
+                x_in = y[l - 1] if closed and l > 0 else x_cur[l]
+                stc.dcu_selective_layer(layers[l][0], x_in, sel_idx[l], sel_cnt[l], kc[l], vc[l],
                                         y[l], max_rows=max_rows, workspace=ws, events=le)
             else:
                 rec(e, 2)
@@ -322,6 +341,11 @@ def main():
         rec(e, 1)
         stc.frechet_commit(conf.view(B, M_CAND), DELTA, n_commit=n_commit, order=order)
         rec(e, 2)
+        if closed:
+            # the committed positions place the next step's windows; the first layer's input
+            # alternates between its two synthetic states (its cached input is the other one)
+            stc.dllm_commit_positions(order, n_commit, slot_pos, N_KEYS, key_pos=keys)
+            x_cur[0], x_prev[0] = x_prev[0], x_cur[0]
 
     def make_events(full):
         """Events of one step: every stage boundary (full), or only the two around the roofline

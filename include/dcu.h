@@ -7,6 +7,7 @@
  *   dcu_budget           per-layer recompute budgets from the previous step's layer means
  *   dcu_distance         per-token cosine distance between a layer's input now and its cached input
  *                        from the previous step, plus the per-group mean (layer dynamics)
+ *   dcu_distance_rows    the same on listed rows only, with the cache roll (closed-loop layers)
  *   dcu_select           per-sequence top-B selection by distance, united with forced windows
  *   dcu_selective_layer  QKV / attention / output projection / SwiGLU FFN on the selected rows only,
  *                        with K/V and output rows scattered back into caller-owned caches
@@ -14,6 +15,7 @@
  *   frechet_commit       sort, prefix sum and the Frechet margin rule -> how many positions commit
  *   dllm_commit          the same with the factor, threshold or per-position threshold rule
  *   dllm_apd             adaptive-parallel-decoding signals and per-position thresholds
+ *   dllm_commit_positions  committed positions -> the next step's key positions
  *   dcu_pack_weights, dcu_pack_gate_up   the projections' blocked weight layout (set-up, not a step)
  *
  * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
@@ -89,6 +91,28 @@ int dcu_budget(const float* s_prev, int32_t B, int32_t L, int32_t b_layer, int32
  */
 int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype, int64_t G, int64_t N,
                  int64_t d, float* dist, float* mean, void* stream);
+
+/*
+ * dcu_distance_rows -- dcu_distance when only listed rows can have changed (closed-loop layers).
+ * Dynamic-dLLM notes, Key design 2 (a token not updated at layer l keeps its cached output, so its
+ * input to layer l+1 is unchanged and its distance there is 0): when layer l+1's input is layer l's
+ * output buffer, only the rows layer l scattered can differ from the cached input, so only those
+ * are read.
+ * x_cur, x_prev  [B, N, d] (dtype DCU_BF16 or DCU_F32), not overlapping. Every row not listed must
+ *                be bitwise equal in both (the caller's guarantee; its distance is reported as 0).
+ * sel_idx, sel_count  [B, N] / [B] int32: the listed positions of each sequence (each at most
+ *                once; counts clamped to [0, N]; entries outside [0, N) skipped), e.g. the previous
+ *                layer's dcu_select output.
+ * dist     [B, N] fp32 out: bit for bit dcu_distance's value on every row under that guarantee.
+ * roll     non-zero: afterwards each listed row of x_cur is copied into x_prev (the cache roll of
+ *          the rows that changed; the others are already equal).
+ * The layer mean is then available from dcu_select (mean argument), which reads every distance.
+ * Errors: EINVAL on NULL pointers, B, N, d <= 0 or a bad dtype; EUNSUPPORTED if d is not a
+ *         multiple of 8 (bf16) or 4 (fp32), a pointer is not 16-byte aligned, or B > 65535.
+ */
+int dcu_distance_rows(const void* x_cur, void* x_prev, int32_t dtype, int64_t B, int64_t N,
+                      int64_t d, const int32_t* sel_idx, const int32_t* sel_count, float* dist,
+                      int32_t roll, void* stream);
 
 /*
  * dcu_select -- recompute set of one layer for each sequence.
@@ -299,6 +323,19 @@ int frechet_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t
 #define DCU_COMMIT_TAU 3
 int dllm_commit(const float* conf, const int32_t* m_valid, int32_t B, int32_t m, int32_t rule,
                 double param, const float* tau, int32_t* n_commit, int32_t* order, void* stream);
+
+/*
+ * dllm_commit_positions -- the positions committed this step, as the next step's key positions.
+ * Dynamic-dLLM notes, Key design 2: the forced window sits around each position unmasked at the
+ * previous step; this closes the loop from a commit to the next step's dcu_select.
+ * order, n_commit  [B, m] / [B] int32 from frechet_commit or dllm_commit.
+ * slot_pos  [B, m] int32: the sequence position of each candidate slot.
+ * key_pos   [B, P] int32 out: the positions of the first min(n_commit[b], P) committed slots (the
+ *           most confident first), -1 after them.
+ * Errors: EINVAL on NULL pointers or B, m, P <= 0.
+ */
+int dllm_commit_positions(const int32_t* order, const int32_t* n_commit, const int32_t* slot_pos,
+                          int32_t B, int32_t m, int32_t P, int32_t* key_pos, void* stream);
 
 /*
  * dllm_apd -- adaptive-parallel-decoding signals and per-position thresholds of one step.

@@ -46,6 +46,8 @@ EXPORTS = {
     "dcu_version": (ctypes.c_int, []),
     "dcu_budget": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "dcu_distance": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "dcu_distance_rows": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
+                                         _vp]),
     "dcu_select": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
                                   _vp, _vp]),
     "dcu_pack_weights": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
@@ -64,6 +66,7 @@ EXPORTS = {
     "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
     "dllm_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, ctypes.c_double, _vp, _vp, _vp,
                                    _vp]),
+    "dllm_commit_positions": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "dllm_apd": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
@@ -155,6 +158,25 @@ def dcu_distance(x_cur: torch.Tensor, x_prev: torch.Tensor, dist=None, mean=None
                              _stream(stream))
     _check("dcu_distance", st)
     return dist, mean
+
+
+def dcu_distance_rows(x_cur: torch.Tensor, x_prev: torch.Tensor, sel_idx: torch.Tensor,
+                      sel_count: torch.Tensor, dist=None, roll: bool = True, stream=None):
+    """x_cur, x_prev [G, N, d]; only the listed rows (sel_idx [G, N], sel_count [G]) may differ ->
+    dist [G, N] fp32 (0 on the other rows); roll copies the listed rows of x_cur into x_prev."""
+    _need(x_cur, "x_cur")
+    _need(x_prev, "x_prev", x_cur.dtype, x_cur.shape)
+    if x_cur.dim() != 3 or x_cur.dtype not in _DT:
+        raise ValueError("x_cur must be [G, N, d] bf16 or fp32")
+    G, N, d = x_cur.shape
+    _need(sel_idx, "sel_idx", torch.int32, (G, N))
+    _need(sel_count, "sel_count", torch.int32, (G,))
+    dist = torch.empty((G, N), dtype=torch.float32, device=x_cur.device) if dist is None else dist
+    _need(dist, "dist", torch.float32, (G, N))
+    st = load().dcu_distance_rows(_p(x_cur), _p(x_prev), _DT[x_cur.dtype], G, N, d, _p(sel_idx),
+                                  _p(sel_count), _p(dist), int(bool(roll)), _stream(stream))
+    _check("dcu_distance_rows", st)
+    return dist
 
 
 def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: torch.Tensor | None,
@@ -394,3 +416,18 @@ def dcu_v_features(layer: Layer, x_in: torch.Tensor, v_out=None, workspace=None,
                                workspace.numel(), _stream(stream))
     _check("dcu_v_features", st)
     return v_out
+
+
+def dllm_commit_positions(order: torch.Tensor, n_commit: torch.Tensor, slot_pos: torch.Tensor,
+                          P: int, key_pos=None, stream=None) -> torch.Tensor:
+    """order [B, m], n_commit [B], slot_pos [B, m] int32 -> key_pos [B, P] int32 (-1 padded)."""
+    _need(order, "order", torch.int32)
+    B, m = order.shape
+    _need(n_commit, "n_commit", torch.int32, (B,))
+    _need(slot_pos, "slot_pos", torch.int32, (B, m))
+    key_pos = torch.empty((B, P), dtype=torch.int32, device=order.device) if key_pos is None else key_pos
+    _need(key_pos, "key_pos", torch.int32, (B, P))
+    st = load().dllm_commit_positions(_p(order), _p(n_commit), _p(slot_pos), B, m, P, _p(key_pos),
+                                      _stream(stream))
+    _check("dllm_commit_positions", st)
+    return key_pos

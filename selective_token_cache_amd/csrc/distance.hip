@@ -50,15 +50,11 @@ __device__ __forceinline__ void acc_f32_pair(Acc& s, uint32_t wa0, uint32_t wa1,
   s.nb1 = fma(b1, b1, s.nb1);
 }
 
+// distance of one row pair by one wave: fp64 sums of the products, XOR flag for identical rows;
+// every lane returns the same value
 template <bool kBf16>
-__global__ __launch_bounds__(256) void k_distance(const uint4* __restrict__ xc,
-                                                  const uint4* __restrict__ xp, int64_t rows,
-                                                  int chunks, float* __restrict__ dist) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
-  if (row >= rows) return;
-  const uint4* a = xc + row * chunks;
-  const uint4* b = xp + row * chunks;
+__device__ __forceinline__ double row_distance(const uint4* __restrict__ a,
+                                               const uint4* __restrict__ b, int chunks, int lane) {
   Acc s;
   for (int base = 0; base < chunks; base += kWave * kUnroll) {
     uint4 ra[kUnroll], rb[kUnroll];
@@ -90,20 +86,61 @@ __global__ __launch_bounds__(256) void k_distance(const uint4* __restrict__ xc,
   double na = wave_sum(s.na0 + s.na1);
   double nb = wave_sum(s.nb0 + s.nb1);
   uint32_t diff = wave_or(s.diff);
-  if (lane == 0) {
-    double d;
-    if (diff == 0u) {
-      d = 0.0;
-    } else if (na == 0.0 && nb == 0.0) {
-      d = 0.0;
-    } else if (na == 0.0 || nb == 0.0) {
-      d = 1.0;
-    } else {
-      d = 1.0 - dot / sqrt(na * nb);
-      d = d < 0.0 ? 0.0 : (d > 2.0 ? 2.0 : d);
-    }
-    dist[row] = float(d);
+  double d;
+  if (diff == 0u) {
+    d = 0.0;
+  } else if (na == 0.0 && nb == 0.0) {
+    d = 0.0;
+  } else if (na == 0.0 || nb == 0.0) {
+    d = 1.0;
+  } else {
+    d = 1.0 - dot / sqrt(na * nb);
+    d = d < 0.0 ? 0.0 : (d > 2.0 ? 2.0 : d);
   }
+  return d;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void k_distance(const uint4* __restrict__ xc,
+                                                  const uint4* __restrict__ xp, int64_t rows,
+                                                  int chunks, float* __restrict__ dist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * kRowsPerBlock + (threadIdx.x / kWave);
+  if (row >= rows) return;
+  const double d = row_distance<kBf16>(xc + row * chunks, xp + row * chunks, chunks, lane);
+  if (lane == 0) dist[row] = float(d);
+}
+
+// Listed rows only (closed-loop chaining: the previous layer scattered exactly these rows, every
+// other row of x_cur equals x_prev bit for bit and has distance 0): one wave per list slot j of
+// sequence b; with roll, the row of x_cur is then copied into x_prev (the cache roll of that row).
+__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0.0f;
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void k_distance_rows(const uint4* __restrict__ xc,
+                                                       uint4* __restrict__ xp, int N, int chunks,
+                                                       const int32_t* __restrict__ sel_idx,
+                                                       const int32_t* __restrict__ sel_count,
+                                                       int roll, float* __restrict__ dist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  int cnt = sel_count[b];
+  cnt = cnt < 0 ? 0 : (cnt > N ? N : cnt);
+  if (j >= cnt) return;
+  const int pos = sel_idx[int64_t(b) * N + j];
+  if (pos < 0 || pos >= N) return;
+  const int64_t row = int64_t(b) * N + pos;
+  const uint4* a = xc + row * chunks;
+  uint4* p = xp + row * chunks;
+  const double d = row_distance<kBf16>(a, p, chunks, lane);
+  if (lane == 0) dist[row] = float(d);
+  if (roll)
+    for (int c = lane; c < chunks; c += kWave) p[c] = a[c];
 }
 
 // one workgroup per group; fixed per-thread strides and a fixed reduction tree
@@ -152,5 +189,37 @@ extern "C" int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype
     hipLaunchKernelGGL(dcu::k_group_mean, dim3(unsigned(G)), dim3(256), 0, s, dist, N, mean);
     DCU_LAUNCH_CHECK();
   }
+  return DCU_OK;
+}
+
+extern "C" int dcu_distance_rows(const void* x_cur, void* x_prev, int32_t dtype, int64_t B,
+                                 int64_t N, int64_t d, const int32_t* sel_idx,
+                                 const int32_t* sel_count, float* dist, int32_t roll,
+                                 void* stream) {
+  if (!x_cur || !x_prev || !sel_idx || !sel_count || !dist || B <= 0 || N <= 0 || d <= 0)
+    return DCU_EINVAL;
+  if (dtype != DCU_BF16 && dtype != DCU_F32) return DCU_EINVAL;
+  const int64_t per_chunk = dtype == DCU_BF16 ? 8 : 4;
+  if (d % per_chunk != 0) return DCU_EUNSUPPORTED;
+  if (!dcu_aligned16(x_cur) || !dcu_aligned16(x_prev)) return DCU_EUNSUPPORTED;
+  if (B > 65535 || N > (int64_t(1) << 30)) return DCU_EUNSUPPORTED;
+  const int64_t chunks = d / per_chunk;
+  if (chunks > (int64_t(1) << 30)) return DCU_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = B * N;
+  const int64_t zb = (n + 255) / 256;
+  hipLaunchKernelGGL(dcu::k_zero_f32, dim3(unsigned(zb < 4096 ? zb : 4096)), dim3(256), 0, s, dist,
+                     n);
+  DCU_LAUNCH_CHECK();
+  const dim3 grid(unsigned((N + dcu::kRowsPerBlock - 1) / dcu::kRowsPerBlock), unsigned(B));
+  const uint4* xc = static_cast<const uint4*>(x_cur);
+  uint4* xp = static_cast<uint4*>(x_prev);
+  if (dtype == DCU_BF16)
+    hipLaunchKernelGGL(dcu::k_distance_rows<true>, grid, dim3(256), 0, s, xc, xp, int(N),
+                       int(chunks), sel_idx, sel_count, int(roll), dist);
+  else
+    hipLaunchKernelGGL(dcu::k_distance_rows<false>, grid, dim3(256), 0, s, xc, xp, int(N),
+                       int(chunks), sel_idx, sel_count, int(roll), dist);
+  DCU_LAUNCH_CHECK();
   return DCU_OK;
 }

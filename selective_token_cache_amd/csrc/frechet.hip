@@ -176,6 +176,25 @@ __global__ __launch_bounds__(kThreads) void k_frechet(const float* __restrict__ 
   for (int i = t; i < m; i += kThreads) ord[i] = i < mv ? int32_t(keys[i] & slot_mask) : -1;
 }
 
+// the positions of the first min(n_commit, P) committed slots of each sequence, -1 after them
+__global__ __launch_bounds__(256) void k_commit_positions(const int32_t* __restrict__ order,
+                                                          const int32_t* __restrict__ n_commit,
+                                                          const int32_t* __restrict__ slot_pos,
+                                                          int m, int P,
+                                                          int32_t* __restrict__ key_pos) {
+  const int b = blockIdx.x;
+  int n = n_commit[b];
+  n = n < 0 ? 0 : (n > m ? m : n);
+  for (int k = threadIdx.x; k < P; k += blockDim.x) {
+    int32_t pos = -1;
+    if (k < n) {
+      const int slot = order[int64_t(b) * m + k];
+      if (slot >= 0 && slot < m) pos = slot_pos[int64_t(b) * m + slot];
+    }
+    key_pos[int64_t(b) * P + k] = pos;
+  }
+}
+
 }  // namespace
 }  // namespace dcu
 
@@ -208,4 +227,16 @@ extern "C" int frechet_commit(const float* conf, const int32_t* m_valid, int32_t
   if (!(delta >= 0.0)) return DCU_EINVAL;  // also rejects NaN
   return dllm_commit(conf, m_valid, B, m, DCU_COMMIT_FRECHET, delta, nullptr, n_commit, order,
                      stream);
+}
+
+extern "C" int dllm_commit_positions(const int32_t* order, const int32_t* n_commit,
+                                     const int32_t* slot_pos, int32_t B, int32_t m, int32_t P,
+                                     int32_t* key_pos, void* stream) {
+  if (!order || !n_commit || !slot_pos || !key_pos || B <= 0 || m <= 0 || P <= 0)
+    return DCU_EINVAL;
+  hipLaunchKernelGGL(dcu::k_commit_positions, dim3(unsigned(B)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), order, n_commit, slot_pos, int(m), int(P),
+                     key_pos);
+  DCU_LAUNCH_CHECK();
+  return DCU_OK;
 }

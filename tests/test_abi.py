@@ -64,6 +64,16 @@ def test_distance_validation():
     assert L.dcu_distance(odd, FAKE, 1, 1, 1, 8, FAKE, None, None) == _lib.EUNSUPPORTED
 
 
+def test_distance_rows_validation():
+    L = stc.load()
+    assert L.dcu_distance_rows(None, FAKE, 1, 1, 4, 8, FAKE, FAKE, FAKE, 1, None) == _lib.EINVAL
+    assert L.dcu_distance_rows(FAKE, FAKE, 1, 1, 4, 8, None, FAKE, FAKE, 1, None) == _lib.EINVAL
+    assert L.dcu_distance_rows(FAKE, FAKE, 7, 1, 4, 8, FAKE, FAKE, FAKE, 1, None) == _lib.EINVAL
+    assert L.dcu_distance_rows(FAKE, FAKE, 1, 0, 4, 8, FAKE, FAKE, FAKE, 1, None) == _lib.EINVAL
+    assert L.dcu_distance_rows(FAKE, FAKE, 1, 1, 4, 12, FAKE, FAKE, FAKE, 1, None) == _lib.EUNSUPPORTED
+    assert L.dcu_distance_rows(FAKE, FAKE, 1, 70000, 4, 8, FAKE, FAKE, FAKE, 1, None) == _lib.EUNSUPPORTED
+
+
 def test_select_validation():
     L = stc.load()
     args = dict(dist=FAKE, budgets=FAKE, L=4, layer=0, key_pos=FAKE, P=1, B=2, N=64, bw=8,
@@ -169,3 +179,10 @@ def test_layer_validation():
     # workspace smaller than the query says
     assert L.dcu_selective_layer(ctypes.byref(_desc()), FAKE, None, None, 2, 64, 0, FAKE, FAKE, FAKE,
                                  FAKE, 16, None) == _lib.EWORKSPACE
+
+
+def test_commit_positions_validation():
+    L = stc.load()
+    assert L.dllm_commit_positions(None, FAKE, FAKE, 2, 16, 4, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit_positions(FAKE, FAKE, FAKE, 2, 16, 0, FAKE, None) == _lib.EINVAL
+    assert L.dllm_commit_positions(FAKE, FAKE, None, 2, 16, 4, FAKE, None) == _lib.EINVAL

@@ -393,3 +393,46 @@ def test_commit_per_position_thresholds(m):
         rn, ro = oapd.unmask(conf, tau, mvalid)
         assert np.array_equal(n.cpu().numpy(), rn)
         assert np.array_equal(order.cpu().numpy(), ro)
+
+
+# ----------------------------------------------------------------------------- closed loop (f1)
+@pytest.mark.parametrize("bf16", [True, False])
+def test_distance_rows_equals_full_distance_and_rolls(bf16):
+    """Only listed rows differ between x_cur and x_prev: dcu_distance_rows gives dcu_distance's
+    result bit for bit, and the roll leaves x_prev equal to x_cur."""
+    g = synth.rng(970, int(bf16))
+    B, N, d = 3, 300, 256
+    prev = g.standard_normal((B, N, d)).astype(np.float32)
+    cur = prev.copy()
+    sel = np.full((B, N), -1, np.int32)
+    cnt = np.array([40, 0, 300], np.int32)
+    for b in range(B):
+        rows = np.sort(g.choice(N, cnt[b], replace=False))
+        sel[b, :cnt[b]] = rows
+        changed = rows[: cnt[b] * 3 // 4]                       # a listed row may also be unchanged
+        cur[b, changed] += g.normal(0, 0.05, (len(changed), d)).astype(np.float32)
+    to_dev = (lambda a: dev_bf16(synth.f32_to_bf16(a))) if bf16 else dev
+    xc, xp = to_dev(cur), to_dev(prev)
+    full, _ = stc.dcu_distance(xc, xp, want_mean=False)
+    xp2 = xp.clone()
+    got = stc.dcu_distance_rows(xc, xp2, dev(sel), dev(cnt), roll=True)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), full.cpu().numpy().view(np.uint32))
+    assert torch.equal(xp2.view(torch.uint8) if bf16 else xp2, xc.view(torch.uint8) if bf16 else xc)
+    assert float(got[1].abs().sum()) == 0.0
+
+
+def test_commit_positions():
+    g = synth.rng(971, 0)
+    B, m, P = 4, 32, 4
+    conf = g.uniform(0, 1, (B, m)).astype(np.float32)
+    n, order = stc.frechet_commit(dev(conf), 0.0)
+    n_h = n.cpu().numpy()
+    n_h[2] = 0
+    n_h[3] = 9
+    slot_pos = (512 + g.permutation(m * B).reshape(B, m)).astype(np.int32)
+    keys = stc.dllm_commit_positions(order, dev(n_h), dev(slot_pos), P).cpu().numpy()
+    o = order.cpu().numpy()
+    for b in range(B):
+        k = min(int(n_h[b]), P)
+        want = [int(slot_pos[b, o[b, j]]) for j in range(k)] + [-1] * (P - k)
+        assert keys[b].tolist() == want
