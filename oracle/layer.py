@@ -8,8 +8,13 @@ a SwiGLU feed-forward block.
 
 The pages do not fix the layer internals. Reading used here ("parity unpinned"
 by the pages, pinned by the tests as an implementation of this reading):
-* pre-norm residual block with RMSNorm (gain vectors, eps given), no rotary embedding, no attention
-  mask, softmax scale 1/sqrt(head_dim);
+* pre-norm residual block with RMSNorm (gain vectors, eps given), no attention mask, softmax scale
+  1/sqrt(head_dim);
+* rotary position embedding optional (rope_theta > 0; 0 = none, the default): the RoFormer rotation
+  in the rotate-half pairing used by LLaMA-family models such as LLaDA, applied to every head's q
+  and k (not v) with the token's position in its sequence (its row index, 0 .. N-1). Head dim i and
+  i + dh/2 (i < dh/2) form a pair rotated by the angle pos * theta^(-2i/dh). The pages say nothing
+  about positions; this is the standard form of the model family they evaluate;
 * weights stored [out, in]; w_qkv rows are Wq | Wk | Wv; heads are contiguous head_dim slices;
 * cached K/V rows of the selected tokens are overwritten before attention, so the selected queries
   see each other's new keys and values;
@@ -47,10 +52,25 @@ def softmax_rows(s: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary embedding of head vectors x [..., dh] at positions pos (broadcast against x[..., 0]):
+    with h = dh/2 and angle a_i = pos * theta^(-2i/dh), the pair (x_i, x_{i+h}) becomes
+    (x_i cos a_i - x_{i+h} sin a_i, x_{i+h} cos a_i + x_i sin a_i). fp64."""
+    dh = x.shape[-1]
+    h = dh // 2
+    inv_freq = float(theta) ** (-(2.0 * np.arange(h)) / dh)
+    ang = np.asarray(pos, np.float64)[..., None] * inv_freq
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
 def selective_layer_seq(w64: dict, n_heads: int, head_dim: int, eps: float, x: np.ndarray,
-                        rows: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, y: np.ndarray):
+                        rows: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, y: np.ndarray,
+                        rope_theta: float = 0.0):
     """One sequence. x [N, d] fp64 layer input; rows: ascending selected positions;
-    k_cache, v_cache [N, H, dh] fp64; y [N, d] fp64. Returns new (k_cache, v_cache, y) copies."""
+    k_cache, v_cache [N, H, dh] fp64; y [N, d] fp64. Returns new (k_cache, v_cache, y) copies.
+    rope_theta > 0 rotates q and k of each selected row by its position (its row index)."""
     N, d = x.shape
     H, dh = n_heads, head_dim
     kc = k_cache.copy()
@@ -63,7 +83,11 @@ def selective_layer_seq(w64: dict, n_heads: int, head_dim: int, eps: float, x: n
     xn = rmsnorm(xs, w64["g_attn"], eps)
     qkv = xn @ w64["w_qkv"].T                         # [M, 3d]
     q = qkv[:, :d].reshape(-1, H, dh)
-    kc[rows] = qkv[:, d:2 * d].reshape(-1, H, dh)     # K/V scatter into the cache
+    k = qkv[:, d:2 * d].reshape(-1, H, dh)
+    if rope_theta > 0:
+        q = rope(q, rows[:, None], rope_theta)
+        k = rope(k, rows[:, None], rope_theta)
+    kc[rows] = k                                      # K/V scatter into the cache
     vc[rows] = qkv[:, 2 * d:].reshape(-1, H, dh)
     o = np.empty((len(rows), H, dh))
     scale = 1.0 / np.sqrt(dh)
@@ -79,7 +103,8 @@ def selective_layer_seq(w64: dict, n_heads: int, head_dim: int, eps: float, x: n
 
 def selective_layer(w: dict, n_heads: int, head_dim: int, eps: float, x_in: np.ndarray,
                     sel_idx: np.ndarray | None, sel_count: np.ndarray | None,
-                    k_cache: np.ndarray, v_cache: np.ndarray, y: np.ndarray):
+                    k_cache: np.ndarray, v_cache: np.ndarray, y: np.ndarray,
+                    rope_theta: float = 0.0):
     """Batched form matching the library call. x_in [B, N, d]; sel_idx [B, N] (first sel_count[b]
     valid) or None for every row (dense mode); caches [B, N, H, dh]; y [B, N, d].
     Returns fp64 (k_cache, v_cache, y)."""
@@ -92,7 +117,7 @@ def selective_layer(w: dict, n_heads: int, head_dim: int, eps: float, x_in: np.n
     for b in range(B):
         rows = np.arange(N) if sel_idx is None else np.asarray(sel_idx[b, :int(sel_count[b])])
         kc[b], vc[b], yo[b] = selective_layer_seq(w64, n_heads, head_dim, eps, x[b], rows,
-                                                  kc[b], vc[b], yo[b])
+                                                  kc[b], vc[b], yo[b], rope_theta)
     return kc, vc, yo
 
 

@@ -21,8 +21,9 @@ def _weights(seed, shape=S, std=0.3):
     return synth.layer_weights(synth.rng(400, seed), shape, std=std, bf16=False, gain_jitter=0.5)
 
 
-def _loops_dense(w, x, shape):
-    """Independent dense layer written with explicit Python loops (tiny shapes only)."""
+def _loops_dense(w, x, shape, theta=0.0):
+    """Independent dense layer written with explicit Python loops (tiny shapes only); theta > 0
+    turns each head's (i, i + dh/2) pair of q and k at row p by p * theta^(-2i/dh) radians."""
     N, d = len(x), shape.d
     H, dh, F = shape.n_heads, shape.head_dim, shape.ffn
 
@@ -35,6 +36,14 @@ def _loops_dense(w, x, shape):
 
     xn = [rms([float(t) for t in x[i]], w["g_attn"]) for i in range(N)]
     qkv = [mv(w["w_qkv"], xn[i], 3 * d, d) for i in range(N)]
+    if theta > 0:
+        for p in range(N):
+            for base in [h * dh for h in range(2 * H)]:           # the Q heads, then the K heads
+                for i in range(dh // 2):
+                    ang = p * theta ** (-2.0 * i / dh)
+                    a, b = qkv[p][base + i], qkv[p][base + i + dh // 2]
+                    qkv[p][base + i] = a * math.cos(ang) - b * math.sin(ang)
+                    qkv[p][base + i + dh // 2] = b * math.cos(ang) + a * math.sin(ang)
     out_k = [[qkv[i][d + j] for j in range(d)] for i in range(N)]
     out_v = [[qkv[i][2 * d + j] for j in range(d)] for i in range(N)]
     ys = []
@@ -60,20 +69,21 @@ def _loops_dense(w, x, shape):
     return np.array(out_k), np.array(out_v), np.array(ys)
 
 
-def _run(w, x, rows, kc=None, vc=None, y=None, shape=S):
+def _run(w, x, rows, kc=None, vc=None, y=None, shape=S, theta=0.0):
     N = len(x)
     kc = np.zeros((N, shape.n_heads, shape.head_dim)) if kc is None else kc
     vc = np.zeros_like(kc) if vc is None else vc
     y = np.zeros((N, shape.d)) if y is None else y
     return ol.selective_layer_seq(ol.weights64(w), shape.n_heads, shape.head_dim, shape.eps,
-                                  np.asarray(x, np.float64), rows, kc, vc, y)
+                                  np.asarray(x, np.float64), rows, kc, vc, y, theta)
 
 
-def test_full_selection_matches_independent_python_loops():
+@pytest.mark.parametrize("theta", [0.0, 10.0])
+def test_full_selection_matches_independent_python_loops(theta):
     w = _weights(0)
     x = synth.rng(400, 1).standard_normal((5, S.d))
-    k, v, y = _run(w, x, np.arange(5))
-    rk, rv, ry = _loops_dense(w, x, S)
+    k, v, y = _run(w, x, np.arange(5), theta=theta)
+    rk, rv, ry = _loops_dense(w, x, S, theta)
     np.testing.assert_allclose(k.reshape(5, -1), rk, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(v.reshape(5, -1), rv, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(y, ry, rtol=1e-12, atol=1e-12)
@@ -124,17 +134,19 @@ def test_unselected_rows_are_bitwise_untouched():
     assert not np.allclose(y2[rows], y[rows])
 
 
-def test_selected_rows_equal_dense_when_all_changed_rows_are_selected():
+@pytest.mark.parametrize("theta", [0.0, 100.0])
+def test_selected_rows_equal_dense_when_all_changed_rows_are_selected(theta):
+    """With RoPE this also fixes the position of a selected row: its row index, not its slot."""
     w = _weights(8)
     g = synth.rng(400, 9)
     x_prev = g.standard_normal((10, S.d))
-    k0, v0, y0 = _run(w, x_prev, np.arange(10))            # dense fill on the cached inputs
+    k0, v0, y0 = _run(w, x_prev, np.arange(10), theta=theta)   # dense fill on the cached inputs
     x_cur = x_prev.copy()
     changed = np.array([2, 7])
     x_cur[changed] += 0.5 * g.standard_normal((2, S.d))
     rows = np.array([0, 2, 5, 7])                           # a superset of the changed rows
-    k1, v1, y1 = _run(w, x_cur, rows, k0, v0, y0)
-    kd, vd, yd = _run(w, x_cur, np.arange(10))              # dense on the current inputs
+    k1, v1, y1 = _run(w, x_cur, rows, k0, v0, y0, theta=theta)
+    kd, vd, yd = _run(w, x_cur, np.arange(10), theta=theta)    # dense on the current inputs
     np.testing.assert_allclose(y1[rows], yd[rows], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(k1, kd, rtol=1e-12, atol=1e-12)
 
@@ -195,3 +207,61 @@ def test_v_features_closed_form():
     assert np.allclose(np.mean(v * v, axis=-1), 1.0, rtol=1e-12)
     ratio = v / x
     assert np.allclose(ratio, ratio[..., :1], rtol=1e-12)
+
+
+# --- rotary position embedding (RoFormer's rotation; rotate-half pairing of LLaMA-family models)
+
+def test_rope_position_zero_is_the_identity():
+    x = synth.rng(400, 20).standard_normal((3, 16))
+    assert np.array_equal(ol.rope(x, np.zeros(3), 10000.0), x)
+
+
+def test_rope_two_dims_is_a_plane_rotation_by_the_position():
+    """dh = 2: the only frequency is theta^0 = 1, so (a, b) turns by pos radians whatever theta:
+    the complex product (a + ib) e^{i pos}."""
+    g = synth.rng(400, 21)
+    x = g.standard_normal((7, 2))
+    pos = np.arange(7) * 3.0
+    for theta in (10.0, 5e5):
+        z = (x[:, 0] + 1j * x[:, 1]) * np.exp(1j * pos)
+        np.testing.assert_allclose(ol.rope(x, pos, theta), np.stack([z.real, z.imag], 1),
+                                   rtol=1e-13, atol=1e-13)
+
+
+def test_rope_frequencies_and_pairing_on_unit_vectors():
+    """dh = 4, theta = 10000: frequencies 1 and 10000^(-1/2) = 0.01; e_1 at position p lands on
+    cos(0.01 p) e_1 + sin(0.01 p) e_3 (dims 1 and 3 are a pair), e_0 on cos p e_0 + sin p e_2."""
+    p = 37.0
+    e = np.eye(4)
+    r = ol.rope(e, np.full(4, p), 10000.0)
+    np.testing.assert_allclose(r[0], [math.cos(p), 0, math.sin(p), 0], atol=1e-14)
+    np.testing.assert_allclose(r[1], [0, math.cos(0.01 * p), 0, math.sin(0.01 * p)], atol=1e-14)
+    np.testing.assert_allclose(r[2], [-math.sin(p), 0, math.cos(p), 0], atol=1e-14)
+    np.testing.assert_allclose(r[3], [0, -math.sin(0.01 * p), 0, math.cos(0.01 * p)], atol=1e-14)
+
+
+def test_rope_keeps_norms_and_scores_depend_on_the_offset_only():
+    """A rotation keeps every pair's length, and <R(m) q, R(n) k> is a function of m - n."""
+    g = synth.rng(400, 22)
+    q, k = g.standard_normal((2, 128))
+    theta = 5e5
+    rq = ol.rope(q[None], np.array([5.0]), theta)[0]
+    np.testing.assert_allclose(np.hypot(rq[:64], rq[64:]), np.hypot(q[:64], q[64:]), rtol=1e-13)
+    def score(m, n):
+        return ol.rope(q[None], np.array([m]), theta)[0] @ ol.rope(k[None], np.array([n]), theta)[0]
+    for m, n, s in [(3.0, 10.0, 1000.0), (900.0, 17.0, 2500.0)]:
+        np.testing.assert_allclose(score(m + s, n + s), score(m, n), rtol=1e-9, atol=1e-10)
+    assert abs(score(3.0, 10.0) - score(10.0, 3.0)) > 1e-6     # not symmetric: order matters
+
+
+def test_rope_layer_rotates_cached_keys_by_row_position_and_leaves_values():
+    w = _weights(30)
+    g = synth.rng(400, 31)
+    x = g.standard_normal((9, S.d))
+    rows = np.array([1, 6, 8])
+    k0, v0, _ = _run(w, x, rows)
+    k1, v1, _ = _run(w, x, rows, theta=50.0)
+    assert np.array_equal(v1, v0)
+    np.testing.assert_allclose(k1[rows], ol.rope(k0[rows], rows[:, None].astype(float), 50.0),
+                               rtol=1e-13, atol=1e-14)
+    assert not np.allclose(k1[rows[1:]], k0[rows[1:]])
