@@ -45,6 +45,7 @@ D, H, DH, F = 4096, 32, 128, 12288
 V, M_CAND = 126464, 256
 B_WINDOW, DELTA = 32, 0.1
 APD_ALPHA, APD_BETA = 0.1, 0.1
+ROPE_THETA = 500000.0           # rotary base of the LLaDA-8B configuration
 
 # name -> shape of the run; sigma(l) is the drift of layer l's inputs
 WORKLOADS = {
@@ -205,6 +206,17 @@ def torch_dense_layer(w, x, eps):
 
     qkv = Fn.linear(rms(x2, w["g_attn"]), w["w_qkv"])
     q, k, v = (t.reshape(Bsz, Nseq, H, DH).transpose(1, 2).contiguous() for t in qkv.split(d, dim=1))
+    # rotary embedding of q and k (pairs i, i + DH/2), angles in fp32
+    half = DH // 2
+    inv = ROPE_THETA ** (-torch.arange(half, device=x.device, dtype=torch.float64) * 2 / DH)
+    ang = (torch.arange(Nseq, device=x.device, dtype=torch.float64)[:, None] * inv).float()
+    cs, sn = torch.cos(ang), torch.sin(ang)
+
+    def rot(t):
+        t1, t2 = t[..., :half].float(), t[..., half:].float()
+        return torch.cat([t1 * cs - t2 * sn, t2 * cs + t1 * sn], dim=-1).to(torch.bfloat16)
+
+    q, k = rot(q), rot(k)
     s = torch.matmul(q, k.transpose(-1, -2).contiguous()).float() * (1.0 / DH ** 0.5)
     p = torch.softmax(s, dim=-1).to(torch.bfloat16)
     o = torch.matmul(p, v).transpose(1, 2).reshape(Bsz * Nseq, d)
@@ -261,7 +273,8 @@ def main():
             # the layer keeps its own blocked copy; row-major weights stay only for layer 0
             # (the PyTorch dense reference)
             layers.append((stc.Layer(D, H, DH, F, 1e-5, w["w_qkv"], w["w_o"], w["w_gate"], w["w_up"],
-                                     w["w_down"], w["g_attn"], w["g_ffn"]), w if l == 0 else None))
+                                     w["w_down"], w["g_attn"], w["g_ffn"], rope_theta=ROPE_THETA),
+                           w if l == 0 else None))
             del w
             kc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
             vc.append(torch.empty((B, N, H, DH), dtype=torch.bfloat16, device=dev))
@@ -700,7 +713,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "batch": B, "seq_len": N, "layers": L_, "d": D, "heads": H,
-                   "head_dim": DH, "ffn": F, "vocab": V if wl["end"] else None, "b_layer": B_LAYER,
+                   "head_dim": DH, "ffn": F, "rope_theta": ROPE_THETA if wl["layers"] else None, "vocab": V if wl["end"] else None, "b_layer": B_LAYER,
                    "b_window": B_WINDOW, "max_rows": max_rows if wl["layers"] else None,
                    "keys_per_seq": N_KEYS, "drift_rows": 0.3,
                    "parallelism": "single GPU"},
@@ -758,7 +771,7 @@ def cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, log
         d, _ = odist.distance_and_mean(xc, xp)
         sel, cnt = osel.select(d, bud, l, kp, B_WINDOW)
         if lay is not None:
-            olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, *lay)
+            olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, *lay, ROPE_THETA)
     t_layer = (time.perf_counter() - t0) / len(sample_layers)
     t_end = 0.0
     if wl["end"]:

@@ -16,7 +16,7 @@
  *   dllm_commit          the same with the factor, threshold or per-position threshold rule
  *   dllm_apd             adaptive-parallel-decoding signals and per-position thresholds
  *   dllm_commit_positions  committed positions -> the next step's key positions
- *   dcu_pack_weights, dcu_pack_gate_up   the projections' blocked weight layout (set-up, not a step)
+ *   dcu_pack_weights, dcu_pack_gate_up, dcu_pack_qkv   the projections' blocked weight layout (set-up)
  *
  * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
  * Acceleration of Diffusion LLM" (reading notes), Key designs 1-2; "Fast-dLLM++: Frechet Profile
@@ -171,9 +171,27 @@ int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void* out, void*
 int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d, void* out,
                      void* stream);
 
-/* dcu_layer.weight_layout: the only layout the layer accepts (matrices from dcu_pack_weights and
- * dcu_pack_gate_up) */
+/*
+ * dcu_pack_qkv -- W_qkv in the blocked layout for a layer with rotary position embedding.
+ * (A data layout of this library, as dcu_pack_weights. Rotary embedding is not part of the
+ * Dynamic-dLLM notes; it belongs to the LLaMA-family models, LLaDA among them, that the notes'
+ * diffusion LLMs are built on, and turns each pair (i, i + head_dim/2) of a head's q and k.)
+ * w_qkv  [3d, d] bf16 row-major, rows Wq | Wk | Wv. Not modified.
+ * out    3 * d * d bf16, caller-owned, must not overlap w_qkv: the blocked layout of
+ *        dcu_pack_weights applied to the matrix whose Q and K rows are reordered inside every head
+ *        (head dim j < head_dim/2 at head row 2j, j >= head_dim/2 at head row 2(j - head_dim/2) + 1),
+ *        so that the two dims of a rotation pair are adjacent outputs; the V rows keep their order.
+ * Errors: EINVAL on NULL pointers, d or head_dim <= 0, d % head_dim != 0; EUNSUPPORTED if
+ *         head_dim not in {32, 64, 128}, d % 64 != 0, 3 * d * d >= 2^40, or a pointer not 16-byte
+ *         aligned.
+ */
+int dcu_pack_qkv(const void* w_qkv, int32_t d, int32_t head_dim, void* out, void* stream);
+
+/* dcu_layer.weight_layout: the layouts the layer accepts. BLOCKED: all matrices from
+ * dcu_pack_weights / dcu_pack_gate_up, no rotary embedding (rope_theta must be 0). BLOCKED_ROPE:
+ * W_qkv from dcu_pack_qkv, the rest as BLOCKED, rotary embedding with base rope_theta (> 0). */
 #define DCU_WEIGHTS_BLOCKED 1
+#define DCU_WEIGHTS_BLOCKED_ROPE 2
 
 /*
  * One pre-norm transformer layer (bf16 weights; W[out, in] below means the [out, in] matrix
@@ -181,6 +199,10 @@ int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d,
  *   xn = RMSNorm(x; g_attn), [q|k|v] = xn W_qkv^T, o = softmax(q K^T / sqrt(head_dim)) V per head
  *   over all N cached rows (no mask), a = x + o W_o^T, an = RMSNorm(a; g_ffn),
  *   y = a + (silu(an W_gate^T) * (an W_up^T)) W_down^T.
+ * With DCU_WEIGHTS_BLOCKED_ROPE, q and k of a row at position p (its index in the sequence) are
+ * rotated before k is cached and attention runs: in every head, dims i and i + head_dim/2 turn by
+ * p * rope_theta^(-2i/head_dim) radians (x_i cos - x_{i+h} sin, x_{i+h} cos + x_i sin). The cache
+ * holds rotated keys in the standard [head, dim] order.
  */
 typedef struct {
   int32_t d;          /* model width, = n_heads * head_dim          */
@@ -194,7 +216,8 @@ typedef struct {
   const void* w_down; /* bf16 [d, F] blocked                          */
   const void* g_attn; /* bf16 [d] RMSNorm gain before attention       */
   const void* g_ffn;  /* bf16 [d] RMSNorm gain before the FFN         */
-  int32_t weight_layout; /* must be DCU_WEIGHTS_BLOCKED                */
+  int32_t weight_layout; /* DCU_WEIGHTS_BLOCKED or DCU_WEIGHTS_BLOCKED_ROPE */
+  float rope_theta;   /* rotary base (BLOCKED_ROPE), 0 with BLOCKED     */
 } dcu_layer;
 
 /* Workspace bytes dcu_selective_layer needs for these shapes (max_rows <= 0 means B*N). */
@@ -220,8 +243,9 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  *           split-K partial tiles of one call.
  * Results are bitwise reproducible for a given device: every reduction runs in a fixed order.
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
- *         d != n_heads*head_dim, rms_eps < 0; EUNSUPPORTED if weight_layout is not
- *         DCU_WEIGHTS_BLOCKED, head_dim not in {32, 64, 128}, d or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte
+ *         d != n_heads*head_dim, rms_eps < 0, rope_theta not 0 with DCU_WEIGHTS_BLOCKED or not
+ *         positive and finite with DCU_WEIGHTS_BLOCKED_ROPE; EUNSUPPORTED if weight_layout is
+ *         neither, head_dim not in {32, 64, 128}, d or ffn not a multiple of 64, N > 65536, B > 4096, B*N > 2^28, or a pointer not 16-byte
  *         aligned;
  *         EWORKSPACE if the workspace is too small or not 256-byte aligned.
  */

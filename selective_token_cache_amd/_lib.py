@@ -33,10 +33,12 @@ class LayerDesc(ctypes.Structure):
     """Mirror of dcu_layer in include/dcu.h."""
     _fields_ = [("d", _i32), ("n_heads", _i32), ("head_dim", _i32), ("ffn", _i32),
                 ("rms_eps", ctypes.c_float), ("w_qkv", _vp), ("w_o", _vp), ("w_gate_up", _vp),
-                ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp), ("weight_layout", _i32)]
+                ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp), ("weight_layout", _i32),
+                ("rope_theta", ctypes.c_float)]
 
 
-WEIGHTS_BLOCKED = 1  # DCU_WEIGHTS_BLOCKED
+WEIGHTS_BLOCKED = 1       # DCU_WEIGHTS_BLOCKED
+WEIGHTS_BLOCKED_ROPE = 2  # DCU_WEIGHTS_BLOCKED_ROPE
 
 
 _lib = None
@@ -52,6 +54,7 @@ EXPORTS = {
                                   _vp, _vp]),
     "dcu_pack_weights": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "dcu_pack_gate_up": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "dcu_pack_qkv": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp]),
     "dcu_selective_layer_workspace": (ctypes.c_size_t,
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
@@ -237,25 +240,44 @@ def dcu_pack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, out: torch.Tensor
     return out
 
 
+def dcu_pack_qkv(w_qkv: torch.Tensor, head_dim: int, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """The blocked [3d, d] W_qkv of a layer with rotary embedding (Q and K rows pair-interleaved
+    inside each head, see include/dcu.h)."""
+    _need(w_qkv, "w_qkv", torch.bfloat16)
+    if w_qkv.dim() != 2 or w_qkv.shape[0] != 3 * w_qkv.shape[1]:
+        raise ValueError("w_qkv must be a [3d, d] matrix")
+    if out is None:
+        out = torch.empty_like(w_qkv)
+    _need(out, "out", torch.bfloat16, tuple(w_qkv.shape))
+    _check("dcu_pack_qkv", load().dcu_pack_qkv(_p(w_qkv), w_qkv.shape[1], head_dim, _p(out),
+                                               _stream(stream)))
+    return out
+
+
 class Layer:
     """Holds the device weights of one layer and the matching dcu_layer descriptor. The five
     projection matrices are given row-major ([out, in]) and copied once into the library's blocked
-    layout (dcu_pack_weights; gate and up fused by dcu_pack_gate_up; on the current stream); the
-    caller's tensors are not kept."""
+    layout (dcu_pack_weights, or dcu_pack_qkv for W_qkv when rope_theta > 0; gate and up fused by
+    dcu_pack_gate_up; on the current stream); the caller's tensors are not kept. rope_theta > 0
+    turns on rotary position embedding with that base."""
 
     def __init__(self, d, n_heads, head_dim, ffn, eps, w_qkv, w_o, w_gate, w_up, w_down, g_attn,
-                 g_ffn):
+                 g_ffn, rope_theta: float = 0.0):
         for name, t, shape in [("w_qkv", w_qkv, (3 * d, d)), ("w_o", w_o, (d, d)),
                                ("w_gate", w_gate, (ffn, d)), ("w_up", w_up, (ffn, d)),
                                ("w_down", w_down, (d, ffn)), ("g_attn", g_attn, (d,)),
                                ("g_ffn", g_ffn, (d,))]:
             _need(t, name, torch.bfloat16, shape)
-        packed = [dcu_pack_weights(w_qkv), dcu_pack_weights(w_o), dcu_pack_gate_up(w_gate, w_up),
+        rope = float(rope_theta) > 0
+        qkv = dcu_pack_qkv(w_qkv, head_dim) if rope else dcu_pack_weights(w_qkv)
+        packed = [qkv, dcu_pack_weights(w_o), dcu_pack_gate_up(w_gate, w_up),
                   dcu_pack_weights(w_down)]
         self.tensors = (*packed, g_attn, g_ffn)
         self.d, self.n_heads, self.head_dim, self.ffn, self.eps = d, n_heads, head_dim, ffn, eps
+        self.rope_theta = float(rope_theta)
         self.desc = LayerDesc(d, n_heads, head_dim, ffn, float(eps), *[_p(t) for t in self.tensors],
-                              WEIGHTS_BLOCKED)
+                              WEIGHTS_BLOCKED_ROPE if rope else WEIGHTS_BLOCKED, self.rope_theta)
 
     def workspace_bytes(self, B: int, N: int, max_rows: int = 0) -> int:
         return int(load().dcu_selective_layer_workspace(ctypes.byref(self.desc), B, N, max_rows))

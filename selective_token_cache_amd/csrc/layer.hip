@@ -251,7 +251,38 @@ struct GemmArgs {
   uint16_t* h;          // SWIGLU: out [M, F]
   uint16_t* y;          // DOWN: scatter target; VPROJ: V rows out (via the row map)
   float* part;          // split tail partial tiles [2 * grid, BM * BN] fp32
+  int N;                // QKV: sequence length (a row's position is its global row mod N)
+  int rope_dh;          // QKV: head_dim with rotary embedding (W_qkv from dcu_pack_qkv), else 0
+  float rope_l2t;       // QKV: log2(theta) of the rotary embedding
 };
+
+// QKV output columns n .. n+3 of compacted row m (global row grow; n a multiple of 4): Q to the q
+// rows, K and V to the caches. With rotary embedding, W_qkv was packed by dcu_pack_qkv: inside every
+// Q and K head, packed column 2i holds head dim i and 2i+1 holds head dim i + dh/2, so the four
+// values are the rotation pairs (i, i + dh/2) and (i+1, i+1 + dh/2). Each pair turns by
+// pos * theta^(-2i/dh) and both land back on their own head dims (standard cache layout).
+__device__ __forceinline__ void store_qkv(const GemmArgs& g, int m, int64_t grow, int n, float w0,
+                                          float w1, float w2, float w3) {
+  const int part = n / g.d, col = n - part * g.d;
+  uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
+  if (g.rope_dh == 0 || part == 2) {
+    uint2 st;
+    st.x = pack_bf2(w0, w1);
+    st.y = pack_bf2(w2, w3);
+    *reinterpret_cast<uint2*>(dst + col) = st;
+    return;
+  }
+  const int dh = g.rope_dh, c = col & (dh - 1), i = c >> 1;
+  const float pos = float(grow % g.N);
+  const float step = g.rope_l2t / float(dh);
+  float s0, c0, s1, c1;
+  sincosf(pos * exp2f(-float(2 * i) * step), &s0, &c0);
+  sincosf(pos * exp2f(-float(2 * i + 2) * step), &s1, &c1);
+  uint16_t* head = dst + (col - c);
+  *reinterpret_cast<uint32_t*>(head + i) = pack_bf2(w0 * c0 - w1 * s0, w2 * c1 - w3 * s1);
+  *reinterpret_cast<uint32_t*>(head + i + (dh >> 1)) =
+      pack_bf2(w1 * c0 + w0 * s0, w3 * c1 + w2 * s1);
+}
 
 // Tail splitting: with a persistent grid of G workgroup slots and T output tiles, the last round holds
 // T mod G tiles and leaves the other slots idle. Those tail tiles (all tiles when T < G) are cut
@@ -386,12 +417,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         if (n >= g.Nout) continue;
         const gemm::f32x4 v = acc[fm][fn];
         if constexpr (EPI == EPI_QKV) {
-          uint2 st;
-          st.x = pack_bf2(v[0], v[1]);
-          st.y = pack_bf2(v[2], v[3]);
-          const int part = n / g.d, col = n - part * g.d;
-          uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
-          *reinterpret_cast<uint2*>(dst + col) = st;
+          store_qkv(g, m, grow, n, v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           float4 o;
@@ -597,12 +623,7 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
         const int n = n_t * C::BN + c4;
         const int64_t grow = int64_t(g.rowmap[m]);
         if constexpr (EPI == EPI_QKV) {
-          uint2 st;
-          st.x = pack_bf2(w.x, w.y);
-          st.y = pack_bf2(w.z, w.w);
-          const int part = n / g.d, col = n - part * g.d;
-          uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
-          *reinterpret_cast<uint2*>(dst + col) = st;
+          store_qkv(g, m, grow, n, w.x, w.y, w.z, w.w);
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
@@ -1044,7 +1065,13 @@ int validate(const dcu_layer* w, int B, int N) {
   if (!w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down || !w->g_attn || !w->g_ffn)
     return DCU_EINVAL;
   if (w->d <= 0 || w->n_heads <= 0 || w->head_dim <= 0 || w->ffn <= 0) return DCU_EINVAL;
-  if (w->weight_layout != DCU_WEIGHTS_BLOCKED) return DCU_EUNSUPPORTED;
+  if (w->weight_layout == DCU_WEIGHTS_BLOCKED) {
+    if (w->rope_theta != 0.0f) return DCU_EINVAL;
+  } else if (w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE) {
+    if (!(w->rope_theta > 0.0f) || w->rope_theta - w->rope_theta != 0.0f) return DCU_EINVAL;
+  } else {
+    return DCU_EUNSUPPORTED;
+  }
   if (int64_t(w->n_heads) * w->head_dim != w->d) return DCU_EINVAL;
   if (!(w->rms_eps >= 0.0f)) return DCU_EINVAL;
   if (w->head_dim != 32 && w->head_dim != 64 && w->head_dim != 128) return DCU_EUNSUPPORTED;
@@ -1085,10 +1112,13 @@ void launch_fixup(const GemmArgs& ga, hipStream_t s, int M_cap) {
 
 // Row-major [rows, cols] -> blocked layout (gemm.h): one 16-byte chunk per thread, reads coalesced
 // along the rows. With a second source b (the up matrix), the 16-row groups of a and b alternate
-// in the output (a's group g -> group 2g, b's group g -> group 2g + 1).
+// in the output (a's group g -> group 2g, b's group g -> group 2g + 1). With rope_rows > 0 (the Q
+// and K rows of W_qkv) the rows below rope_rows are reordered inside each head of dh rows: head dim
+// j < dh/2 becomes row 2j of the head, j >= dh/2 row 2(j - dh/2) + 1.
 __global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ a,
                                                       const u32x4* __restrict__ b, int64_t rows,
-                                                      int64_t cols, u32x4* __restrict__ out) {
+                                                      int64_t cols, int64_t rope_rows, int dh,
+                                                      u32x4* __restrict__ out) {
   const int64_t cpr = cols / 8;  // chunks per row
   const int64_t n = rows * cpr;  // chunks per source
   const int64_t kt_n = cols / 64;
@@ -1097,21 +1127,26 @@ __global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ 
        i += int64_t(gridDim.x) * blockDim.x) {
     const int m = i < n ? 0 : 1;
     const int64_t k = i - m * n;
-    const int64_t r = k / cpr, ch = k - r * cpr;
+    const int64_t r0 = k / cpr, ch = k - r0 * cpr;
+    int64_t r = r0;
+    if (r0 < rope_rows) {
+      const int64_t j = r0 % dh, h = dh / 2;
+      r = r0 - j + (j < h ? 2 * j : 2 * (j - h) + 1);
+    }
     const int64_t g = (r >> 4) * nsrc + m, kt = ch >> 3;
     const int rr = int(r & 15), c = int(ch & 7);
     out[(g * kt_n + kt) * 128 + c * 16 + rr] = (m ? b : a)[k];
   }
 }
 
-int launch_pack(const void* a, const void* b, int64_t rows, int64_t cols, void* out,
-                void* stream) {
+int launch_pack(const void* a, const void* b, int64_t rows, int64_t cols, int64_t rope_rows,
+                int dh, void* out, void* stream) {
   const int64_t chunks = rows * cols / 8 * (b ? 2 : 1);
   const int64_t want = (chunks + 255) / 256;
   const unsigned grid = unsigned(want < 8192 ? want : 8192);
   hipLaunchKernelGGL(k_pack_weights, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(a), static_cast<const u32x4*>(b), rows, cols,
-                     static_cast<u32x4*>(out));
+                     rope_rows, dh, static_cast<u32x4*>(out));
   DCU_LAUNCH_CHECK();
   return DCU_OK;
 }
@@ -1125,7 +1160,18 @@ extern "C" int dcu_pack_weights(const void* w, int32_t rows, int32_t cols, void*
   if (rows % 16 != 0 || cols % 64 != 0) return DCU_EUNSUPPORTED;
   if (int64_t(rows) * cols >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
   if (!dcu_aligned16(w) || !dcu_aligned16(out)) return DCU_EUNSUPPORTED;
-  return dcu::launch_pack(w, nullptr, rows, cols, out, stream);
+  return dcu::launch_pack(w, nullptr, rows, cols, 0, 1, out, stream);
+}
+
+extern "C" int dcu_pack_qkv(const void* w_qkv, int32_t d, int32_t head_dim, void* out,
+                            void* stream) {
+  if (!w_qkv || !out || d <= 0 || head_dim <= 0) return DCU_EINVAL;
+  if (d % head_dim != 0) return DCU_EINVAL;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return DCU_EUNSUPPORTED;
+  if (d % 64 != 0 || 3 * int64_t(d) * d >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
+  if (!dcu_aligned16(w_qkv) || !dcu_aligned16(out)) return DCU_EUNSUPPORTED;
+  return dcu::launch_pack(w_qkv, nullptr, 3 * int64_t(d), d, 2 * int64_t(d), head_dim, out,
+                          stream);
 }
 
 extern "C" int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d,
@@ -1135,7 +1181,7 @@ extern "C" int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F,
   if (2 * int64_t(F) * d >= (int64_t(1) << 40)) return DCU_EUNSUPPORTED;
   if (!dcu_aligned16(w_gate) || !dcu_aligned16(w_up) || !dcu_aligned16(out))
     return DCU_EUNSUPPORTED;
-  return dcu::launch_pack(w_gate, w_up, F, d, out, stream);
+  return dcu::launch_pack(w_gate, w_up, F, d, 0, 1, out, stream);
 }
 
 extern "C" size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N,
@@ -1219,6 +1265,11 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.q = P.q;
   ga.kc = static_cast<uint16_t*>(k_cache);
   ga.vc = static_cast<uint16_t*>(v_cache);
+  ga.N = N;
+  if (w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE) {
+    ga.rope_dh = w->head_dim;
+    ga.rope_l2t = float(log2(double(w->rope_theta)));
+  }
   launch_gemm<EPI_QKV>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;

@@ -151,11 +151,25 @@ def test_pack_gate_up_validation():
     assert L.dcu_pack_gate_up(FAKE, FAKE, 16, 32, FAKE, None) == _lib.EUNSUPPORTED   # d % 64
 
 
+def test_pack_qkv_validation():
+    L = stc.load()
+    assert L.dcu_pack_qkv(None, 256, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_qkv(FAKE, 256, 64, None, None) == _lib.EINVAL
+    assert L.dcu_pack_qkv(FAKE, 0, 64, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_qkv(FAKE, 256, 0, FAKE, None) == _lib.EINVAL
+    assert L.dcu_pack_qkv(FAKE, 320, 128, FAKE, None) == _lib.EINVAL          # d % head_dim
+    assert L.dcu_pack_qkv(FAKE, 192, 96, FAKE, None) == _lib.EUNSUPPORTED     # head_dim 96
+    assert L.dcu_pack_qkv(FAKE, 96, 32, FAKE, None) == _lib.EUNSUPPORTED      # d % 64
+    odd = ctypes.c_void_p(256 + 8)
+    assert L.dcu_pack_qkv(FAKE, 256, 64, odd, None) == _lib.EUNSUPPORTED
+
+
 def _desc(**kw):
-    a = dict(d=256, n_heads=4, head_dim=64, ffn=512, eps=1e-5, layout=_lib.WEIGHTS_BLOCKED)
+    a = dict(d=256, n_heads=4, head_dim=64, ffn=512, eps=1e-5, layout=_lib.WEIGHTS_BLOCKED,
+             theta=0.0)
     a.update(kw)
     return _lib.LayerDesc(a["d"], a["n_heads"], a["head_dim"], a["ffn"], a["eps"],
-                          *([FAKE] * 6), a["layout"])
+                          *([FAKE] * 6), a["layout"], a["theta"])
 
 
 def test_layer_validation():
@@ -173,6 +187,12 @@ def test_layer_validation():
     assert call(_desc(d=192, n_heads=2, head_dim=96)) == _lib.EUNSUPPORTED   # head_dim 96
     assert call(_desc(ffn=500)) == _lib.EUNSUPPORTED              # ffn % 64
     assert call(_desc(eps=-1.0)) == _lib.EINVAL
+    assert call(_desc(layout=3)) == _lib.EUNSUPPORTED
+    assert call(_desc(theta=1e4)) == _lib.EINVAL                   # rotary base without its layout
+    rope = _lib.WEIGHTS_BLOCKED_ROPE
+    assert ws(ctypes.byref(_desc(layout=rope, theta=5e5)), 2, 64, 0) > 0
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(_desc(layout=rope, theta=bad)) == _lib.EINVAL
     assert call(_desc(), B=0) == _lib.EINVAL
     assert call(_desc(), N=70000) == _lib.EUNSUPPORTED
     assert call(_desc(), sel=FAKE) == _lib.EINVAL                  # only one of sel_idx / sel_count

@@ -16,6 +16,7 @@ from tests.util import assert_rel, dev, dev_bf16, host_bf16, rel_l2
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
+THETA = 1e4  # rotary embedding on, as in the models the chain stands for
 
 
 def test_closed_loop_steps_against_the_oracle():
@@ -28,7 +29,8 @@ def test_closed_loop_steps_against_the_oracle():
     for w in ws_host:
         t = {k: dev_bf16(v) for k, v in w.items()}
         layers.append(stc.Layer(d, shape.n_heads, shape.head_dim, shape.ffn, shape.eps, t["w_qkv"],
-                                t["w_o"], t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"]))
+                                t["w_o"], t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"],
+                                rope_theta=THETA))
     # two alternating first-layer inputs that differ on a third of the rows
     a, bb, _ = synth.drift_pair(g, B * N, d, (B * N) // 3, 0.1)
     x0 = [dev_bf16(a.reshape(B, N, d)), dev_bf16(bb.reshape(B, N, d))]
@@ -79,7 +81,7 @@ def test_closed_loop_steps_against_the_oracle():
             k0, v0, y0 = host_bf16(kc[l]), host_bf16(vc[l]), host_bf16(y[l])
             stc.dcu_selective_layer(layers[l], X, sel[l], cnt[l], kc[l], vc[l], y[l], workspace=ws)
             rk, rv, ry = olayer.selective_layer(ws_host[l], shape.n_heads, shape.head_dim, shape.eps,
-                                                ref_in, rs, rc, k0, v0, y0)
+                                                ref_in, rs, rc, k0, v0, y0, THETA)
             gy = synth.bf16_to_f32(host_bf16(y[l]))
             for b in range(B):
                 r = rs[b, :rc[b]]

@@ -21,9 +21,9 @@ def _log(msg):
 
 
 class Case:
-    def __init__(self, shape, B, N, seed, std=0.02):
+    def __init__(self, shape, B, N, seed, std=0.02, theta=0.0):
         g = synth.rng(950, seed)
-        self.shape, self.B, self.N = shape, B, N
+        self.shape, self.B, self.N, self.theta = shape, B, N, theta
         self.w = synth.layer_weights(g, shape, std=std, gain_jitter=0.2)
         self.x = synth.normal_bf16(g, (B, N, shape.d))
         # a previous step's cache contents, scaled like projections of unit-RMS rows
@@ -38,7 +38,8 @@ class Case:
         t = {k: dev_bf16(v) for k, v in self.w.items()}
         self._t = t
         return stc.Layer(s.d, s.n_heads, s.head_dim, s.ffn, s.eps, t["w_qkv"], t["w_o"],
-                         t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"])
+                         t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"],
+                         rope_theta=self.theta)
 
     def run_gpu(self, sel, cnt, max_rows=0, reps=1):
         L = self.layer()
@@ -55,7 +56,7 @@ class Case:
     def run_oracle(self, sel, cnt):
         s = self.shape
         return olayer.selective_layer(self.w, s.n_heads, s.head_dim, s.eps, self.x, sel, cnt,
-                                      self.kc, self.vc, self.y)
+                                      self.kc, self.vc, self.y, self.theta)
 
 
 @pytest.mark.parametrize("rows,cols", [(16, 64), (48, 192), (3 * 4096, 4096)])
@@ -203,25 +204,27 @@ def test_full_size_single_sequence_64_rows():
     _compare(case, got64, ref, _rows(sel, cnt, 1, 1024))
 
 
-@pytest.mark.parametrize("counts,b", [
+@pytest.mark.parametrize("counts,b,theta", [
     # 1041 rows: 9 row tiles, the output and down projections (288 tiles) run one whole tile per CU
     # plus 32 tiles in 8 K-segments
-    ([150, 90, 200, 64, 128, 170, 99, 140], 2),
+    ([150, 90, 200, 64, 128, 170, 99, 140], 2, 0.0),
     # 1250 rows (320 tiles: 64 tiles in 4 segments) and 1400 rows (352 tiles: 96 in 2)
-    ([160, 170, 150, 180, 155, 140, 165, 130], 5),
-    ([180, 175, 170, 185, 176, 168, 172, 174], 7),
+    ([160, 170, 150, 180, 155, 140, 165, 130], 5, 0.0),
+    ([180, 175, 170, 185, 176, 168, 172, 174], 7, 0.0),
+    # rotary embedding with LLaDA's base, positions up to 1023
+    ([160, 170, 150, 180, 155, 140, 165, 130], 3, 5e5),
 ])
-def test_full_size_batched_sampled(counts, b):
+def test_full_size_batched_sampled(counts, b, theta):
     """Batch 8, N=1024, LLaDA-8B shapes, ~130-200 rows per sequence; the oracle recomputes one
     sequence completely (its rows depend only on that sequence's cache)."""
-    _log(f"layer full size batch 8, {sum(counts)} rows")
+    _log(f"layer full size batch 8, {sum(counts)} rows, rope theta {theta}")
     shape = synth.LLADA8B
-    case = Case(shape, 8, 1024, seed=4 + b)
+    case = Case(shape, 8, 1024, seed=4 + b, theta=theta)
     sel, cnt = _random_selection(case.g, 8, 1024, counts)
     (got,) = case.run_gpu(sel, cnt)
     ref = olayer.selective_layer(case.w, shape.n_heads, shape.head_dim, shape.eps,
                                  case.x[b:b + 1], sel[b:b + 1], cnt[b:b + 1], case.kc[b:b + 1],
-                                 case.vc[b:b + 1], case.y[b:b + 1])
+                                 case.vc[b:b + 1], case.y[b:b + 1], theta)
     sub = Case.__new__(Case)
     sub.kc, sub.vc, sub.y, sub.N = case.kc[b:b + 1], case.vc[b:b + 1], case.y[b:b + 1], 1024
     _compare(sub, tuple(t[b:b + 1] for t in got), ref, _rows(sel[b:b + 1], cnt[b:b + 1], 1, 1024))
@@ -252,6 +255,61 @@ def test_full_size_batch8_n2048_sampled():
         keep = np.setdiff1d(np.arange(2048), sel[bb, :cnt[bb]])
         assert np.array_equal(got[2][bb, keep], case.y[bb, keep])
         assert np.array_equal(got[0][bb, keep], case.kc[bb, keep])
+
+
+@pytest.mark.parametrize("d,dh", [(128, 64), (256, 32), (512, 128), (4096, 128)])
+def test_pack_qkv_layout(d, dh):
+    """dcu_pack_qkv against its header, bit for bit: the blocked layout (dcu_pack_weights, itself
+    checked against its formula above) of W_qkv with each Q and K head's rows reordered to
+    dims 0, h, 1, h+1, ... (h = dh/2); the V rows in order."""
+    _log(f"pack qkv d={d} dh={dh}")
+    g = np.random.default_rng(d + dh)
+    w = g.integers(0, 1 << 16, size=(3 * d, d), dtype=np.uint16)
+    h = dh // 2
+    order = np.stack([np.arange(h), np.arange(h) + h], axis=1).reshape(dh)   # 0, h, 1, h+1, ...
+    rows = np.concatenate([hd * dh + order for hd in range(2 * d // dh)] + [np.arange(2 * d, 3 * d)])
+    got = host_bf16(stc.dcu_pack_qkv(dev_bf16(w), dh))
+    want = host_bf16(stc.dcu_pack_weights(dev_bf16(np.ascontiguousarray(w[rows]))))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("shape,B,N,counts,max_rows,theta", [
+    (synth.TINY, 2, 64, [20, 41], 0, 1e4),
+    (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 4, 77, [77, 5, 33, 64], 0, 1e4),
+    (synth.LayerShape(d=512, n_heads=4, head_dim=128, ffn=768), 2, 300, [64, 257], 0, 5e5),
+    # split K on every projection (fixup epilogue), one and few rows
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 1, 256, [1], 1, 5e5),
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 2, 256, [100, 37], 0, 5e5),
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 3, 90, [17, 40, 7], 64, 5e5),
+])
+def test_selective_layer_rope(shape, B, N, counts, max_rows, theta):
+    """Rotary embedding in the QKV epilogue (direct and split-K fixup, 64-row and 128-row tiles):
+    keys cached rotated by their row's position; outputs against the oracle's rotated layer."""
+    _log(f"layer rope d={shape.d} dh={shape.head_dim} B={B} N={N} theta={theta}")
+    case = Case(shape, B, N, seed=shape.d + N + 5, theta=theta)
+    sel, cnt = _random_selection(case.g, B, N, counts)
+    (got, got2) = case.run_gpu(sel, cnt, max_rows=max_rows, reps=2)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
+
+
+def test_selective_layer_rope_dense():
+    """Dense mode (no selection) with rotary embedding: every row rotated by its own position."""
+    shape = synth.LayerShape(d=256, n_heads=2, head_dim=128, ffn=320)
+    case = Case(shape, 2, 150, seed=17, theta=5e5)
+    (got,) = case.run_gpu(None, None)
+    _compare(case, got, case.run_oracle(None, None), _rows(None, None, 2, 150))
+
+
+def test_full_size_rope_single_sequence_n2048():
+    """LLaDA-8B shapes with rotary base 500000, batch 1, N = 2048, 64 rows spread over the whole
+    sequence (positions up to 2047)."""
+    _log("layer rope full size N 2048")
+    case = Case(synth.LLADA8B, 1, 2048, seed=19, theta=5e5)
+    sel, cnt = _random_selection(case.g, 1, 2048, [64])
+    (got,) = case.run_gpu(sel, cnt)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, 1, 2048))
 
 
 @pytest.mark.parametrize("shape,B,N", [
