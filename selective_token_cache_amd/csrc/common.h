@@ -77,14 +77,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* lds, int* total) {
   int inc = wave_incl_scan(v);
   if (lane == kWave - 1) lds[wid] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < nw; ++i) {
-      int t = lds[i];
-      lds[i] = run;
-      run += t;
-    }
-    lds[16] = run;
+  if (threadIdx.x < kWave) {  // wave 0 scans the (at most 16) wave totals
+    const int tv = lane < nw ? lds[lane] : 0;
+    const int ti = wave_incl_scan(tv);
+    if (lane < nw) lds[lane] = ti - tv;
+    if (lane == kWave - 1) lds[16] = ti;
   }
   __syncthreads();
   int res = lds[wid] + inc - v;

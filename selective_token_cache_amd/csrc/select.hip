@@ -8,8 +8,9 @@
 // positions in registers (N <= 8192).
 //  1. window mask and candidate flags (not in a window, d > 0); key = fp32 bits of d (monotone for
 //     d >= 0), 0 for non-candidates;
-//  2. exact k-th largest key by an 8-bit LDS radix select (4 histogram passes, each followed by a
-//     parallel scan of the 256 bins from the top);
+//  2. exact k-th largest key by an 8-bit LDS radix select (4 histogram passes into two alternating
+//     LDS histograms; after each, one wave scans the 256 bins from the top, 4 per lane, and clears
+//     the other histogram: two barriers per pass);
 //  3. keys equal to the threshold are taken lowest position first (a block scan gives each tied
 //     key its rank);
 //  4. a block scan compacts W u A into ascending positions.
@@ -29,11 +30,10 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
                                                      int32_t* __restrict__ sel_idx,
                                                      int32_t* __restrict__ sel_count,
                                                      float* __restrict__ mean) {
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];  // radix histograms, used alternately
   __shared__ int scan_lds[17];
   __shared__ uint32_t s_prefix;
   __shared__ int s_remaining;
-  __shared__ int wtot[4];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int E = (N + kThreads - 1) / kThreads;
@@ -41,6 +41,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
   const float* d = dist + int64_t(b) * N;
   const int32_t* keys = key_pos ? key_pos + int64_t(b) * P : nullptr;
   const int half = b_window / 2;
+  int budget = budgets[int64_t(b) * L + layer];  // issued early: its latency overlaps the loads below
+  if (t < 256) hist[0][t] = 0;  // ordered before the first pass by the block sum's barriers
 
   uint32_t key[kMaxE];
   bool inw[kMaxE];
@@ -82,7 +84,6 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
   const int nC = block_sum_int(ncand, scan_lds);
   if (mean && t == 0)
     mean[b] = float(((mpart[0] + mpart[1]) + (mpart[2] + mpart[3])) / double(N));
-  int budget = budgets[int64_t(b) * L + layer];
   budget = budget < 0 ? 0 : budget;
   const int k = budget < nC ? budget : nC;
 
@@ -95,38 +96,48 @@ __global__ __launch_bounds__(kThreads) void k_select(const float* __restrict__ d
   } else if (k > 0) {
     uint32_t prefix = 0u;
     int remaining = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      const uint32_t hi_mask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-      if (t < 256) hist[t] = 0;
-      __syncthreads();
+    const int lane = t & (kWave - 1);
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+      int* H = hist[pass & 1];
 #pragma unroll
       for (int e = 0; e < kMaxE; ++e) {
         if (key[e] != 0u && ((key[e] ^ prefix) & hi_mask) == 0u)
-          atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
+          atomicAdd(&H[(key[e] >> shift) & 255u], 1);
       }
-      __syncthreads();
-      // thread j looks at bin 255-j: an inclusive scan in descending-bin order finds the bin
-      // that holds the remaining-th largest key
-      int inc_w = 0;
-      if (t < 256) {
-        inc_w = wave_incl_scan(hist[255 - t]);
-        if ((t & (kWave - 1)) == kWave - 1) wtot[t / kWave] = inc_w;
-      }
-      __syncthreads();
-      if (t < 256) {
-        int before = 0;
-        for (int w = 0; w < t / kWave; ++w) before += wtot[w];
-        const int inc = inc_w + before;
-        const int exc = inc - hist[255 - t];
+      __syncthreads();  // histogram complete
+      if (t < kWave) {
+        // wave 0: lane l holds bins 255-4l .. 252-4l (descending); an inclusive scan over the lanes
+        // finds the bin that holds the remaining-th largest key
+        const int b0 = 255 - 4 * lane;
+        const int c0 = H[b0], c1 = H[b0 - 1], c2 = H[b0 - 2], c3 = H[b0 - 3];
+        const int sum = c0 + c1 + c2 + c3;
+        const int inc = wave_incl_scan(sum);
+        const int exc = inc - sum;
         if (exc < remaining && inc >= remaining) {
-          s_prefix = prefix | (uint32_t(255 - t) << shift);
-          s_remaining = remaining - exc;
+          const int r = remaining - exc;
+          int bin, rem;
+          if (r <= c0) {
+            bin = b0; rem = r;
+          } else if (r <= c0 + c1) {
+            bin = b0 - 1; rem = r - c0;
+          } else if (r <= c0 + c1 + c2) {
+            bin = b0 - 2; rem = r - c0 - c1;
+          } else {
+            bin = b0 - 3; rem = r - c0 - c1 - c2;
+          }
+          s_prefix = prefix | (uint32_t(bin) << shift);
+          s_remaining = rem;
         }
+        // the other histogram is free (its pass ended two barriers ago): clear it for the next
+        int* Hn = hist[(pass + 1) & 1];
+        Hn[b0] = 0; Hn[b0 - 1] = 0; Hn[b0 - 2] = 0; Hn[b0 - 3] = 0;
       }
-      __syncthreads();
+      __syncthreads();  // threshold bin published
       prefix = s_prefix;
       remaining = s_remaining;
-      __syncthreads();
     }
     K = prefix;
     take_eq = remaining;

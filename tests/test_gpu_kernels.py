@@ -160,6 +160,23 @@ def test_select_bit_exact(N):
     _check_select(d, budgets, 5, None, 0)
 
 
+@pytest.mark.parametrize("N,frac", [(2048, 0.3), (2048, 0.9), (8192, 0.1), (8192, 0.6), (1024, 1.0)])
+def test_select_candidate_fractions(N, frac):
+    """Few and many candidates (distance > 0 outside the windows), ties included, at 1, 2 and 8
+    positions per thread: the oracle's selection bit for bit."""
+    _log(f"select paths N={N} frac={frac}")
+    g = synth.rng(905, N)
+    B, L = 3, 4
+    d = g.uniform(1e-6, 1e-3, (B, N)).astype(np.float32)
+    d[g.random((B, N)) >= frac] = 0.0
+    ties = g.random((B, N)) < 0.15
+    d[ties & (d > 0)] = np.float32(2.5e-4)
+    budgets = g.integers(1, max(2, int(N * frac)), (B, L)).astype(np.int32)
+    keys = g.integers(0, N, (B, 4)).astype(np.int32)
+    for bw in [0, 16]:
+        _check_select(d, budgets, 1, keys, bw)
+
+
 def test_select_identical_inputs_give_only_windows():
     d = np.zeros((2, 1024), np.float32)
     budgets = np.full((2, 32), 32, np.int32)
