@@ -61,7 +61,15 @@ struct Ptrs {
   uint16_t* h;    // [M_cap, F]
   float* opart;   // [S, M_cap, d]      (split attention only)
   float* ml;      // [S, M_cap, H, 2]   (split attention only)
+  float2* rope;   // [M_cap, rope_dh / 2] (cos, sin) of each row's rotation angles
+  int rope_dh;    // head_dim with rotary embedding, else 0
+  float rope_l2t; // log2(theta)
 };
+
+// Rotation angle of head-dim pair i (i < dh/2) at position pos: pos * theta^(-2i/dh), in fp32
+__device__ __forceinline__ float rope_angle(float pos, int i, int dh, float l2t) {
+  return pos * exp2f(-float(2 * i) * (l2t / float(dh)));
+}
 
 // ------------------------------------------------------------------------------ 1+2. plan, gather, RMSNorm
 constexpr int kMaxSeqs = 4096;  // sequences per call (LDS prefix of the per-sequence counts)
@@ -217,6 +225,14 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
     const int b = lo, j = r - off[b];
     const int grow = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
     if (lane == 0) P.rowmap[r] = grow;
+    if (P.rope_dh > 0) {  // (cos, sin) of the row's rotation angles, read by the QKV epilogue
+      const float pos = float(grow - b * N);
+      for (int i = lane; i < P.rope_dh / 2; i += kWave) {
+        float sn, cs;
+        sincosf(rope_angle(pos, i, P.rope_dh, P.rope_l2t), &sn, &cs);
+        P.rope[int64_t(r) * (P.rope_dh / 2) + i] = make_float2(cs, sn);
+      }
+    }
     rms_row<NC, false>(x + int64_t(grow) * d, gain, d, eps, out + int64_t(r) * d, lane);
   }
 }
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ a
 }
 
 // ------------------------------------------------------------------------------ 3/5/7/8. GEMM
-enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3, EPI_VPROJ = 4 };
+enum { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_DOWN = 3, EPI_VPROJ = 4, EPI_QKV_ROPE = 5 };
 
 struct GemmArgs {
   const uint16_t* A;    // [M, K] compacted rows (workspace)
@@ -251,21 +267,31 @@ struct GemmArgs {
   uint16_t* h;          // SWIGLU: out [M, F]
   uint16_t* y;          // DOWN: scatter target; VPROJ: V rows out (via the row map)
   float* part;          // split tail partial tiles [2 * grid, BM * BN] fp32
-  int N;                // QKV: sequence length (a row's position is its global row mod N)
   int rope_dh;          // QKV: head_dim with rotary embedding (W_qkv from dcu_pack_qkv), else 0
-  float rope_l2t;       // QKV: log2(theta) of the rotary embedding
+  const float2* rope;   // QKV: [M, rope_dh / 2] (cos, sin) per row, written by the gather kernel
 };
 
 // QKV output columns n .. n+3 of compacted row m (global row grow; n a multiple of 4): Q to the q
 // rows, K and V to the caches. With rotary embedding, W_qkv was packed by dcu_pack_qkv: inside every
 // Q and K head, packed column 2i holds head dim i and 2i+1 holds head dim i + dh/2, so the four
 // values are the rotation pairs (i, i + dh/2) and (i+1, i+1 + dh/2). Each pair turns by
-// pos * theta^(-2i/dh) and both land back on their own head dims (standard cache layout).
+// pos * theta^(-2i/dh) (cos and sin from the row's table) and both land back on their own head
+// dims (standard cache layout).
+// (cos, sin) of the two rotation pairs that QKV output columns n .. n+3 of compacted row m hold
+// (zeros outside the Q and K parts)
+__device__ __forceinline__ float4 rope_cs(const GemmArgs& g, int m, int n) {
+  const int part = n / g.d, col = n - part * g.d;
+  if (part == 2) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const int i = (col & (g.rope_dh - 1)) >> 1;
+  return *reinterpret_cast<const float4*>(g.rope + int64_t(m) * (g.rope_dh >> 1) + i);
+}
+
+template <bool kRope>
 __device__ __forceinline__ void store_qkv(const GemmArgs& g, int m, int64_t grow, int n, float w0,
-                                          float w1, float w2, float w3) {
+                                          float w1, float w2, float w3, float4 cs) {
   const int part = n / g.d, col = n - part * g.d;
   uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
-  if (g.rope_dh == 0 || part == 2) {
+  if (!kRope || part == 2) {
     uint2 st;
     st.x = pack_bf2(w0, w1);
     st.y = pack_bf2(w2, w3);
@@ -273,11 +299,7 @@ __device__ __forceinline__ void store_qkv(const GemmArgs& g, int m, int64_t grow
     return;
   }
   const int dh = g.rope_dh, c = col & (dh - 1), i = c >> 1;
-  const float pos = float(grow % g.N);
-  const float step = g.rope_l2t / float(dh);
-  float s0, c0, s1, c1;
-  sincosf(pos * exp2f(-float(2 * i) * step), &s0, &c0);
-  sincosf(pos * exp2f(-float(2 * i + 2) * step), &s1, &c1);
+  const float c0 = cs.x, s0 = cs.y, c1 = cs.z, s1 = cs.w;
   uint16_t* head = dst + (col - c);
   *reinterpret_cast<uint32_t*>(head + i) = pack_bf2(w0 * c0 - w1 * s0, w2 * c1 - w3 * s1);
   *reinterpret_cast<uint32_t*>(head + i + (dh >> 1)) =
@@ -375,7 +397,8 @@ __device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
 // batch 8, N = 1024, output 58.0 + 17.8 (split fixup) -> 60.4 + 6.8 us, down and QKV even.
 template <int EPI, class C>
 constexpr bool early_refill() {
-  return (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_DOWN || EPI == EPI_VPROJ) &&
+  return (EPI == EPI_QKV || EPI == EPI_QKV_ROPE || EPI == EPI_RESID || EPI == EPI_DOWN ||
+          EPI == EPI_VPROJ) &&
          std::is_same<C, CfgSmall>::value;
 }
 template <int EPI, class C>
@@ -390,11 +413,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / C::WGN, wn = wid % C::WGN;
   const int cg = (lane >> 4) * 4;
+  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
-    if (m >= M) continue;
-    if constexpr (EPI == EPI_SWIGLU) {
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+      if (m >= M) continue;
 #pragma unroll
       for (int fn = 0; fn < C::FN / 2; ++fn) {
         const int j = n_t * (C::BN / 2) + wn * (C::WN / 2) + fn * 16 + cg;
@@ -409,7 +432,59 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         st.y = pack_bf2(v[2], v[3]);
         *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
       }
-    } else {
+    }
+  } else if constexpr (EPI == EPI_QKV_ROPE || EPI == EPI_DOWN) {
+    // Every load of these epilogues (row map, rotary table, fp32 a) is issued before the first
+    // store: loads and stores share one memory counter, so a load issued after a store also waits
+    // for the store. (Measured faster for these two; the others keep their loads next to the
+    // stores.)
+    int64_t grow[C::FM];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+      grow[fm] = m < M ? int64_t(g.rowmap[m]) : 0;
+    }
+    float4 opnd[C::FM][C::FN];  // EPI_QKV_ROPE: (cos, sin) pairs; EPI_DOWN: fp32 a
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+        opnd[fm][fn] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m >= M || n >= g.Nout) continue;
+        if constexpr (EPI == EPI_QKV_ROPE)
+          opnd[fm][fn] = rope_cs(g, m, n);
+        else
+          opnd[fm][fn] = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+        if (n >= g.Nout) continue;
+        const gemm::f32x4 v = acc[fm][fn];
+        const float4 p = opnd[fm][fn];
+        if constexpr (EPI == EPI_QKV_ROPE) {
+          store_qkv<true>(g, m, grow[fm], n, v[0], v[1], v[2], v[3], p);
+        } else {
+          uint2 st;
+          st.x = pack_bf2(p.x + v[0], p.y + v[1]);
+          st.y = pack_bf2(p.z + v[2], p.w + v[3]);
+          *reinterpret_cast<uint2*>(g.y + grow[fm] * g.d + n) = st;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+      if (m >= M) continue;
       const int64_t grow = int64_t(g.rowmap[m]);
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
@@ -417,7 +492,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         if (n >= g.Nout) continue;
         const gemm::f32x4 v = acc[fm][fn];
         if constexpr (EPI == EPI_QKV) {
-          store_qkv(g, m, grow, n, v[0], v[1], v[2], v[3]);
+          store_qkv<false>(g, m, grow, n, v[0], v[1], v[2], v[3], float4{});
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           float4 o;
@@ -426,16 +501,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
           o.z = bf_lo(xr.y) + v[2];
           o.w = bf_hi(xr.y) + v[3];
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
-        } else if constexpr (EPI == EPI_VPROJ) {
+        } else {  // EPI_VPROJ
           uint2 st;
           st.x = pack_bf2(v[0], v[1]);
           st.y = pack_bf2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
-        } else {  // EPI_DOWN
-          const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
-          uint2 st;
-          st.x = pack_bf2(ar.x + v[0], ar.y + v[1]);
-          st.y = pack_bf2(ar.z + v[2], ar.w + v[3]);
           *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
         }
       }
@@ -623,7 +692,9 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
         const int n = n_t * C::BN + c4;
         const int64_t grow = int64_t(g.rowmap[m]);
         if constexpr (EPI == EPI_QKV) {
-          store_qkv(g, m, grow, n, w.x, w.y, w.z, w.w);
+          store_qkv<false>(g, m, grow, n, w.x, w.y, w.z, w.w, float4{});
+        } else if constexpr (EPI == EPI_QKV_ROPE) {
+          store_qkv<true>(g, m, grow, n, w.x, w.y, w.z, w.w, rope_cs(g, m, n));
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
@@ -1024,7 +1095,7 @@ constexpr int kCUs = 256;
 
 struct Layout {
   int M_cap, Tq_max;
-  size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, total;
+  size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, rope, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1056,6 +1127,8 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   // attention split units: [kAttnMaxUnits][kQTile][head_dim] fp32 and [kAttnMaxUnits][kQTile][2]
   L.opart = take(size_t(4) * kAttnMaxUnits * kQTile * w->head_dim);
   L.ml = take(size_t(4) * kAttnMaxUnits * kQTile * 2);
+  // rotary (cos, sin) per row and head-dim pair
+  L.rope = take(w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE ? size_t(4) * M * w->head_dim : 0);
   L.total = off;
   return L;
 }
@@ -1223,6 +1296,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   P.h = reinterpret_cast<uint16_t*>(ws + L.h);
   P.opart = reinterpret_cast<float*>(ws + L.opart);
   P.ml = reinterpret_cast<float*>(ws + L.ml);
+  P.rope = reinterpret_cast<float2*>(ws + L.rope);
+  P.rope_dh = w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE ? w->head_dim : 0;
+  P.rope_l2t = P.rope_dh > 0 ? float(log2(double(w->rope_theta))) : 0.0f;
   const int d = w->d, F = w->ffn, H = w->n_heads, DH = w->head_dim;
   const uint16_t* x = static_cast<const uint16_t*>(x_in);
   int stage = 0;
@@ -1265,15 +1341,18 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.q = P.q;
   ga.kc = static_cast<uint16_t*>(k_cache);
   ga.vc = static_cast<uint16_t*>(v_cache);
-  ga.N = N;
-  if (w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE) {
-    ga.rope_dh = w->head_dim;
-    ga.rope_l2t = float(log2(double(w->rope_theta)));
-  }
-  launch_gemm<EPI_QKV>(ga, s);
+  ga.rope_dh = P.rope_dh;
+  ga.rope = P.rope;
+  if (P.rope_dh > 0)
+    launch_gemm<EPI_QKV_ROPE>(ga, s);
+  else
+    launch_gemm<EPI_QKV>(ga, s);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_QKV>(ga, s, L.M_cap);
+  if (P.rope_dh > 0)
+    launch_fixup<EPI_QKV_ROPE>(ga, s, L.M_cap);
+  else
+    launch_fixup<EPI_QKV>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
