@@ -4,13 +4,17 @@
 //
 // The layer is pre-norm: xn = RMSNorm(x; g_attn), [q|k|v] = xn W_qkv^T, attention of the selected
 // queries over all N cached keys/values (no mask, scale 1/sqrt(head_dim)), a = x + o W_o^T,
-// an = RMSNorm(a; g_ffn), y = a + (silu(an W_gate^T) * an W_up^T) W_down^T.
+// an = RMSNorm(a; g_ffn), y = a + (silu(an W_gate^T) * an W_up^T) W_down^T. Optionally (rotary
+// layout) q and k of a row at position p are turned pairwise (head dims i, i + dh/2) by
+// p * theta^(-2i/dh) before k is cached.
 //
 // Kernels, in stream order (no host synchronisation; ragged per-sequence counts stay on device):
 //  1. k_gather_rmsnorm  per-sequence row offsets (clamped to the workspace capacity) from the
 //                     counts, the compacted row map (selected row -> global cache row), attention
-//                     query-tile tables, and the gather of the selected input rows + RMSNorm -> xn;
-//  3. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches;
+//                     query-tile tables, the gather of the selected input rows + RMSNorm -> xn,
+//                     and (rotary layout) each row's (cos, sin) table;
+//  3. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches
+//                     (k_gemm<QKV_ROPE>: the same with the rotation of q and k);
 //  4. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
 //                     when there are too few tiles to fill the chip) + k_attn_combine;
 //  5. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
