@@ -812,6 +812,26 @@ __device__ __forceinline__ int kvsw(int key) {
 template <int CH>
 __device__ __forceinline__ int kswz(int key, int c) { return key * CH + (c ^ kvsw<CH>(key)); }
 
+// Pair exchange across 16 or 32 lanes with the gfx950 permlane swaps (VALU, no LDS round trip).
+// Called with the same value twice they return, in every lane l, the values of lanes l & ~S and
+// l | S, so a symmetric combine of the two equals the combine with lane l ^ S.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
@@ -945,8 +965,7 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
       for (int f = 0; f < kKF; ++f)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[f][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = max_xor32(max_xor16(mx));
       mx *= g.scale_log2;
       // lazy rescaling: the reference max only moves when a score exceeds it by more than 2^8, so
       // exp2(score - m_ref) <= 256 and the accumulators are rescaled rarely (exact after the final
@@ -1013,8 +1032,7 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
       __builtin_amdgcn_s_barrier();
     }
 
-    float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
-    l_tot += __shfl_xor(l_tot, 32, kWave);
+    const float l_tot = sum_xor32(sum_xor16(l_part));
     if (qvalid) {
       if (w < ap.full) {
         const float inv = 1.0f / l_tot;
