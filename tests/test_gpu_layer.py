@@ -343,3 +343,16 @@ def test_v_features_and_v_distance(shape, B, N):
     sel, cnt = stc.dcu_select(dist, dev(budgets), 0, dev(keys), 8)
     rs, rc = osel.select(dist.cpu().numpy(), budgets, 0, keys, 8)
     assert np.array_equal(cnt.cpu().numpy(), rc) and np.array_equal(sel.cpu().numpy(), rs)
+
+
+def test_v_features_with_the_rotary_layout():
+    """The V rows keep their order in dcu_pack_qkv, so the Value vectors of a rotary layer are
+    bit-identical to those of the same weights in the plain layout (no rotation on V)."""
+    shape = synth.LayerShape(d=256, n_heads=2, head_dim=128, ffn=320)
+    case = Case(shape, 2, 70, seed=23)
+    plain = case.layer()
+    case.theta = 5e5
+    rot = case.layer()
+    x = dev_bf16(case.x)
+    assert torch.equal(stc.dcu_v_features(plain, x).view(torch.int16),
+                       stc.dcu_v_features(rot, x).view(torch.int16))
