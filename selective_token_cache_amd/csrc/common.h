@@ -36,17 +36,56 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
 }
 
 // ---------------------------------------------------------------------------- wave reductions
+// The value of lane l ^ OFF (OFF = 16 or 32) through the gfx950 permlane swaps (VALU, no LDS round
+// trip). Given the same operand twice, a swap returns in every lane l the values of lanes l & ~OFF
+// and l | OFF; the partner is the one that is not lane l.
+template <int OFF>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x) {
+  static_assert(OFF == 16 || OFF == 32, "permlane swap distance");
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const bool upper = (lane & OFF) != 0;
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return upper ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return upper ? r[0] : r[1];
+  }
+}
+template <int OFF, typename T>
+__device__ __forceinline__ T xor_lane(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, xor_lane_u32<OFF>(__builtin_bit_cast(uint32_t, v)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = xor_lane_u32<OFF>(uint32_t(u));
+    const uint64_t hi = xor_lane_u32<OFF>(uint32_t(u >> 32));
+    return __builtin_bit_cast(T, lo | (hi << 32));
+  }
+}
+
+// Butterfly over the wave in the fixed order 32, 16, 8, 4, 2, 1 (every lane ends with the same
+// value); the first two exchanges use the permlane swaps, the rest LDS-free shuffles of the
+// compiler's choice. Each step adds the partner's value: the result does not depend on how the
+// partner value travels.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
+  v += xor_lane<32>(v);
+  v += xor_lane<16>(v);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
+  T o = xor_lane<32>(v);
+  v = o > v ? o : v;
+  o = xor_lane<16>(v);
+  v = o > v ? o : v;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    T o = __shfl_xor(v, off, kWave);
+  for (int off = 8; off > 0; off >>= 1) {
+    o = __shfl_xor(v, off, kWave);
     v = o > v ? o : v;
   }
   return v;

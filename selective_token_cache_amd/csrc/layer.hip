@@ -129,8 +129,7 @@ __device__ __forceinline__ void rms_row(const void* __restrict__ row_v,
     for (int k = 0; k < 8; k += 2) ss += v[k] * v[k] + v[k + 1] * v[k + 1];
     return ss;
   };
-  auto store = [&](int g, const float (&v)[8], float scale) {
-    const uint4 gg = reinterpret_cast<const uint4*>(gain)[g];
+  auto store = [&](int g, const float (&v)[8], float scale, const uint4 gg) {
     uint4 o;
     o.x = pack_bf2(v[0] * scale * bf_lo(gg.x), v[1] * scale * bf_hi(gg.x));
     o.y = pack_bf2(v[2] * scale * bf_lo(gg.y), v[3] * scale * bf_hi(gg.y));
@@ -141,11 +140,13 @@ __device__ __forceinline__ void rms_row(const void* __restrict__ row_v,
   float ss = 0.0f;
   if constexpr (NC > 0) {
     float v[NC][8];
+    uint4 gg[NC];  // the gains are loaded with the row, not after its reduction
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int g = lane + c * kWave;
       if (g < groups) {
         load(g, v[c]);
+        gg[c] = reinterpret_cast<const uint4*>(gain)[g];
       } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[c][k] = 0.0f;
@@ -158,7 +159,7 @@ __device__ __forceinline__ void rms_row(const void* __restrict__ row_v,
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int g = lane + c * kWave;
-      if (g < groups) store(g, v[c], scale);
+      if (g < groups) store(g, v[c], scale, gg[c]);
     }
   } else {
     for (int g = lane; g < groups; g += kWave) {
@@ -171,7 +172,7 @@ __device__ __forceinline__ void rms_row(const void* __restrict__ row_v,
     for (int g = lane; g < groups; g += kWave) {
       float v[8];
       load(g, v);
-      store(g, v, scale);
+      store(g, v, scale, reinterpret_cast<const uint4*>(gain)[g]);
     }
   }
 }
