@@ -179,8 +179,9 @@ int dcu_pack_gate_up(const void* w_gate, const void* w_up, int32_t F, int32_t d,
  * w_qkv  [3d, d] bf16 row-major, rows Wq | Wk | Wv. Not modified.
  * out    3 * d * d bf16, caller-owned, must not overlap w_qkv: the blocked layout of
  *        dcu_pack_weights applied to the matrix whose Q and K rows are reordered inside every head
- *        (head dim j < head_dim/2 at head row 2j, j >= head_dim/2 at head row 2(j - head_dim/2) + 1),
- *        so that the two dims of a rotation pair are adjacent outputs; the V rows keep their order.
+ *        in groups of 16 (with h = head_dim/2: head dims 0..15, h..h+15, 16..31, h+16..h+31, ...),
+ *        so that the two dims of a rotation pair are outputs 16 apart within one 32-row group; the
+ *        V rows keep their order.
  * Errors: EINVAL on NULL pointers, d or head_dim <= 0, d % head_dim != 0; EUNSUPPORTED if
  *         head_dim not in {32, 64, 128}, d % 64 != 0, 3 * d * d >= 2^40, or a pointer not 16-byte
  *         aligned.

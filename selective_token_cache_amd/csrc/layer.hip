@@ -277,38 +277,51 @@ struct GemmArgs {
 };
 
 // QKV output columns n .. n+3 of compacted row m (global row grow; n a multiple of 4): Q to the q
-// rows, K and V to the caches. With rotary embedding, W_qkv was packed by dcu_pack_qkv: inside every
-// Q and K head, packed column 2i holds head dim i and 2i+1 holds head dim i + dh/2, so the four
-// values are the rotation pairs (i, i + dh/2) and (i+1, i+1 + dh/2). Each pair turns by
-// pos * theta^(-2i/dh) (cos and sin from the row's table) and both land back on their own head
-// dims (standard cache layout).
-// (cos, sin) of the two rotation pairs that QKV output columns n .. n+3 of compacted row m hold
-// (zeros outside the Q and K parts)
-__device__ __forceinline__ float4 rope_cs(const GemmArgs& g, int m, int n) {
-  const int part = n / g.d, col = n - part * g.d;
-  if (part == 2) return make_float4(0.f, 0.f, 0.f, 0.f);
-  const int i = (col & (g.rope_dh - 1)) >> 1;
-  return *reinterpret_cast<const float4*>(g.rope + int64_t(m) * (g.rope_dh >> 1) + i);
-}
-
-template <bool kRope>
+// rows, K and V to the caches.
 __device__ __forceinline__ void store_qkv(const GemmArgs& g, int m, int64_t grow, int n, float w0,
-                                          float w1, float w2, float w3, float4 cs) {
+                                          float w1, float w2, float w3) {
   const int part = n / g.d, col = n - part * g.d;
   uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
-  if (!kRope || part == 2) {
-    uint2 st;
-    st.x = pack_bf2(w0, w1);
-    st.y = pack_bf2(w2, w3);
-    *reinterpret_cast<uint2*>(dst + col) = st;
+  uint2 st;
+  st.x = pack_bf2(w0, w1);
+  st.y = pack_bf2(w2, w3);
+  *reinterpret_cast<uint2*>(dst + col) = st;
+}
+
+// Rotary layout (dcu_pack_qkv): inside every Q and K head, packed columns 32k .. 32k+15 hold head
+// dims 16k .. 16k+15 and packed columns 32k+16 .. 32k+31 hold dims h+16k .. h+16k+15 (h = dh/2), so
+// an MFMA fragment and the one 16 columns to its right hold four whole rotation pairs in the same
+// lane. x (packed columns n .. n+3, n in the first half of its 32-column group) pairs with y
+// (n+16 .. n+19); cs0, cs1 are the (cos, sin) of the four pairs. Each half is written back as one
+// 8-byte store at its own head dims (standard cache layout); V columns are stored as they are.
+__device__ __forceinline__ float4 rope_cs(const GemmArgs& g, int m, int n, int which) {
+  const int part = n / g.d, col = n - part * g.d;
+  if (part == 2) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const int c = col & (g.rope_dh - 1);
+  const int i = ((c >> 5) << 4) + (c & 15);  // head dim of the first pair
+  return *reinterpret_cast<const float4*>(g.rope + int64_t(m) * (g.rope_dh >> 1) + i + 2 * which);
+}
+__device__ __forceinline__ void store_qkv_rope(const GemmArgs& g, int m, int64_t grow, int n,
+                                               float4 x, float4 y, float4 cs0, float4 cs1) {
+  const int part = n / g.d, col = n - part * g.d;
+  uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
+  uint2 a, b;
+  if (part == 2) {
+    a.x = pack_bf2(x.x, x.y); a.y = pack_bf2(x.z, x.w);
+    b.x = pack_bf2(y.x, y.y); b.y = pack_bf2(y.z, y.w);
+    *reinterpret_cast<uint2*>(dst + col) = a;
+    *reinterpret_cast<uint2*>(dst + col + 16) = b;
     return;
   }
-  const int dh = g.rope_dh, c = col & (dh - 1), i = c >> 1;
-  const float c0 = cs.x, s0 = cs.y, c1 = cs.z, s1 = cs.w;
+  const int dh = g.rope_dh, c = col & (dh - 1);
+  const int i = ((c >> 5) << 4) + (c & 15);
   uint16_t* head = dst + (col - c);
-  *reinterpret_cast<uint32_t*>(head + i) = pack_bf2(w0 * c0 - w1 * s0, w2 * c1 - w3 * s1);
-  *reinterpret_cast<uint32_t*>(head + i + (dh >> 1)) =
-      pack_bf2(w1 * c0 + w0 * s0, w3 * c1 + w2 * s1);
+  a.x = pack_bf2(x.x * cs0.x - y.x * cs0.y, x.y * cs0.z - y.y * cs0.w);
+  a.y = pack_bf2(x.z * cs1.x - y.z * cs1.y, x.w * cs1.z - y.w * cs1.w);
+  b.x = pack_bf2(y.x * cs0.x + x.x * cs0.y, y.y * cs0.z + x.y * cs0.w);
+  b.y = pack_bf2(y.z * cs1.x + x.z * cs1.y, y.w * cs1.z + x.w * cs1.w);
+  *reinterpret_cast<uint2*>(head + i) = a;
+  *reinterpret_cast<uint2*>(head + i + (dh >> 1)) = b;
 }
 
 // Tail splitting: with a persistent grid of G workgroup slots and T output tiles, the last round holds
@@ -449,19 +462,23 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
       grow[fm] = m < M ? int64_t(g.rowmap[m]) : 0;
     }
-    float4 opnd[C::FM][C::FN];  // EPI_QKV_ROPE: (cos, sin) pairs; EPI_DOWN: fp32 a
+    // EPI_QKV_ROPE: (cos, sin) of the pairs of fragment pair fn/2 (two float4 each);
+    // EPI_DOWN: fp32 a of each fragment
+    float4 opnd[C::FM][C::FN];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
         opnd[fm][fn] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m >= M || n >= g.Nout) continue;
-        if constexpr (EPI == EPI_QKV_ROPE)
-          opnd[fm][fn] = rope_cs(g, m, n);
-        else
-          opnd[fm][fn] = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+        if constexpr (EPI == EPI_QKV_ROPE) {
+          const int n = n_t * C::BN + wn * C::WN + (fn & ~1) * 16 + cg;
+          if (m < M && n < g.Nout) opnd[fm][fn] = rope_cs(g, m, n, fn & 1);
+        } else {
+          const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+          if (m < M && n < g.Nout)
+            opnd[fm][fn] = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -469,15 +486,23 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
       if (m >= M) continue;
+      if constexpr (EPI == EPI_QKV_ROPE) {
+        static_assert(C::FN % 2 == 0, "fragment pairs");
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
-        if (n >= g.Nout) continue;
-        const gemm::f32x4 v = acc[fm][fn];
-        const float4 p = opnd[fm][fn];
-        if constexpr (EPI == EPI_QKV_ROPE) {
-          store_qkv<true>(g, m, grow[fm], n, v[0], v[1], v[2], v[3], p);
-        } else {
+        for (int fp = 0; fp < C::FN; fp += 2) {
+          const int n = n_t * C::BN + wn * C::WN + fp * 16 + cg;
+          if (n >= g.Nout) continue;
+          const gemm::f32x4 x = acc[fm][fp], y = acc[fm][fp + 1];
+          store_qkv_rope(g, m, grow[fm], n, make_float4(x[0], x[1], x[2], x[3]),
+                         make_float4(y[0], y[1], y[2], y[3]), opnd[fm][fp], opnd[fm][fp + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+          if (n >= g.Nout) continue;
+          const gemm::f32x4 v = acc[fm][fn];
+          const float4 p = opnd[fm][fn];
           uint2 st;
           st.x = pack_bf2(p.x + v[0], p.y + v[1]);
           st.y = pack_bf2(p.z + v[2], p.w + v[3]);
@@ -497,7 +522,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         if (n >= g.Nout) continue;
         const gemm::f32x4 v = acc[fm][fn];
         if constexpr (EPI == EPI_QKV) {
-          store_qkv<false>(g, m, grow, n, v[0], v[1], v[2], v[3], float4{});
+          store_qkv(g, m, grow, n, v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           float4 o;
@@ -617,9 +642,12 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
   const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
   const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode<EPI, C>());
   if (sp.rem == 0) return;
-  constexpr int OUTC = EPI == EPI_SWIGLU ? C::BN / 2 : C::BN;  // output columns per tile
-  constexpr int Q = C::BM * OUTC / 4;                          // float4 groups per tile
-  constexpr int NV = EPI == EPI_SWIGLU ? 2 : 1;                // float4 per item and partial
+  // SwiGLU: an item is an output column group from its gate and up columns; rotary QKV: an item is
+  // a column group of a 32-column group's first half together with its partner 16 columns on
+  constexpr bool kPair = EPI == EPI_SWIGLU || EPI == EPI_QKV_ROPE;
+  constexpr int OUTC = kPair ? C::BN / 2 : C::BN;  // items (x 4 columns) per tile row
+  constexpr int Q = C::BM * OUTC / 4;              // float4 groups per tile
+  constexpr int NV = kPair ? 2 : 1;                // float4 per item and partial
   const int64_t total = int64_t(sp.rem) * Q;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   for (int64_t i0 = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i0 < total;
@@ -647,6 +675,11 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
         const int wn = c4 / (C::WN / 2), w = c4 % (C::WN / 2);
         cols[0] = wn * C::WN + w;
         cols[NV - 1] = cols[0] + C::WN / 2;
+      } else if constexpr (EPI == EPI_QKV_ROPE) {
+        cols[0] = (c4 >> 4) * 32 + (c4 & 15);
+        cols[NV - 1] = cols[0] + 16;
+        n = n_t * C::BN + cols[0];
+        ok[u] = i < total && m < M && n < g.Nout;
       } else {
         cols[0] = c4;
       }
@@ -697,9 +730,11 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
         const int n = n_t * C::BN + c4;
         const int64_t grow = int64_t(g.rowmap[m]);
         if constexpr (EPI == EPI_QKV) {
-          store_qkv<false>(g, m, grow, n, w.x, w.y, w.z, w.w, float4{});
+          store_qkv(g, m, grow, n, w.x, w.y, w.z, w.w);
         } else if constexpr (EPI == EPI_QKV_ROPE) {
-          store_qkv<true>(g, m, grow, n, w.x, w.y, w.z, w.w, rope_cs(g, m, n));
+          const int np = n_t * C::BN + cols_u[u][0];
+          store_qkv_rope(g, m, grow, np, w, v[u][NV - 1], rope_cs(g, m, np, 0),
+                         rope_cs(g, m, np, 1));
         } else if constexpr (EPI == EPI_RESID) {
           const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
@@ -1210,7 +1245,7 @@ void launch_fixup(const GemmArgs& ga, hipStream_t s, int M_cap) {
 // along the rows. With a second source b (the up matrix), the 16-row groups of a and b alternate
 // in the output (a's group g -> group 2g, b's group g -> group 2g + 1). With rope_rows > 0 (the Q
 // and K rows of W_qkv) the rows below rope_rows are reordered inside each head of dh rows: head dim
-// j < dh/2 becomes row 2j of the head, j >= dh/2 row 2(j - dh/2) + 1.
+// j < dh/2 becomes row 32(j/16) + j%16 of the head, j >= dh/2 row 32((j-dh/2)/16) + 16 + j%16.
 __global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ a,
                                                       const u32x4* __restrict__ b, int64_t rows,
                                                       int64_t cols, int64_t rope_rows, int dh,
@@ -1227,7 +1262,8 @@ __global__ __launch_bounds__(256) void k_pack_weights(const u32x4* __restrict__ 
     int64_t r = r0;
     if (r0 < rope_rows) {
       const int64_t j = r0 % dh, h = dh / 2;
-      r = r0 - j + (j < h ? 2 * j : 2 * (j - h) + 1);
+      const int64_t jj = j < h ? j : j - h;
+      r = r0 - j + (jj >> 4) * 32 + (j < h ? 0 : 16) + (jj & 15);
     }
     const int64_t g = (r >> 4) * nsrc + m, kt = ch >> 3;
     const int rr = int(r & 15), c = int(ch & 7);

@@ -260,13 +260,14 @@ def test_full_size_batch8_n2048_sampled():
 @pytest.mark.parametrize("d,dh", [(128, 64), (256, 32), (512, 128), (4096, 128)])
 def test_pack_qkv_layout(d, dh):
     """dcu_pack_qkv against its header, bit for bit: the blocked layout (dcu_pack_weights, itself
-    checked against its formula above) of W_qkv with each Q and K head's rows reordered to
-    dims 0, h, 1, h+1, ... (h = dh/2); the V rows in order."""
+    checked against its formula above) of W_qkv with each Q and K head's rows reordered in groups
+    of 16: dims 0..15, h..h+15, 16..31, h+16..h+31, ... (h = dh/2); the V rows in order."""
     _log(f"pack qkv d={d} dh={dh}")
     g = np.random.default_rng(d + dh)
     w = g.integers(0, 1 << 16, size=(3 * d, d), dtype=np.uint16)
     h = dh // 2
-    order = np.stack([np.arange(h), np.arange(h) + h], axis=1).reshape(dh)   # 0, h, 1, h+1, ...
+    order = np.concatenate([np.r_[16 * k:16 * k + 16, h + 16 * k:h + 16 * k + 16]
+                            for k in range(h // 16)])
     rows = np.concatenate([hd * dh + order for hd in range(2 * d // dh)] + [np.arange(2 * d, 3 * d)])
     got = host_bf16(stc.dcu_pack_qkv(dev_bf16(w), dh))
     want = host_bf16(stc.dcu_pack_weights(dev_bf16(np.ascontiguousarray(w[rows]))))
@@ -281,6 +282,9 @@ def test_pack_qkv_layout(d, dh):
     (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 1, 256, [1], 1, 5e5),
     (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 2, 256, [100, 37], 0, 5e5),
     (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 3, 90, [17, 40, 7], 64, 5e5),
+    # ragged QKV tiles (960 output columns) with 64- and 128-row tiles
+    (synth.LayerShape(d=320, n_heads=5, head_dim=64, ffn=448), 2, 100, [30, 23], 60, 1e4),
+    (synth.LayerShape(d=320, n_heads=5, head_dim=64, ffn=448), 2, 100, [70, 41], 0, 1e4),
 ])
 def test_selective_layer_rope(shape, B, N, counts, max_rows, theta):
     """Rotary embedding in the QKV epilogue (direct and split-K fixup, 64-row and 128-row tiles):
