@@ -517,6 +517,12 @@ def main():
                  "input_distance_us": round(t_xd, 2),
                  "v_proxy_over_input_proxy": round((t_vf + t_vd) / t_xd, 2),
                  "v_features_TFLOPps": round(2.0 * B * N * D * D / (t_vf * 1e-6) / 1e12, 1)}
+        # the attention-context feature (DyLLM style): q of every row and its attention over the
+        # caches, then the same distance on the contexts
+        t_ac = timed(lambda: stc.dcu_attention_context(layers[0][0], x_cur[0], kc[0], vc[0],
+                                                       ctx_out=v_new, workspace=ws))
+        vfeat["attention_context_us"] = round(t_ac, 2)
+        vfeat["context_proxy_over_input_proxy"] = round((t_ac + t_vd) / t_xd, 2)
         del v_new
 
     # adaptive parallel decoding on the same positions: the previous step's logits are this step's

@@ -16,6 +16,8 @@
  *   dllm_commit          the same with the factor, threshold or per-position threshold rule
  *   dllm_apd             adaptive-parallel-decoding signals and per-position thresholds
  *   dllm_commit_positions  committed positions -> the next step's key positions
+ *   dcu_v_features, dcu_attention_context  other distance features (Value vectors, attention
+ *                        contexts of every row)
  *   dcu_pack_weights, dcu_pack_gate_up, dcu_pack_qkv   the projections' blocked weight layout (set-up)
  *
  * Sources: "Dynamic-dLLM: Dynamic Cache-Budget and Adaptive Parallel Decoding for Training-Free
@@ -254,6 +256,24 @@ int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel
                         const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
                         void* k_cache, void* v_cache, void* y_out, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * dcu_attention_context -- the attention context of every row of a layer, for an attention-context
+ * distance. (DyLLM, in the pages' listing of related papers, finds its salient tokens by the cosine
+ * similarity of attention contexts between adjacent denoising steps; apply dcu_distance to ctx_out
+ * and the previous step's contexts.)
+ * For every row of x_in: xn = RMSNorm(x; g_attn), q = xn W_q^T (rotated by the row's position with
+ * DCU_WEIGHTS_BLOCKED_ROPE), ctx = softmax(q K^T / sqrt(head_dim)) V per head over the N cached
+ * rows of its sequence, with W_q the rows 0 .. d-1 of the layer's blocked W_qkv.
+ * x_in      [B, N, d] bf16.
+ * k_cache, v_cache  [B, N, n_heads, head_dim] bf16, read only (the caches as given; not updated).
+ * ctx_out   [B, N, d] bf16 out (heads contiguous), caller-owned.
+ * workspace at least dcu_selective_layer_workspace(w, B, N, B*N) bytes, 256-byte aligned.
+ * Errors: as dcu_selective_layer; EINVAL on a NULL x_in, cache or ctx_out.
+ */
+int dcu_attention_context(const dcu_layer* w, const void* x_in, int32_t B, int32_t N,
+                          const void* k_cache, const void* v_cache, void* ctx_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * dcu_v_features -- the Value vectors of every row of a layer, for the V-feature distance.

@@ -129,3 +129,28 @@ def v_features(w: dict, eps: float, x: np.ndarray) -> np.ndarray:
     x64 = as64(x)
     xn = rmsnorm(x64, w64["g_attn"], eps)
     return xn @ w64["w_qkv"][2 * d:3 * d].T
+
+
+def attention_context(w: dict, n_heads: int, head_dim: int, eps: float, x: np.ndarray,
+                      k_cache: np.ndarray, v_cache: np.ndarray, rope_theta: float = 0.0) -> np.ndarray:
+    """Attention context of every row (the DyLLM-style saliency feature: its cosine similarity
+    between adjacent steps marks the salient tokens), [B, N, d] fp64: per sequence and head,
+    softmax(q K^T / sqrt(head_dim)) V over the N cached rows as given, with q = RMSNorm(x; g_attn)
+    W_q^T (W_q the first d rows of W_qkv), rotated by each row's position when rope_theta > 0.
+    Reading: the caches are the previous step's (the feature decides what to recompute, so it is
+    taken before any recomputation)."""
+    w64 = weights64(w)
+    x64 = as64(x)
+    kc, vc = as64(k_cache), as64(v_cache)
+    B, N, d = x64.shape
+    H, dh = n_heads, head_dim
+    out = np.empty((B, N, d))
+    scale = 1.0 / np.sqrt(dh)
+    for b in range(B):
+        q = (rmsnorm(x64[b], w64["g_attn"], eps) @ w64["w_qkv"][:d].T).reshape(N, H, dh)
+        if rope_theta > 0:
+            q = rope(q, np.arange(N)[:, None], rope_theta)
+        for h in range(H):
+            p = softmax_rows((q[:, h, :] @ kc[b, :, h, :].T) * scale)
+            out[b, :, h * dh:(h + 1) * dh] = p @ vc[b, :, h, :]
+    return out

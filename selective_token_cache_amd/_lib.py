@@ -61,6 +61,8 @@ EXPORTS = {
                                            _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "dcu_v_features": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
+    "dcu_attention_context": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
+                                             _vp, _vp, ctypes.c_size_t, _vp]),
     "dcu_selective_layer_staged": (ctypes.c_int,
                                    [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                     _vp, _vp, _vp, ctypes.c_size_t, _vp,
@@ -438,6 +440,30 @@ def dcu_v_features(layer: Layer, x_in: torch.Tensor, v_out=None, workspace=None,
                                workspace.numel(), _stream(stream))
     _check("dcu_v_features", st)
     return v_out
+
+
+def dcu_attention_context(layer: Layer, x_in: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, ctx_out=None, workspace=None, stream=None):
+    """Attention context of every row: x_in [B, N, d] bf16 and the caches [B, N, H, dh] bf16 (read
+    only) -> ctx_out [B, N, d] bf16 = softmax(q K^T / sqrt(dh)) V per head, q = RMSNorm(x) W_q^T
+    (rotated with the rotary layout)."""
+    _need(x_in, "x_in", torch.bfloat16)
+    B, N, d = x_in.shape
+    if d != layer.d:
+        raise ValueError("x_in width does not match the layer")
+    _need(k_cache, "k_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    ctx_out = torch.empty_like(x_in) if ctx_out is None else ctx_out
+    _need(ctx_out, "ctx_out", torch.bfloat16, (B, N, d))
+    need = layer.workspace_bytes(B, N, B * N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+    _need(workspace, "workspace", torch.uint8)
+    st = load().dcu_attention_context(ctypes.byref(layer.desc), _p(x_in), B, N, _p(k_cache),
+                                      _p(v_cache), _p(ctx_out), _p(workspace), workspace.numel(),
+                                      _stream(stream))
+    _check("dcu_attention_context", st)
+    return ctx_out
 
 
 def dllm_commit_positions(order: torch.Tensor, n_commit: torch.Tensor, slot_pos: torch.Tensor,

@@ -1151,6 +1151,23 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH, int at
 // ------------------------------------------------------------------------------ host side
 constexpr int kCUs = 256;
 
+// Attention of the device-side query tiles over the caches, then the merge of split units (it exits
+// at once unless the device-side plan split the items).
+int launch_attention(const AttnArgs& aa, int DH, hipStream_t s) {
+  const int attn_blocks = kAttnWgs * kCUs;  // persistent; the plan depends on the device row count
+  static_assert(2 * (kAttnWgs * kCUs) <= kAttnMaxUnits, "attention split slots");
+  if (DH == 128)
+    hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  else if (DH == 64)
+    hipLaunchKernelGGL(k_attn<64>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  else
+    hipLaunchKernelGGL(k_attn<32>, dim3(attn_blocks), dim3(256), 0, s, aa);
+  DCU_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_attn_combine, dim3(kCUs), dim3(256), 0, s, aa, DH, attn_blocks);
+  DCU_LAUNCH_CHECK();
+  return DCU_OK;
+}
+
 struct Layout {
   int M_cap, Tq_max;
   size_t hdr, seq_off, tile_off, tile_seq, rowmap, xn, q, o, a, h, part, opart, ml, rope, total;
@@ -1432,18 +1449,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.d = d;
   aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;  // key ranges of >= 128 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
-  const int attn_blocks = kAttnWgs * kCUs;  // persistent; the plan depends on the device row count
-  static_assert(2 * (kAttnWgs * kCUs) <= kAttnMaxUnits, "attention split slots");
-  if (DH == 128)
-    hipLaunchKernelGGL(k_attn<128>, dim3(attn_blocks), dim3(256), 0, s, aa);
-  else if (DH == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3(attn_blocks), dim3(256), 0, s, aa);
-  else
-    hipLaunchKernelGGL(k_attn<32>, dim3(attn_blocks), dim3(256), 0, s, aa);
-  DCU_LAUNCH_CHECK();
-  // the merge exits at once unless the device-side plan split the items
-  hipLaunchKernelGGL(k_attn_combine, dim3(kCUs), dim3(256), 0, s, aa, DH, attn_blocks);
-  DCU_LAUNCH_CHECK();
+  st = launch_attention(aa, DH, s);
+  if (st != DCU_OK) return st;
   if (!mark()) return DCU_EHIP;
 
   // output projection + residual -> a (fp32)
@@ -1562,6 +1569,99 @@ extern "C" int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, i
   launch_fixup<EPI_VPROJ>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   return DCU_OK;
+}
+
+extern "C" int dcu_attention_context(const dcu_layer* w, const void* x_in, int32_t B, int32_t N,
+                                     const void* k_cache, const void* v_cache, void* ctx_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace dcu;
+  int st = validate(w, B, N);
+  if (st != DCU_OK) return st;
+  if (!x_in || !k_cache || !v_cache || !ctx_out) return DCU_EINVAL;
+  if (!dcu_aligned16(x_in) || !dcu_aligned16(k_cache) || !dcu_aligned16(v_cache) ||
+      !dcu_aligned16(ctx_out))
+    return DCU_EUNSUPPORTED;
+  const Layout L = make_layout(w, B, N, 0);
+  if (!workspace || workspace_bytes < L.total) return DCU_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DCU_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Ptrs P{};
+  P.hdr = reinterpret_cast<int*>(ws + L.hdr);
+  P.seq_off = reinterpret_cast<int*>(ws + L.seq_off);
+  P.tile_off = reinterpret_cast<int*>(ws + L.tile_off);
+  P.tile_seq = reinterpret_cast<int*>(ws + L.tile_seq);
+  P.rowmap = reinterpret_cast<int*>(ws + L.rowmap);
+  P.xn = reinterpret_cast<uint16_t*>(ws + L.xn);
+  P.q = reinterpret_cast<uint16_t*>(ws + L.q);
+  P.opart = reinterpret_cast<float*>(ws + L.opart);
+  P.ml = reinterpret_cast<float*>(ws + L.ml);
+  P.rope = reinterpret_cast<float2*>(ws + L.rope);
+  P.rope_dh = w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE ? w->head_dim : 0;
+  P.rope_l2t = P.rope_dh > 0 ? float(log2(double(w->rope_theta))) : 0.0f;
+  const int d = w->d, DH = w->head_dim;
+  // every row (dense plan): RMSNorm with the attention gain, row map, query tiles, rotary table
+  const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
+  {
+    const uint16_t* x = static_cast<const uint16_t*>(x_in);
+    const uint16_t* ga_ = static_cast<const uint16_t*>(w->g_attn);
+#define DCU_GATHER(NC)                                                                        \
+  hipLaunchKernelGGL(k_gather_rmsnorm<NC>, dim3(norm_blocks), dim3(256), 0, s, x, nullptr,    \
+                     nullptr, int(B), int(N), L.M_cap, ga_, d, w->rms_eps, P.xn, P)
+    switch (rms_nc(d, false)) {
+      case 1: DCU_GATHER(1); break;
+      case 2: DCU_GATHER(2); break;
+      case 4: DCU_GATHER(4); break;
+      case 8: DCU_GATHER(8); break;
+      case 16: DCU_GATHER(16); break;
+      default: DCU_GATHER(0); break;
+    }
+#undef DCU_GATHER
+  }
+  DCU_LAUNCH_CHECK();
+  // q = xn W_q^T: the first d rows of the blocked W_qkv (every output column is a Q column, so
+  // the QKV epilogue only writes q rows; the caches are not touched)
+  GemmArgs ga{};
+  ga.part = reinterpret_cast<float*>(ws + L.part);
+  ga.hdr = P.hdr;
+  ga.rowmap = P.rowmap;
+  ga.d = d;
+  ga.A = P.xn;
+  ga.W = static_cast<const uint16_t*>(w->w_qkv);
+  ga.K = d;
+  ga.Nout = d;
+  ga.q = P.q;
+  ga.rope_dh = P.rope_dh;
+  ga.rope = P.rope;
+  if (P.rope_dh > 0) {
+    launch_gemm<EPI_QKV_ROPE>(ga, s);
+    DCU_LAUNCH_CHECK();
+    launch_fixup<EPI_QKV_ROPE>(ga, s, L.M_cap);
+  } else {
+    launch_gemm<EPI_QKV>(ga, s);
+    DCU_LAUNCH_CHECK();
+    launch_fixup<EPI_QKV>(ga, s, L.M_cap);
+  }
+  DCU_LAUNCH_CHECK();
+  // attention of every row over the caches as given; in the dense plan compacted row r is global
+  // row r, so the context rows land in place
+  AttnArgs aa{};
+  aa.q = P.q;
+  aa.kc = static_cast<const uint16_t*>(k_cache);
+  aa.vc = static_cast<const uint16_t*>(v_cache);
+  aa.o = static_cast<uint16_t*>(ctx_out);
+  aa.opart = P.opart;
+  aa.ml = P.ml;
+  aa.hdr = P.hdr;
+  aa.seq_off = P.seq_off;
+  aa.tile_off = P.tile_off;
+  aa.tile_seq = P.tile_seq;
+  aa.N = N;
+  aa.H = w->n_heads;
+  aa.d = d;
+  aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;
+  aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
+  return launch_attention(aa, DH, s);
 }
 
 extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,

@@ -201,6 +201,22 @@ def test_layer_validation():
                                  FAKE, 16, None) == _lib.EWORKSPACE
 
 
+def test_attention_context_validation():
+    L = stc.load()
+
+    def call(desc=None, x=FAKE, k=FAKE, v=FAKE, out=FAKE, B=2, N=64, wsb=1 << 40):
+        return L.dcu_attention_context(ctypes.byref(desc or _desc()), x, B, N, k, v, out, FAKE, wsb,
+                                       None)
+
+    assert call(x=None) == _lib.EINVAL
+    assert call(k=None) == _lib.EINVAL
+    assert call(out=None) == _lib.EINVAL
+    assert call(B=0) == _lib.EINVAL
+    assert call(desc=_desc(layout=0)) == _lib.EUNSUPPORTED
+    assert call(v=ctypes.c_void_p(256 + 8)) == _lib.EUNSUPPORTED
+    assert call(wsb=16) == _lib.EWORKSPACE
+
+
 def test_commit_positions_validation():
     L = stc.load()
     assert L.dllm_commit_positions(None, FAKE, FAKE, 2, 16, 4, FAKE, None) == _lib.EINVAL

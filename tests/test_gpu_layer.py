@@ -360,3 +360,38 @@ def test_v_features_with_the_rotary_layout():
     x = dev_bf16(case.x)
     assert torch.equal(stc.dcu_v_features(plain, x).view(torch.int16),
                        stc.dcu_v_features(rot, x).view(torch.int16))
+
+
+@pytest.mark.parametrize("shape,B,N,theta", [
+    (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 2, 77, 0.0),
+    (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 3, 100, 1e4),
+    (synth.LayerShape(d=512, n_heads=4, head_dim=128, ffn=768), 1, 300, 5e5),
+    (synth.LLADA8B, 1, 1024, 5e5),
+])
+def test_attention_context(shape, B, N, theta):
+    """dcu_attention_context (RMSNorm, W_q, rotary, attention of every row over the caches as
+    given) against the oracle; the caches are read only; the attention-context distance between two
+    steps' contexts against the oracle's distance of the GPU contexts."""
+    from oracle import distance as odist
+    _log(f"attention context d={shape.d} dh={shape.head_dim} B={B} N={N} theta={theta}")
+    case = Case(shape, B, N, seed=shape.d + N + 31, theta=theta)
+    L = case.layer()
+    kc, vc = dev_bf16(case.kc), dev_bf16(case.vc)
+    ctx = stc.dcu_attention_context(L, dev_bf16(case.x), kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(kc), case.kc) and np.array_equal(host_bf16(vc), case.vc)
+    got = synth.bf16_to_f32(host_bf16(ctx)).reshape(B * N, shape.d)
+    ref = olayer.attention_context(case.w, shape.n_heads, shape.head_dim, shape.eps, case.x,
+                                   case.kc, case.vc, theta).reshape(B * N, shape.d)
+    e = rel_l2(got, ref)
+    _log(f"  rel-L2 ctx {e:.2e}")
+    assert e <= TOL
+    # a second step: inputs drifted on a third of the rows
+    x2 = case.x.copy()
+    rows = case.g.choice(B * N, (B * N) // 3, replace=False)
+    flat = x2.reshape(B * N, shape.d)
+    flat[rows] = synth.normal_bf16(case.g, (len(rows), shape.d))
+    ctx2 = stc.dcu_attention_context(L, dev_bf16(x2), kc, vc)
+    dist, _ = stc.dcu_distance(ctx2, ctx)
+    rd, _ = odist.distance_and_mean(host_bf16(ctx2), host_bf16(ctx))
+    assert np.allclose(dist.cpu().numpy(), rd, rtol=1e-5, atol=1e-6)

@@ -265,3 +265,50 @@ def test_rope_layer_rotates_cached_keys_by_row_position_and_leaves_values():
     np.testing.assert_allclose(k1[rows], ol.rope(k0[rows], rows[:, None].astype(float), 50.0),
                                rtol=1e-13, atol=1e-14)
     assert not np.allclose(k1[rows[1:]], k0[rows[1:]])
+
+
+# --- attention context of every row (DyLLM-style feature)
+
+def test_attention_context_matches_torch_attention():
+    """Against torch's scaled_dot_product_attention on the same q (RMSNorm + W_q) and caches."""
+    shape = synth.LayerShape(d=32, n_heads=4, head_dim=8, ffn=48)
+    w = _weights(40, shape, std=0.3)
+    g = synth.rng(400, 41)
+    B, N = 2, 11
+    x = g.standard_normal((B, N, shape.d))
+    kc = g.standard_normal((B, N, shape.n_heads, shape.head_dim))
+    vc = g.standard_normal((B, N, shape.n_heads, shape.head_dim))
+    got = ol.attention_context(w, shape.n_heads, shape.head_dim, shape.eps, x, kc, vc)
+    F = torch.nn.functional
+    tw = {k: torch.tensor(v, dtype=torch.float64) for k, v in w.items()}
+    for b in range(B):
+        xn = F.rms_norm(torch.tensor(x[b]), (shape.d,), tw["g_attn"], shape.eps)
+        q = (xn @ tw["w_qkv"][:shape.d].T).reshape(N, shape.n_heads, shape.head_dim).transpose(0, 1)
+        k = torch.tensor(kc[b]).transpose(0, 1)
+        v = torch.tensor(vc[b]).transpose(0, 1)
+        ref = F.scaled_dot_product_attention(q, k, v).transpose(0, 1).reshape(N, shape.d)
+        np.testing.assert_allclose(got[b], ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_attention_context_closed_forms():
+    """One cached row: every context is that row's value; zero query weights: uniform attention,
+    the mean of the values; rotary embedding at N = 1 changes nothing (position 0)."""
+    w = _weights(42)
+    g = synth.rng(400, 43)
+    x = g.standard_normal((1, 1, S.d))
+    kc = g.standard_normal((1, 1, S.n_heads, S.head_dim))
+    vc = g.standard_normal((1, 1, S.n_heads, S.head_dim))
+    c = ol.attention_context(w, S.n_heads, S.head_dim, S.eps, x, kc, vc)
+    np.testing.assert_allclose(c.reshape(-1), vc.reshape(-1), rtol=1e-14)
+    c2 = ol.attention_context(w, S.n_heads, S.head_dim, S.eps, x, kc, vc, rope_theta=100.0)
+    np.testing.assert_allclose(c2, c, rtol=1e-14)
+    w0 = dict(w)
+    w0["w_qkv"] = np.array(w["w_qkv"], copy=True)
+    w0["w_qkv"][:S.d] = 0.0
+    N = 7
+    x = g.standard_normal((1, N, S.d))
+    kc = g.standard_normal((1, N, S.n_heads, S.head_dim))
+    vc = g.standard_normal((1, N, S.n_heads, S.head_dim))
+    c = ol.attention_context(w0, S.n_heads, S.head_dim, S.eps, x, kc, vc, rope_theta=100.0)
+    np.testing.assert_allclose(c[0], np.broadcast_to(vc[0].mean(axis=0).reshape(-1), (N, S.d)),
+                               rtol=1e-12, atol=1e-13)
