@@ -395,3 +395,32 @@ def test_attention_context(shape, B, N, theta):
     dist, _ = stc.dcu_distance(ctx2, ctx)
     rd, _ = odist.distance_and_mean(host_bf16(ctx2), host_bf16(ctx))
     assert np.allclose(dist.cpu().numpy(), rd, rtol=1e-5, atol=1e-6)
+
+
+def test_maximum_sequence_length_with_rotary():
+    """N = 65536 (the largest sequence the layer accepts), one sequence, 40 rows spread over it
+    (positions up to 65535 for the rotary angles and cache addressing), attention of each over all
+    65536 cached rows."""
+    shape = synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=128)
+    N = 65536
+    _log(f"layer max N {N}")
+    case = Case(shape, 1, N, seed=41, theta=1e4)
+    sel = np.full((1, N), -1, np.int32)
+    rows = np.sort(np.concatenate([case.g.choice(N - 1, 39, replace=False), [N - 1]]))
+    sel[0, :40] = rows
+    cnt = np.array([40], np.int32)
+    (got,) = case.run_gpu(sel, cnt)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, 1, N))
+
+
+def test_maximum_sequence_count():
+    """B = 4096 sequences (the most one call accepts) of N = 8 with ragged counts 0..8: row offsets,
+    per-sequence attention tiles and the scatter for every sequence."""
+    shape = synth.LayerShape(d=64, n_heads=1, head_dim=64, ffn=64)
+    B, N = 4096, 8
+    _log(f"layer max B {B}")
+    case = Case(shape, B, N, seed=43)
+    counts = case.g.integers(0, N + 1, B)
+    sel, cnt = _random_selection(case.g, B, N, counts.tolist())
+    (got,) = case.run_gpu(sel, cnt)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
