@@ -25,7 +25,8 @@ def _log(msg):
 
 # ----------------------------------------------------------------------------- distance
 @pytest.mark.parametrize("G,N,d,frac,sigma", [(3, 37, 8, 0.5, 0.1), (2, 100, 72, 0.3, 0.01),
-                                              (1, 1, 4096, 1.0, 0.01), (5, 64, 640, 0.25, 0.2)])
+                                              (1, 1, 4096, 1.0, 0.01), (5, 64, 640, 0.25, 0.2),
+                                              (1, 5, 16384, 1.0, 0.01), (2, 3, 8200, 0.7, 0.05)])
 def test_distance_bf16_small(G, N, d, frac, sigma):
     _log(f"distance bf16 G={G} N={N} d={d}")
     g = synth.rng(900, G, N, d)
