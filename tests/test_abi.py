@@ -222,3 +222,15 @@ def test_commit_positions_validation():
     assert L.dllm_commit_positions(None, FAKE, FAKE, 2, 16, 4, FAKE, None) == _lib.EINVAL
     assert L.dllm_commit_positions(FAKE, FAKE, FAKE, 2, 16, 0, FAKE, None) == _lib.EINVAL
     assert L.dllm_commit_positions(FAKE, FAKE, None, 2, 16, 4, FAKE, None) == _lib.EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more exits with a message before touching a GPU."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
