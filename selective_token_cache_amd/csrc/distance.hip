@@ -129,10 +129,11 @@ __global__ __launch_bounds__(256) void k_distance_rows(const uint4* __restrict__
   const int lane = threadIdx.x & (kWave - 1);
   const int b = blockIdx.y;
   const int j = blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  // the slot's position is loaded with the count (j < N: in bounds either way), one round trip
+  const int pos = j < N ? sel_idx[int64_t(b) * N + j] : -1;
   int cnt = sel_count[b];
   cnt = cnt < 0 ? 0 : (cnt > N ? N : cnt);
   if (j >= cnt) return;
-  const int pos = sel_idx[int64_t(b) * N + j];
   if (pos < 0 || pos >= N) return;
   const int64_t row = int64_t(b) * N + pos;
   const uint4* a = xc + row * chunks;
