@@ -4,7 +4,6 @@ floor plus largest remainder with ties to the lower layer."""
 from fractions import Fraction
 
 import numpy as np
-import pytest
 
 from oracle import budget as ob
 from workloads import synth

@@ -1,7 +1,6 @@
 """Pins of the oracle's selection: top-B by distance outside the forced windows, united with the
 windows (Dynamic-dLLM notes, Key designs 1 and 2)."""
 import numpy as np
-import pytest
 
 from oracle import select as osel
 from workloads import synth

@@ -2,7 +2,6 @@
 (Key design 2: a token not recomputed at layer l has distance exactly 0 at layer l+1), full budget
 reproducing the dense step, identical inputs selecting only the windows, and determinism."""
 import numpy as np
-import pytest
 
 from oracle import layer as ol
 from oracle import step as ostep
