@@ -48,10 +48,17 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 // lds_addr + 16 i. Written as asm so that the compiler does not add its own (conservative) waits
 // for the LDS writes: completion is tracked explicitly with s_waitcnt vmcnt before each barrier.
 // No output registers; "memory" keeps other memory accesses from moving across it.
+// M0 (the DMA's LDS base) is a register the compiler reserves, hence its -Winline-asm note that a
+// clobbered M0 is not preserved: nothing here needs it preserved. The compiler itself uses M0 only
+// for LDS DMA, GWS, message and indirect register-index instructions, and the kernels that call
+// this function contain none of those (their device assembly shows M0 written only by this asm).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt with vmcnt = n (0..63) and lgkmcnt = 0; expcnt left at its maximum
 template <int n>
