@@ -104,90 +104,185 @@ def stage_flops_bytes(M: int, B: int, N: int):
     }
 
 
-def summarize_profiles(ktrace_dir, fetch_dir, write_dir, bench_json, steps, cmds):
-    """Write the committed profile summaries from rocprofv3 outputs of the commands in `cmds`:
-    the kernel-trace average of the gate/up GEMM over the timed steps' launches (the last
-    steps*32), and its per-launch HBM-side bytes from FETCH_SIZE / WRITE_SIZE scaled by what those
-    counters read for a plain 1 GiB device copy (the runtime's copy kernel) in the same run."""
+# kernels of the step as the profiler names them -> (stage, launches per layer-step (1) or per
+# step (0)); the algorithmic amounts per launch come from stage_flops_bytes and the end-of-step sizes
+PROFILED_KERNELS = [
+    ("k_budget", "budget", 0), ("k_distance<", "distance", 1), ("k_select", "select", 1),
+    ("k_gather_rmsnorm<", "gather_rmsnorm", 1), ("k_gemm<5>", "qkv_scatter", 1),
+    ("k_gemm_fixup<5>", "qkv_fixup", 1), ("k_attn<", "attention", 1),
+    ("k_attn_combine", "attention_combine", 1), ("k_gemm<1>", "o_proj_residual", 1),
+    ("k_gemm_fixup<1>", "o_proj_fixup", 1), ("k_rmsnorm_f32<", "rmsnorm", 1),
+    ("k_gemm<2>", "gate_up_swiglu", 1), ("k_gemm_fixup<2>", "gate_up_fixup", 1),
+    ("k_gemm<3>", "down_residual_scatter", 1), ("k_gemm_fixup<3>", "down_fixup", 1),
+    ("k_confidence<", "confidence", 0), ("k_frechet", "commit", 0),
+]
+
+
+def summarize_profiles(ktrace_dir, fetch_dir, write_dir, mfma_dir, bench_json, steps, cmds):
+    """Write the committed profile summaries from rocprofv3 outputs of the commands in `cmds`
+    (kernel trace, FETCH_SIZE, WRITE_SIZE, MFMA counters; all runs of `bench.py --profile`):
+    per kernel of the step, the kernel-trace average over the timed steps' launches, the HBM-side
+    bytes per launch from FETCH_SIZE / WRITE_SIZE scaled by what those counters read for a plain
+    1 GiB device copy (the runtime's copy kernel) in the same run, the algorithmic bytes and flops
+    per launch, and for the MFMA kernels the hardware MFMA flops and busy fraction."""
     import csv
     import glob
 
     def rows(d, suffix):
         return list(csv.DictReader(open(glob.glob(os.path.join(d, f"*{suffix}"))[0])))
 
-    tag = "k_gemm<2>"
-    kt = [r for r in rows(ktrace_dir, "_kernel_trace.csv") if tag in r["Kernel_Name"]]
-    kt.sort(key=lambda r: int(r["Start_Timestamp"]))
-    timed = kt[-steps * L:]
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
-    avg_us = sum(durs) / len(durs)
+    def match(name, tag):
+        return f"::{tag}" in name
+
     bj = json.loads(open(bench_json).read().strip().splitlines()[-1])
-    stats = rows(ktrace_dir, "_kernel_stats.csv")
-    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    M_l = bj["rows_per_layer"]
+    cfg = bj["config"]
+    B, N = cfg["batch"], cfg["seq_len"]
+    kt_all = rows(ktrace_dir, "_kernel_trace.csv")
+    kt_all.sort(key=lambda r: int(r["Start_Timestamp"]))
 
-    def counter(d, name):
+    def durations(tag, per_layer):
+        ks = [r for r in kt_all if match(r["Kernel_Name"], tag)]
+        n = steps * (L if per_layer else 1)
+        return [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in ks[-n:]]
+
+    def counters(d):
         rs = rows(d, "_counter_collection.csv")
-        g = [float(r["Counter_Value"]) for r in rs if tag in r["Kernel_Name"]][-L:]
-        cp = [float(r["Counter_Value"]) for r in rs
-              if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer") and int(r["Grid_Size"]) >= 131072][-3:]
-        return sum(g) / len(g), sum(cp) / len(cp)
+        by = {}
+        for r in rs:
+            by.setdefault((r["Counter_Name"], r["Kernel_Name"]), []).append(
+                (int(r.get("Dispatch_Id", 0) or 0), float(r["Counter_Value"]), int(r["Grid_Size"])))
+        return rs, by
 
-    f_k, f_cp = counter(fetch_dir, "FETCH_SIZE")
-    w_k, w_cp = counter(write_dir, "WRITE_SIZE")
+    def counter_avg(by, cname, tag, per_layer):
+        vals = []
+        for (c, kname), v in by.items():
+            if c == cname and match(kname, tag):
+                vals += v
+        vals.sort()
+        n = L if per_layer else 1
+        vals = [x[1] for x in vals[-n:]]
+        return (sum(vals) / len(vals)) if vals else None
+
+    def copy_cal(by, cname):
+        vals = []
+        for (c, kname), v in by.items():
+            if c == cname and kname.startswith("__amd_rocclr_copyBuffer"):
+                vals += [x for x in v if x[2] >= 131072]
+        vals.sort()
+        vals = [x[1] for x in vals[-3:]]
+        return sum(vals) / len(vals)
+
+    _, fby = counters(fetch_dir)
+    _, wby = counters(write_dir)
+    _, mby = counters(mfma_dir)
     gib_kib = float(1 << 20)
-    f_scale, w_scale = f_cp / gib_kib, w_cp / gib_kib
-    fetch_b = f_k * 1024 / f_scale
-    write_b = w_k * 1024 / w_scale
+    f_scale = copy_cal(fby, "FETCH_SIZE") / gib_kib
+    w_scale = copy_cal(wby, "WRITE_SIZE") / gib_kib
+    table = []
+    for tag, stage, per_layer in PROFILED_KERNELS:
+        durs = durations(tag, per_layer)
+        if not durs:
+            continue
+        avg_us = sum(durs) / len(durs)
+        if per_layer:
+            amounts = [stage_flops_bytes(int(m), B, N).get(stage, {}) for m in M_l]
+            alg_b = sum(a.get("bytes", 0) for a in amounts) / len(amounts)
+            alg_f = sum(a.get("flops", 0) for a in amounts) / len(amounts)
+        elif stage == "confidence":
+            alg_b, alg_f = B * M_CAND * V * 2, 0
+        elif stage == "commit":
+            alg_b, alg_f = B * M_CAND * 8, 0
+        else:
+            alg_b, alg_f = 2 * 4 * B * L, 0
+        fk = counter_avg(fby, "FETCH_SIZE", tag, per_layer)
+        wk = counter_avg(wby, "WRITE_SIZE", tag, per_layer)
+        traffic = None
+        if fk is not None and wk is not None:
+            traffic = fk * 1024 / f_scale + wk * 1024 / w_scale
+        hw_f = counter_avg(mby, "MfmaFlopsBF16", tag, per_layer)
+        util = counter_avg(mby, "MfmaUtil", tag, per_layer)
+        table.append(dict(kernel=tag.rstrip("<"), stage=stage, launches=len(durs), avg_us=avg_us,
+                          alg_bytes=alg_b, alg_flops=alg_f, traffic=traffic, hw_mfma_flops=hw_f,
+                          mfma_util=util))
+    gu = next(t for t in table if t["stage"] == "gate_up_swiglu")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     traffic = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU), 128x128 tiles",
                "workload": "full 32-layer step, batch 8, N=1024, LLaDA-8B shapes",
                "source_sha256": source_hash(),
-               "fetch_size_kib_per_launch": round(f_k, 1), "write_size_kib_per_launch": round(w_k, 1),
-               "copy_1GiB_fetch_kib": round(f_cp, 1), "copy_1GiB_write_kib": round(w_cp, 1),
                "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-               "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
-               "traffic_bytes_per_launch": int(fetch_b + write_b),
-               "algorithmic_bytes_per_launch": None,
-               "commands": cmds[1:]}
-    M_avg = bj["rows_per_step"] / L
-    alg = 2 * F * D * 2 + M_avg * D * 2 + M_avg * F * 2
-    traffic["algorithmic_bytes_per_launch"] = int(alg)
+               "traffic_bytes_per_launch": int(gu["traffic"]),
+               "algorithmic_bytes_per_launch": int(gu["alg_bytes"]),
+               "commands": cmds[1:3]}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(traffic, f, indent=1)
+    step_us = sum(t["avg_us"] * (L if dict((k[1], k[2]) for k in PROFILED_KERNELS)[t["stage"]] else 1)
+                  for t in table)
     lines = [
+        "# Kernels of the full 32-layer DCU step, batch 8, N=1024 (LLaDA-8B-shaped layers, rotary, bf16)",
+        "",
+        "Commands (run from the repository root; each is `bench.py --profile`: set-up, warm-up and the",
+        "timed steps only):",
+        "",
+        *["    " + c for c in cmds],
+        "",
+        f"Per launch, averaged over the timed region (kernel trace: last {steps} steps; counters: the",
+        "one profiled step). `alg` = the algorithmic amount of the method (rows, weights, caches read",
+        "or written once); `HBM` = FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy in the same run",
+        f"(FETCH_SIZE reads {f_scale:.3f} KiB per KiB copied, WRITE_SIZE {w_scale:.3f}). Rates are algorithmic",
+        "amounts over the trace duration; peaks 8 TB/s HBM, 2.5 PFLOP/s dense bf16 MFMA.",
+        "",
+        "| kernel | stage | launches | avg us | alg MB | HBM MB | HBM/alg | alg GB/s (% of 8 TB/s) "
+        "| alg TFLOP/s (% of 2.5 PF) | MFMA busy % | hw MFMA flops / alg |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for t in table:
+        gbs = t["alg_bytes"] / (t["avg_us"] * 1e-6) / 1e9 if t["alg_bytes"] else None
+        tf = t["alg_flops"] / (t["avg_us"] * 1e-6) / 1e12 if t["alg_flops"] else None
+        lines.append(
+            f"| `{t['kernel']}` | {t['stage']} | {t['launches']} | {t['avg_us']:.2f} | "
+            f"{t['alg_bytes'] / 1e6:.2f} | "
+            + (f"{t['traffic'] / 1e6:.2f} | {t['traffic'] / t['alg_bytes']:.2f} | " if t["traffic"] and t["alg_bytes"] >= 1e6 else (f"{t['traffic'] / 1e6:.2f} | - | " if t["traffic"] else "- | - | "))
+            + (f"{gbs:.0f} ({100 * gbs / HBM_PEAK_GBS:.1f}%) | " if gbs else "- | ")
+            + (f"{tf:.0f} ({100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f}%) | " if tf else "- | ")
+            + (f"{t['mfma_util']:.1f} | " if t["mfma_util"] is not None and t["alg_flops"] else "- | ")
+            + (f"{t['hw_mfma_flops'] / t['alg_flops']:.3f} |" if t["hw_mfma_flops"] and t["alg_flops"] else "- |"))
+    lines += ["", f"Sum of the listed kernels per step: {step_us / 1e3:.2f} ms "
+                  f"(bench wall time per step in the trace run: {bj['ms_per_step']:.2f} ms; the rest is "
+                  "launch gaps).", ""]
+    out = os.path.join(ROOT, "profiles", "kernels_full_step_b8_n1024.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # the roofline kernel's own summary (the bench line's avg_launch_us must agree with it)
+    stats = rows(ktrace_dir, "_kernel_stats.csv")
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    g_lines = [
         "# gate/up projection GEMM (k_gemm<EPI_SWIGLU>) -- full 32-layer DCU step, batch 8, N=1024",
         "",
         "Kernel trace command (run from the repository root):",
         "",
         "    " + cmds[0],
         "",
-        f"Timed-region launches (last {steps} steps x {L} layers = {len(durs)} launches):",
-        f"  rocprofv3 average duration  {avg_us:9.2f} us",
+        f"Timed-region launches (last {steps} steps x {L} layers = {gu['launches']} launches):",
+        f"  rocprofv3 average duration  {gu['avg_us']:9.2f} us",
         f"  bench.py HIP-event average  {bj['roofline']['avg_launch_us']:9.2f} us",
-        f"  algorithmic flops / launch  {bj['roofline']['algorithmic_flops_per_launch']:.4e}",
-        f"  achieved (bench)            {bj['roofline']['achieved']} TFLOP/s of {bj['roofline']['peak']}",
+        f"  algorithmic flops / launch  {gu['alg_flops']:.4e}",
+        f"  achieved (trace)            {gu['alg_flops'] / (gu['avg_us'] * 1e-6) / 1e12:.1f} TFLOP/s of {MFMA_BF16_PEAK_TFLOPS}",
+        f"  achieved (bench events)     {bj['roofline']['achieved']} TFLOP/s",
+        f"  HBM-side traffic / launch   {gu['traffic'] / 1e6:.1f} MB against {gu['alg_bytes'] / 1e6:.1f} MB algorithmic",
         "",
-        "Counter runs:",
-        "",
-        "    " + cmds[1],
-        "    " + cmds[2],
-        "",
-        f"  FETCH_SIZE per launch {f_k:12.1f} KiB; 1 GiB copy reads as {f_cp:12.1f} KiB (scale {f_scale:.4f})",
-        f"  WRITE_SIZE per launch {w_k:12.1f} KiB; 1 GiB copy writes as {w_cp:12.1f} KiB (scale {w_scale:.4f})",
-        f"  traffic per launch    {(fetch_b + write_b) / 1e6:9.1f} MB (fetch {fetch_b / 1e6:.1f}, write {write_b / 1e6:.1f})",
-        f"  algorithmic per launch {alg / 1e6:8.1f} MB (weights 2*F*d*2 B + rows read and written)",
-        "",
-        "Whole-run kernel statistics (includes setup: weight generation, dense cache fill, warm-up):",
+        "Whole-run kernel statistics (includes set-up: weight generation and packing, dense cache fill):",
         "",
         f"  {'kernel':90s} {'calls':>6s} {'avg us':>10s} {'pct':>6s}",
     ]
     for r in stats[:16]:
-        lines.append(f"  {r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['Percentage']):6.2f}")
-    out = os.path.join(ROOT, "profiles", "gemm_gate_up_swiglu_full_step_b8_n1024.md")
-    with open(out, "w") as f:
-        f.write("\n".join(lines) + "\n")
+        g_lines.append(f"  {r['Name'][:90]:90s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                       f"{float(r['Percentage']):6.2f}")
+    out2 = os.path.join(ROOT, "profiles", "gemm_gate_up_swiglu_full_step_b8_n1024.md")
+    with open(out2, "w") as f:
+        f.write("\n".join(g_lines) + "\n")
     print(out)
+    print(out2)
 
 
 def torch_dense_layer(w, x, eps):
@@ -228,8 +323,9 @@ def torch_dense_layer(w, x, eps):
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
+        # ktrace_dir fetch_dir write_dir mfma_dir bench_json steps cmd_trace cmd_fetch cmd_write cmd_mfma
         a = sys.argv[2:]
-        summarize_profiles(a[0], a[1], a[2], a[3], int(a[4]), a[5:8])
+        summarize_profiles(a[0], a[1], a[2], a[3], a[4], int(a[5]), a[6:10])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +339,12 @@ def main():
                     help="row bound passed to the layer calls (default: B * min(N, L * b_layer + window))")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also launch a plain 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--profile", action="store_true",
+                    help="profiler runs: only set-up, warm-up and the timed steps (no side measurements)")
     args = ap.parse_args()
+    if args.profile:
+        args.no_cpu_baseline = args.no_graph = True
+        args.dense_layers = 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the path is measured on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -314,8 +415,8 @@ def main():
         torch.cuda.synchronize()
 
     # host-side bound on the selected rows of one layer call: a sequence's budget for one layer is
-    # at most its whole step budget L * b_layer, plus the window, and never more than N
-    max_rows = args.max_rows if args.max_rows > 0 else B * min(N, L_ * B_LAYER + B_WINDOW)
+    # at most its whole step budget L * b_layer, plus the windows of its keys, and never more than N
+    max_rows = args.max_rows if args.max_rows > 0 else B * min(N, L_ * B_LAYER + N_KEYS * B_WINDOW)
     stages = list(LAYER_STAGES) if wl["layers"] else []
     n_ev_layer = 2 + len(stages) + 1 if wl["layers"] else 3
 
@@ -417,7 +518,7 @@ def main():
             else:
                 roof_ms[l] += e[0].elapsed_time(e[1])
 
-    KI = min(K, 5)
+    KI = 0 if args.profile else min(K, 5)
     ievs = [make_events(True) for _ in range(KI)]
     torch.cuda.synchronize()
     log(f"instrumented {KI} steps")
@@ -439,7 +540,7 @@ def main():
             for i, n in enumerate(names):
                 stage_ms[n] += e[i].elapsed_time(e[i + 1])
     kernels = {}
-    for n in names:
+    for n in names if KI else []:
         per_layer_ms = stage_ms[n] / (KI * L_)
         fb = [stage_flops_bytes(int(m), B, N)[n] for m in M_l]
         flops = sum(x.get("flops", 0) for x in fb) / L_
@@ -452,8 +553,8 @@ def main():
             k["TFLOPps"] = round(flops / (per_layer_ms * 1e-3) / 1e12, 1)
             k["mfma_frac"] = round(k["TFLOPps"] / MFMA_BF16_PEAK_TFLOPS, 3)
         kernels[n] = k
-    if wl["end"]:
-        end_ms = {"confidence": 0.0, "commit": 0.0}
+    end_ms = {"confidence": 0.0, "commit": 0.0}
+    if wl["end"] and KI:
         for it in range(KI):
             e = ievs[it][L_]
             end_ms["confidence"] += e[0].elapsed_time(e[1])
@@ -468,7 +569,7 @@ def main():
     # sequence and device time per call, Frechet at the step's delta and the page's default, the
     # matched factor rule f = 1 - delta, and the threshold rule tau = 0.9
     commit_rules = None
-    if wl["end"]:
+    if wl["end"] and not args.profile:
         c2 = conf.view(B, M_CAND)
         commit_rules = {}
         for name, rule, param in [("frechet_delta_0.1", "frechet", DELTA),
@@ -494,7 +595,7 @@ def main():
     # the V-feature distance (Value vectors recomputed for every row, compared with the V cache)
     # against the input distance the step uses, on layer 0
     vfeat = None
-    if wl["layers"]:
+    if wl["layers"] and not args.profile:
         v_new = torch.empty((B, N, D), dtype=torch.bfloat16, device=dev)
         vcache = vc[0].view(B, N, D)
 
@@ -529,7 +630,7 @@ def main():
     # with N(0, 0.3^2) noise; thresholds start at 0.9 (alpha = beta = 0.1: the page leaves them
     # open); one call streams both [B*256, V] logit matrices
     apd = None
-    if wl["end"]:
+    if wl["end"] and not args.profile:
         R = B * M_CAND
         zprev = wd.drifted_logits(logits, 0.3, CFG)
         tau = torch.empty((R,), dtype=torch.float32, device=dev)
@@ -633,7 +734,7 @@ def main():
         d_ms = sum(e[0].elapsed_time(e[-1]) for e in dev_ev) / n_dense
         d_gu = sum(e[gi].elapsed_time(e[gi + 1]) for e in dev_ev) / n_dense
         # selective layer-step from the timed (uninstrumented) steps, end of step excluded
-        sel_ms = ms_step / L_ - (sum(end_ms.values()) / KI / L_ if wl["end"] else 0.0)
+        sel_ms = ms_step / L_ - (sum(end_ms.values()) / KI / L_ if wl["end"] and KI else 0.0)
         dense_flops = 2.0 * B * N * (4 * D * D + 3 * D * F) + 4.0 * B * N * N * D
         dense = {"layer_ms": round(d_ms, 3), "selective_layer_step_ms": round(sel_ms, 3),
                  "speedup_selective_vs_dense": round(d_ms / sel_ms, 2),
@@ -658,6 +759,17 @@ def main():
         dense["torch_layer_ms"] = round(t_ms, 3)
         dense["speedup_selective_vs_torch_dense"] = round(t_ms / sel_ms, 2)
         torch.cuda.empty_cache()
+
+    # the batch-1 layer (one sequence, budget 32 + a 32-wide window: ~64 rows) against the dense
+    # layer at the same shape, with the step's first-layer weights
+    layer_b1 = None
+    if wl["layers"] and args.workload == "step" and not args.profile:
+        log("batch-1 layer")
+        layer_b1 = batch1_layer(stc, torch, wd, layers[0][0], N, dev)
+    peaks = None
+    if not args.profile:
+        log("measured peaks")
+        peaks = measure_peaks(stc, torch, dev)
 
     if args.calib_copy:
         log("calibration copy")
@@ -726,7 +838,10 @@ def main():
         "recomputed_tokens_per_s": round(rows_step / (ms_step * 1e-3), 1),
         "rows_per_step": rows_step,
         "rows_per_layer_min_max": [int(M_l.min()), int(M_l.max())],
+        "rows_per_layer": [int(m) for m in M_l],
         "kernels": kernels,
+        "layer_b1": layer_b1,
+        "peaks": peaks,
         "commit_rules": commit_rules,
         "apd": apd,
         "v_feature_distance": vfeat,
@@ -738,15 +853,124 @@ def main():
     if not wl["layers"]:
         out["metric"] = "distance+budget+select layer-steps/s at N=1024; % HBM peak"
         out["recomputed_tokens_per_s"] = None
+    if peaks is not None and roofline is not None:
+        # the same achieved rate against what this device's own peak kernel reaches
+        key = "mfma_loop_TFLOPps" if roofline["bound"] == "mfma" else "stream_read_GBps"
+        roofline["measured_peak"] = peaks[key]
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks[key], 4)
     print(json.dumps(out), flush=True)
 
 
+def _event_time_ms(torch, fn, reps, warm=2):
+    """Average device time of fn() over reps back-to-back calls, events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_peaks(stc, torch, dev):
+    """This device's own peaks: a streaming read of 2 GiB (8x the 256 MB last-level cache, so the
+    bytes come from HBM; best of three grid sizes) and a loop of independent bf16 MFMAs."""
+    buf = torch.empty((2 << 30,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros((256,), dtype=torch.int32, device=dev)
+    best = 0.0
+    for grid in (1024, 2048, 4096):
+        ms = _event_time_ms(torch, lambda: stc.dcu_measure_stream_read(buf, grid, sink), 5)
+        best = max(best, buf.numel() / (ms * 1e-3) / 1e9)
+    del buf
+    fs = torch.zeros((256,), dtype=torch.float32, device=dev)
+    best_f = 0.0
+    for grid in (512, 1024):
+        flops = [0]
+
+        def run():
+            flops[0] = stc.dcu_measure_mfma_loop(grid, 2048, fs)
+        ms = _event_time_ms(torch, run, 3)
+        best_f = max(best_f, flops[0] / (ms * 1e-3) / 1e12)
+    return {"stream_read_GBps": round(best, 1), "hbm_nominal_GBps": HBM_PEAK_GBS,
+            "stream_read_frac_of_nominal": round(best / HBM_PEAK_GBS, 3),
+            "mfma_loop_TFLOPps": round(best_f, 1), "mfma_bf16_nominal_TFLOPps": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_loop_frac_of_nominal": round(best_f / MFMA_BF16_PEAK_TFLOPS, 3),
+            "kernels": "dcu_measure_stream_read (2 GiB, 16-byte non-temporal loads, best of grids "
+                       "1024/2048/4096 x 256 threads); dcu_measure_mfma_loop (8 independent "
+                       "v_mfma_f32_16x16x32_bf16 chains per wave, best of 512/1024 workgroups)"}
+
+
+def batch1_layer(stc, torch, wd, layer, N, dev):
+    """One sequence of N tokens through one LLaDA-8B-shaped layer with rotary embedding: the
+    selective layer-step (distance, select with budget 32 and a 32-wide window around one key in
+    [N/2, N), the layer on the ~64 selected rows) against the dense layer (all N rows) at the same
+    shape, both this library; eager and replayed from a HIP graph."""
+    sigma = 0.01 * (1 + 31 / 8)
+    x_cur, x_prev = wd.drift_inputs(1, N, D, 0.3, sigma, 3, 0, device=dev)
+    keys = wd.key_positions(1, 1, N // 2, N, 3, device=dev)
+    kc = torch.empty((1, N, H, DH), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    y = torch.empty((1, N, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((layer.workspace_bytes(1, N, N),), dtype=torch.uint8, device=dev)
+    stc.dcu_selective_layer(layer, x_prev, None, None, kc, vc, y, max_rows=N, workspace=ws)
+    budgets = torch.full((1, 1), 32, dtype=torch.int32, device=dev)
+    dist = torch.empty((1, N), dtype=torch.float32, device=dev)
+    sel = torch.empty((1, N), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1,), dtype=torch.int32, device=dev)
+    mean = torch.empty((1,), dtype=torch.float32, device=dev)
+    max_rows = 32 + B_WINDOW
+
+    def selective():
+        stc.dcu_distance(x_cur, x_prev, dist=dist, want_mean=False)
+        stc.dcu_select(dist, budgets, 0, keys, B_WINDOW, sel_idx=sel, sel_count=cnt, mean=mean)
+        stc.dcu_selective_layer(layer, x_cur, sel, cnt, kc, vc, y, max_rows=max_rows, workspace=ws)
+
+    kd, vd, yd = torch.empty_like(kc), torch.empty_like(vc), torch.empty_like(y)
+
+    def dense():
+        stc.dcu_selective_layer(layer, x_cur, None, None, kd, vd, yd, max_rows=N, workspace=ws)
+
+    t_sel = _event_time_ms(torch, selective, 50)
+    t_dense = _event_time_ms(torch, dense, 20)
+    rows = int(cnt.item())
+    out = {"workload": "one LLaDA-8B-shaped layer with rotary embedding, batch 1, N=%d, budget 32 "
+                       "+ a 32-wide window around one key" % N,
+           "rows": rows, "selective_layer_step_us": round(t_sel * 1e3, 2),
+           "dense_layer_us": round(t_dense * 1e3, 2), "speedup": round(t_dense / t_sel, 2),
+           "layer_steps_per_s": round(1e3 / t_sel, 1),
+           "recomputed_tokens_per_s": round(rows / (t_sel * 1e-3), 1)}
+    try:
+        gs, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gs):
+            selective()
+        with torch.cuda.graph(gd):
+            dense()
+        tg_sel = _event_time_ms(torch, gs.replay, 50)
+        tg_dense = _event_time_ms(torch, gd.replay, 20)
+        out.update({"graph_selective_layer_step_us": round(tg_sel * 1e3, 2),
+                    "graph_dense_layer_us": round(tg_dense * 1e3, 2),
+                    "graph_speedup": round(tg_dense / tg_sel, 2)})
+        del gs, gd
+    except Exception as exc:  # capture is an optional measurement
+        out["graph_error"] = str(exc)[:200]
+    return out
+
+
 def cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, logits, torch):
-    """The numpy oracle, untuned, on a bounded sample of the same workload: a subset of the layers
-    for the whole batch (distance, select, and the selective layer when the workload has one) plus
-    the end of step on 1/8 of the candidate rows; scaled to layer-steps/s of the whole step."""
+    """The numpy oracle, untuned, on a bounded sample of the same workload, on this host's cores:
+    a subset of the layers for the whole batch (distance, select, and the selective layer when the
+    workload has one) plus the end of step on 1/8 of the candidate rows, each timed three times
+    (median); scaled to layer-steps/s of the whole step. BLAS threads = the CPUs this process may
+    run on (sched_getaffinity). The oracle computes in fp64 only (it has no fp32 path)."""
+    import statistics
+
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import budget as obud
     from oracle import confidence as oconf
@@ -756,14 +980,23 @@ def cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, log
     from oracle import select as osel
 
     B, L_ = wl["B"], wl["L"]
+    n_cpu = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
 
     def h16(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     if wl["layers"]:
-        sample_layers = list(range(0, L_, 4)) if wl["N"] <= 1024 else [0, 16]
+        sample_layers = list(range(0, L_, 8)) if wl["N"] <= 1024 else [0, 16]
     else:
-        sample_layers = list(range(L_))
+        sample_layers = list(range(0, L_, 2))
     host = []
     for l in sample_layers:
         w = {k: h16(v) for k, v in weights_of(l).items()} if wl["layers"] else None
@@ -771,32 +1004,38 @@ def cpu_baseline(wl, weights_of, x_cur, x_prev, kc, vc, y, s_prev_dev, keys, log
         host.append((w, h16(x_cur[l]), h16(x_prev[l]), lay))
     s_prev = s_prev_dev.cpu().numpy().T.copy()     # [B, L]
     kp = keys.cpu().numpy()
+    lg = h16(logits[: B * M_CAND // 8]) if wl["end"] else None
     t0 = time.perf_counter()
-    bud = obud.layer_budget(s_prev, B, L_, wl["b_layer"])
-    for (w, xc, xp, lay), l in zip(host, sample_layers):
-        d, _ = odist.distance_and_mean(xc, xp)
-        sel, cnt = osel.select(d, bud, l, kp, B_WINDOW)
-        if lay is not None:
-            olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, *lay, ROPE_THETA)
-    t_layer = (time.perf_counter() - t0) / len(sample_layers)
-    t_end = 0.0
-    if wl["end"]:
-        lg = h16(logits[: B * M_CAND // 8])
-        t1 = time.perf_counter()
-        c, _ = oconf.confidence(lg, V)
-        ofre.frechet_commit(c.reshape(B // 8, M_CAND), None, DELTA)
-        t_end = (time.perf_counter() - t1) * 8
+    per_layer, per_end = [], []
+    with threadpool_limits(limits=n_cpu):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for rep in range(3):
+            t1 = time.perf_counter()
+            bud = obud.layer_budget(s_prev, B, L_, wl["b_layer"])
+            for (w, xc, xp, lay), l in zip(host, sample_layers):
+                d, _ = odist.distance_and_mean(xc, xp)
+                sel, cnt = osel.select(d, bud, l, kp, B_WINDOW)
+                if lay is not None:
+                    olayer.selective_layer(w, H, DH, 1e-5, xc, sel, cnt, *lay, ROPE_THETA)
+            per_layer.append((time.perf_counter() - t1) / len(sample_layers))
+            if wl["end"]:
+                t2 = time.perf_counter()
+                c, _ = oconf.confidence(lg, V)
+                ofre.frechet_commit(c.reshape(B // 8, M_CAND), None, DELTA)
+                per_end.append((time.perf_counter() - t2) * 8)
+    t_layer = statistics.median(per_layer)
+    t_end = statistics.median(per_end) if per_end else 0.0
     t_step = L_ * t_layer + t_end
-    sample_s = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     what = "distance, select, selective layer" if wl["layers"] else "distance, select"
-    end = " plus confidence/commit on 1/8 of the candidate rows" if wl["end"] else ""
+    end = " plus confidence/commit on 1/8 of the candidate rows (x8)" if wl["end"] else ""
     return {"value": round(L_ / t_step, 4), "unit": "layer-steps/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "cpus_available": n_cpu,
+            "path": "fp64 numpy oracle (its only path)",
             "sample": f"numpy fp64 oracle on layers {sample_layers} of the batch-{B} step ({what})"
-                      f"{end}; scaled to the whole {L_}-layer step",
-            "sample_seconds": round(sample_s, 2),
-            "cpu_layer_step_s": round(t_layer, 3)}
+                      f"{end}; median of 3 runs, scaled to the whole {L_}-layer step",
+            "sample_seconds": round(time.perf_counter() - t0, 2),
+            "cpu_layer_step_s": round(t_layer, 3),
+            "cpu_layer_step_s_runs": [round(x, 3) for x in per_layer]}
 
 
 if __name__ == "__main__":

@@ -67,7 +67,8 @@ int dcu_version(void);
  * sequence is split across the L layers in proportion to the previous step's layer means.
  *
  * s_prev  [L, B] fp32 layer means of the previous step, layer-major (each layer's dcu_distance
- *         call writes its B means contiguously), or NULL for "no previous step".
+ *         call writes its B means contiguously), or NULL for "no previous step". A mean is never
+ *         negative (an average of distances in [0, 2]); a negative entry is read as 0.
  * budget  [B, L] int32 out. Each row sums to exactly T: floor of T*s/sum(s) plus one for the
  *         largest remainders (ties to the lower layer), computed in IEEE fp64 in a fixed order.
  *         A NULL s_prev, or a row whose means sum to 0, gives b_layer to every layer.
@@ -233,10 +234,12 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  *
  * x_in      [B, N, d] bf16 layer input (only selected rows are read).
  * sel_idx   [B, N] int32 ascending positions and sel_count [B] int32 (from dcu_select), or both
- *           NULL for every row (dense mode).
+ *           NULL for every row (dense mode). Counts are clamped to [0, N]. A listed position
+ *           outside [0, N) (e.g. a -1 pad) is skipped: nothing is read or written for it, and it
+ *           is not counted in rows_done.
  * max_rows  host-side upper bound on sum(sel_count) used to size the workspace (<= 0: B*N).
- *           If the device counts exceed it, only the first max_rows rows in (sequence, position)
- *           order are recomputed.
+ *           If the device counts exceed it, only the first max_rows entries in (sequence,
+ *           position) order are processed; rows_done shows what was recomputed.
  * k_cache, v_cache  [B, N, n_heads, head_dim] bf16 IN/OUT: selected rows are overwritten before
  *           attention reads the cache; other rows are untouched.
  * y_out     [B, N, d] bf16 IN/OUT: selected rows get the layer output; other rows are untouched.
@@ -244,6 +247,8 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
  *           owned by the caller; its contents on entry do not matter. Calls that share a
  *           workspace must be ordered (same stream): it holds the row map, activations and
  *           split-K partial tiles of one call.
+ * rows_done [B] int32 out, or NULL: the number of rows of each sequence actually recomputed
+ *           (listed positions inside [0, N) among the entries that fit in max_rows).
  * Results are bitwise reproducible for a given device: every reduction runs in a fixed order.
  * Errors: EINVAL on NULL pointers or non-positive sizes, only one of sel_idx/sel_count NULL,
  *         d != n_heads*head_dim, rms_eps < 0, rope_theta not 0 with DCU_WEIGHTS_BLOCKED or not
@@ -255,7 +260,7 @@ size_t dcu_selective_layer_workspace(const dcu_layer* w, int32_t B, int32_t N, i
 int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
                         const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
                         void* k_cache, void* v_cache, void* y_out, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        size_t workspace_bytes, int32_t* rows_done, void* stream);
 
 /*
  * dcu_attention_context -- the attention context of every row of a layer, for an attention-context
@@ -307,8 +312,8 @@ int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, int32_t N, v
 int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
                                const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
                                void* k_cache, void* v_cache, void* y_out, void* workspace,
-                               size_t workspace_bytes, void* stream, void* const* events,
-                               int32_t n_events);
+                               size_t workspace_bytes, int32_t* rows_done, void* stream,
+                               void* const* events, int32_t n_events);
 
 /*
  * dllm_confidence -- confidence and argmax of each candidate position.

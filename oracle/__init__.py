@@ -16,12 +16,14 @@ Sources (web pages about the method; each function cites the part it follows):
   design 2 (selection rule n* = max{n : G_n > delta}, else 1), design 3 (Proposition 4.3 /
   Corollary 4.4 decomposition G_n = F_n + B_n).
 
-Modules: distance, budget, select, layer, confidence, frechet, step (the per-step driver).
+Modules: distance, budget, select, layer (with optional rotary position embedding), confidence,
+frechet, apd (adaptive parallel decoding), step (the per-step driver, open or closed loop).
 
 Parity status: every function is pinned by the tests under tests/test_oracle_*.py (closed forms,
 exact rational or high-precision brute force, library routines, the pages' worked example). The
-internal structure of the transformer layer (pre-norm RMSNorm, no rotary embedding, scale
-1/sqrt(head_dim)) is a reading the pages do not fix: the layer function is pinned as an
-implementation of that reading, but the reading itself is "parity unpinned" by the pages.
+internal structure of the transformer layer (pre-norm RMSNorm, scale 1/sqrt(head_dim), rotary
+embedding of q and k in the rotate-half pairing when a base is given) is a reading the pages do
+not fix: the layer function is pinned as an implementation of that reading, but the reading itself
+is "parity unpinned" by the pages.
 """
-from . import budget, confidence, distance, frechet, layer, select, step  # noqa: F401
+from . import apd, budget, confidence, distance, frechet, layer, select, step  # noqa: F401

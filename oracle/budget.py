@@ -8,7 +8,16 @@ previous step because its step index counts down).
 The page gives a real-valued share. Readings:
 * integer budgets by floor plus largest remainder, ties to the lower layer, in IEEE fp64 with the
   fixed operation order below, so that sum_l b_l == T exactly;
-* with no previous step, or when every previous mean is 0, each layer gets B_layer.
+* with no previous step, or when every previous mean is 0, each layer gets B_layer;
+* a layer mean is an average of distances in [0, 2], so it is never negative; a negative entry is
+  read as 0.
+
+The floors never overshoot T, so only the "add one to the largest remainders" step exists: with
+every s_l >= 0 and finite, the sequential fp64 sum S is at least (1 - (L-1) u) times the exact sum
+(u = 2^-53), and each q_l = fl(fl(T s_l) / S) is at most T s_l (1 + u)^2 / S. Summed over the
+layers this bounds sum_l q_l by T (1 + (L + 2) u) up to higher-order terms, which is below T + 1
+for every T < 2^31 and L <= 1024. The floors are integers summing to at most sum_l q_l, hence to at
+most T: the remainder count R = T - sum_l floor(q_l) is never negative.
 """
 from __future__ import annotations
 
@@ -19,7 +28,7 @@ def layer_budget_row(s_prev: np.ndarray | None, L: int, b_layer: int) -> np.ndar
     T = b_layer * L
     if s_prev is None:
         return np.full(L, b_layer, np.int32)
-    s = [float(np.float32(v)) for v in np.asarray(s_prev, np.float32).reshape(L)]
+    s = [max(float(np.float32(v)), 0.0) for v in np.asarray(s_prev, np.float32).reshape(L)]
     S = 0.0
     for v in s:  # ascending layer order
         S += v
@@ -30,18 +39,11 @@ def layer_budget_row(s_prev: np.ndarray | None, L: int, b_layer: int) -> np.ndar
     r = [q[i] - f[i] for i in range(L)]
     b = [int(x) for x in f]
     R = T - sum(b)
-    if R >= 0:
-        # the R largest remainders get +1; ties to the lower layer
-        order = sorted(range(L), key=lambda i: (-r[i], i))
-        for i in order[:R]:
-            b[i] += 1
-    else:
-        # only fp rounding can make the floors overshoot: take 1 from the -R smallest remainders
-        # among layers with a positive floor; ties to the higher layer
-        cand = [i for i in range(L) if b[i] > 0]
-        order = sorted(cand, key=lambda i: (r[i], -i))
-        for i in order[:-R]:
-            b[i] -= 1
+    assert R >= 0, "the floors cannot overshoot T (see the module docstring)"
+    # the R largest remainders get +1; ties to the lower layer
+    order = sorted(range(L), key=lambda i: (-r[i], i))
+    for i in order[:R]:
+        b[i] += 1
     return np.asarray(b, np.int32)
 
 

@@ -15,6 +15,9 @@ makes the "stuck in the mud" effect of Key design 2 in the Dynamic-dLLM notes ob
 
 The initial cache fill is one dense pass (every row selected) over each layer's cached input; the
 pages do not describe the initial fill, so this is a reading.
+
+``rope_theta`` > 0 runs every layer with rotary position embedding of that base (see
+layer.selective_layer_seq), as the models the pages' diffusion LLMs are built on do.
 """
 from __future__ import annotations
 
@@ -39,14 +42,15 @@ class State:
     s_prev: np.ndarray | None = None   # [B, L] fp32
 
 
-def dense_fill(weights: list, n_heads: int, head_dim: int, eps: float, x_prev: list) -> State:
+def dense_fill(weights: list, n_heads: int, head_dim: int, eps: float, x_prev: list,
+               rope_theta: float = 0.0) -> State:
     L = len(weights)
     B, N, d = np.asarray(x_prev[0]).shape
     kc, vc, ys = [], [], []
     for l in range(L):
         z = np.zeros((B, N, n_heads, head_dim))
         k, v, y = _layer.selective_layer(weights[l], n_heads, head_dim, eps, x_prev[l], None, None,
-                                         z, z.copy(), np.zeros((B, N, d)))
+                                         z, z.copy(), np.zeros((B, N, d)), rope_theta)
         kc.append(k)
         vc.append(v)
         ys.append(y)
@@ -54,7 +58,8 @@ def dense_fill(weights: list, n_heads: int, head_dim: int, eps: float, x_prev: l
 
 
 def dcu_step(state: State, weights: list, n_heads: int, head_dim: int, eps: float, b_layer: int,
-             b_window: int, key_pos: np.ndarray, x_cur: list | None = None, x0=None):
+             b_window: int, key_pos: np.ndarray, x_cur: list | None = None, x0=None,
+             rope_theta: float = 0.0):
     """Runs one step in place on ``state``. Open loop if ``x_cur`` (a per-layer list) is given,
     closed loop from the first-layer input ``x0`` otherwise. Returns a per-layer record."""
     L = len(weights)
@@ -70,7 +75,7 @@ def dcu_step(state: State, weights: list, n_heads: int, head_dim: int, eps: floa
         s[:, l] = mean
         sel, cnt = _select.select(d, budgets, l, key_pos, b_window)
         k, v, y = _layer.selective_layer(weights[l], n_heads, head_dim, eps, X, sel, cnt,
-                                         state.k_cache[l], state.v_cache[l], state.y[l])
+                                         state.k_cache[l], state.v_cache[l], state.y[l], rope_theta)
         state.k_cache[l], state.v_cache[l], state.y[l] = k, v, y
         state.x_prev[l] = X
         rec.append(dict(dist=d, mean=mean, sel_idx=sel, sel_count=cnt, budgets=budgets[:, l]))

@@ -58,14 +58,14 @@ EXPORTS = {
     "dcu_selective_layer_workspace": (ctypes.c_size_t,
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
-                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+                                           _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]),
     "dcu_v_features": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
     "dcu_attention_context": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
                                              _vp, _vp, ctypes.c_size_t, _vp]),
     "dcu_selective_layer_staged": (ctypes.c_int,
                                    [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32, _i32, _vp,
-                                    _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                    _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp,
                                     ctypes.POINTER(_vp), _i32]),
     "dllm_confidence": (ctypes.c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
     "frechet_commit": (ctypes.c_int, [_vp, _vp, _i32, _i32, ctypes.c_double, _vp, _vp, _vp]),
@@ -74,6 +74,9 @@ EXPORTS = {
     "dllm_commit_positions": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "dllm_apd": (ctypes.c_int, [_vp, _vp, _i32, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    # include/dcu_measure.h
+    "dcu_measure_stream_read": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
+    "dcu_measure_mfma_loop": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
 }
 
 
@@ -115,6 +118,16 @@ def _stream(stream):
     return _vp(s.cuda_stream)
 
 
+def _new(shape, dtype, device, stream):
+    """A tensor the binding allocates (an output the caller did not pass, or a workspace). It comes
+    from the caching allocator on the current stream; when the work is enqueued on another stream
+    the block is marked as used there, so it is not handed out again before that work is done."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA/HIP tensor")
@@ -139,7 +152,7 @@ def dcu_budget(s_prev: torch.Tensor | None, B: int, L: int, b_layer: int, out=No
         dev = s_prev.device
     else:
         dev = torch.device("cuda", torch.cuda.current_device())
-    out = torch.empty((B, L), dtype=torch.int32, device=dev) if out is None else out
+    out = _new((B, L), torch.int32, dev, stream) if out is None else out
     _need(out, "budget", torch.int32, (B, L))
     _check("dcu_budget", load().dcu_budget(_p(s_prev), B, L, b_layer, _p(out), _stream(stream)))
     return out
@@ -153,10 +166,10 @@ def dcu_distance(x_cur: torch.Tensor, x_prev: torch.Tensor, dist=None, mean=None
     if x_cur.dim() != 3 or x_cur.dtype not in _DT:
         raise ValueError("x_cur must be [G, N, d] bf16 or fp32")
     G, N, d = x_cur.shape
-    dist = torch.empty((G, N), dtype=torch.float32, device=x_cur.device) if dist is None else dist
+    dist = _new((G, N), torch.float32, x_cur.device, stream) if dist is None else dist
     _need(dist, "dist", torch.float32, (G, N))
     if want_mean and mean is None:
-        mean = torch.empty((G,), dtype=torch.float32, device=x_cur.device)
+        mean = _new((G,), torch.float32, x_cur.device, stream)
     if mean is not None:
         _need(mean, "mean", torch.float32, (G,))
     st = load().dcu_distance(_p(x_cur), _p(x_prev), _DT[x_cur.dtype], G, N, d, _p(dist), _p(mean),
@@ -176,7 +189,7 @@ def dcu_distance_rows(x_cur: torch.Tensor, x_prev: torch.Tensor, sel_idx: torch.
     G, N, d = x_cur.shape
     _need(sel_idx, "sel_idx", torch.int32, (G, N))
     _need(sel_count, "sel_count", torch.int32, (G,))
-    dist = torch.empty((G, N), dtype=torch.float32, device=x_cur.device) if dist is None else dist
+    dist = _new((G, N), torch.float32, x_cur.device, stream) if dist is None else dist
     _need(dist, "dist", torch.float32, (G, N))
     st = load().dcu_distance_rows(_p(x_cur), _p(x_prev), _DT[x_cur.dtype], G, N, d, _p(sel_idx),
                                   _p(sel_count), _p(dist), int(bool(roll)), _stream(stream))
@@ -200,8 +213,8 @@ def dcu_select(dist: torch.Tensor, budgets: torch.Tensor, layer: int, key_pos: t
         if key_pos.dim() != 2 or key_pos.shape[0] != B:
             raise ValueError("key_pos must be [B, P]")
         P = key_pos.shape[1]
-    sel_idx = torch.empty((B, N), dtype=torch.int32, device=dist.device) if sel_idx is None else sel_idx
-    sel_count = torch.empty((B,), dtype=torch.int32, device=dist.device) if sel_count is None else sel_count
+    sel_idx = _new((B, N), torch.int32, dist.device, stream) if sel_idx is None else sel_idx
+    sel_count = _new((B,), torch.int32, dist.device, stream) if sel_count is None else sel_count
     _need(sel_idx, "sel_idx", torch.int32, (B, N))
     _need(sel_count, "sel_count", torch.int32, (B,))
     if mean is not None:
@@ -219,7 +232,7 @@ def dcu_pack_weights(w: torch.Tensor, out: torch.Tensor | None = None, stream=No
     if w.dim() != 2:
         raise ValueError("w must be a 2-D [rows, cols] matrix")
     if out is None:
-        out = torch.empty_like(w)
+        out = _new(tuple(w.shape), w.dtype, w.device, stream)
     _need(out, "out", torch.bfloat16, tuple(w.shape))
     _check("dcu_pack_weights",
            load().dcu_pack_weights(_p(w), w.shape[0], w.shape[1], _p(out), _stream(stream)))
@@ -235,7 +248,7 @@ def dcu_pack_gate_up(w_gate: torch.Tensor, w_up: torch.Tensor, out: torch.Tensor
     _need(w_up, "w_up", torch.bfloat16, tuple(w_gate.shape))
     F, d = w_gate.shape
     if out is None:
-        out = torch.empty((2 * F, d), dtype=torch.bfloat16, device=w_gate.device)
+        out = _new((2 * F, d), torch.bfloat16, w_gate.device, stream)
     _need(out, "out", torch.bfloat16, (2 * F, d))
     _check("dcu_pack_gate_up", load().dcu_pack_gate_up(_p(w_gate), _p(w_up), F, d, _p(out),
                                                        _stream(stream)))
@@ -250,7 +263,7 @@ def dcu_pack_qkv(w_qkv: torch.Tensor, head_dim: int, out: torch.Tensor | None = 
     if w_qkv.dim() != 2 or w_qkv.shape[0] != 3 * w_qkv.shape[1]:
         raise ValueError("w_qkv must be a [3d, d] matrix")
     if out is None:
-        out = torch.empty_like(w_qkv)
+        out = _new(tuple(w_qkv.shape), w_qkv.dtype, w_qkv.device, stream)
     _need(out, "out", torch.bfloat16, tuple(w_qkv.shape))
     _check("dcu_pack_qkv", load().dcu_pack_qkv(_p(w_qkv), w_qkv.shape[1], head_dim, _p(out),
                                                _stream(stream)))
@@ -292,9 +305,11 @@ LAYER_STAGES = ("gather_rmsnorm", "qkv_scatter", "qkv_fixup", "attention",
 
 def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_cache, v_cache,
                         y_out, max_rows: int = 0, workspace: torch.Tensor | None = None,
-                        stream=None, events=None):
+                        stream=None, events=None, rows_done: torch.Tensor | None = None):
     """Recompute the selected rows in place (k_cache, v_cache, y_out are in/out).
 
+    rows_done: optional [B] int32 out, the rows of each sequence actually recomputed (listed
+    positions inside [0, N) that fit in max_rows).
     events: optional sequence of len(LAYER_STAGES) + 1 torch.cuda.Event(enable_timing=True) or
     None; event 0 is recorded before the first kernel and event i after stage i, on the library's
     stream (dcu_selective_layer_staged); a None entry skips that mark."""
@@ -310,15 +325,17 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
     if sel_idx is not None:
         _need(sel_idx, "sel_idx", torch.int32, (B, N))
         _need(sel_count, "sel_count", torch.int32, (B,))
+    if rows_done is not None:
+        _need(rows_done, "rows_done", torch.int32, (B,))
     need = layer.workspace_bytes(B, N, max_rows)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+        workspace = _new((max(need, 1),), torch.uint8, x_in.device, stream)
     _need(workspace, "workspace", torch.uint8)
     if events is None:
         st = load().dcu_selective_layer(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
                                         _p(sel_count), B, N, max_rows, _p(k_cache), _p(v_cache),
                                         _p(y_out), _p(workspace), workspace.numel(),
-                                        _stream(stream))
+                                        _p(rows_done), _stream(stream))
         _check("dcu_selective_layer", st)
     else:
         if len(events) < len(LAYER_STAGES) + 1:
@@ -327,8 +344,8 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
         st = load().dcu_selective_layer_staged(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
                                                _p(sel_count), B, N, max_rows, _p(k_cache),
                                                _p(v_cache), _p(y_out), _p(workspace),
-                                               workspace.numel(), _stream(stream), arr,
-                                               len(events))
+                                               workspace.numel(), _p(rows_done), _stream(stream),
+                                               arr, len(events))
         _check("dcu_selective_layer_staged", st)
     return k_cache, v_cache, y_out
 
@@ -340,8 +357,8 @@ def dllm_confidence(logits: torch.Tensor, V: int | None = None, conf=None, token
         raise ValueError("logits must be [R, ld] bf16 or fp32")
     R, ld = logits.shape
     V = ld if V is None else V
-    conf = torch.empty((R,), dtype=torch.float32, device=logits.device) if conf is None else conf
-    token = torch.empty((R,), dtype=torch.int32, device=logits.device) if token is None else token
+    conf = _new((R,), torch.float32, logits.device, stream) if conf is None else conf
+    token = _new((R,), torch.int32, logits.device, stream) if token is None else token
     _need(conf, "conf", torch.float32, (R,))
     _need(token, "token", torch.int32, (R,))
     st = load().dllm_confidence(_p(logits), _DT[logits.dtype], R, V, ld, _p(conf), _p(token),
@@ -357,8 +374,8 @@ def frechet_commit(conf: torch.Tensor, delta: float, m_valid: torch.Tensor | Non
     B, m = conf.shape
     if m_valid is not None:
         _need(m_valid, "m_valid", torch.int32, (B,))
-    n_commit = torch.empty((B,), dtype=torch.int32, device=conf.device) if n_commit is None else n_commit
-    order = torch.empty((B, m), dtype=torch.int32, device=conf.device) if order is None else order
+    n_commit = _new((B,), torch.int32, conf.device, stream) if n_commit is None else n_commit
+    order = _new((B, m), torch.int32, conf.device, stream) if order is None else order
     _need(n_commit, "n_commit", torch.int32, (B,))
     _need(order, "order", torch.int32, (B, m))
     st = load().frechet_commit(_p(conf), _p(m_valid), B, m, float(delta), _p(n_commit), _p(order),
@@ -385,8 +402,8 @@ def dllm_commit(conf: torch.Tensor, rule: str, param: float = 0.0, m_valid: torc
         tau = None
     if m_valid is not None:
         _need(m_valid, "m_valid", torch.int32, (B,))
-    n_commit = torch.empty((B,), dtype=torch.int32, device=conf.device) if n_commit is None else n_commit
-    order = torch.empty((B, m), dtype=torch.int32, device=conf.device) if order is None else order
+    n_commit = _new((B,), torch.int32, conf.device, stream) if n_commit is None else n_commit
+    order = _new((B, m), torch.int32, conf.device, stream) if order is None else order
     _need(n_commit, "n_commit", torch.int32, (B,))
     _need(order, "order", torch.int32, (B, m))
     st = load().dllm_commit(_p(conf), _p(m_valid), B, m, COMMIT_RULES[rule], float(param), _p(tau),
@@ -409,8 +426,8 @@ def dllm_apd(logits: torch.Tensor, logits_prev: torch.Tensor | None, V: int, alp
     _need(tau, "tau", torch.float32, (R,))
     _need(zmax, "zmax", torch.float32, (R,))
     dev_ = logits.device
-    conf = torch.empty((R,), dtype=torch.float32, device=dev_) if conf is None else conf
-    token = torch.empty((R,), dtype=torch.int32, device=dev_) if token is None else token
+    conf = _new((R,), torch.float32, dev_, stream) if conf is None else conf
+    token = _new((R,), torch.int32, dev_, stream) if token is None else token
     _need(conf, "conf", torch.float32, (R,))
     _need(token, "token", torch.int32, (R,))
     for name, t in (("c_conc", c_conc), ("h_instab", h_instab)):
@@ -430,11 +447,11 @@ def dcu_v_features(layer: Layer, x_in: torch.Tensor, v_out=None, workspace=None,
     B, N, d = x_in.shape
     if d != layer.d:
         raise ValueError("x_in width does not match the layer")
-    v_out = torch.empty_like(x_in) if v_out is None else v_out
+    v_out = _new(tuple(x_in.shape), x_in.dtype, x_in.device, stream) if v_out is None else v_out
     _need(v_out, "v_out", torch.bfloat16, (B, N, d))
     need = layer.workspace_bytes(B, N, B * N)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+        workspace = _new((max(need, 1),), torch.uint8, x_in.device, stream)
     _need(workspace, "workspace", torch.uint8)
     st = load().dcu_v_features(ctypes.byref(layer.desc), _p(x_in), B, N, _p(v_out), _p(workspace),
                                workspace.numel(), _stream(stream))
@@ -453,11 +470,11 @@ def dcu_attention_context(layer: Layer, x_in: torch.Tensor, k_cache: torch.Tenso
         raise ValueError("x_in width does not match the layer")
     _need(k_cache, "k_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
     _need(v_cache, "v_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
-    ctx_out = torch.empty_like(x_in) if ctx_out is None else ctx_out
+    ctx_out = _new(tuple(x_in.shape), x_in.dtype, x_in.device, stream) if ctx_out is None else ctx_out
     _need(ctx_out, "ctx_out", torch.bfloat16, (B, N, d))
     need = layer.workspace_bytes(B, N, B * N)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x_in.device)
+        workspace = _new((max(need, 1),), torch.uint8, x_in.device, stream)
     _need(workspace, "workspace", torch.uint8)
     st = load().dcu_attention_context(ctypes.byref(layer.desc), _p(x_in), B, N, _p(k_cache),
                                       _p(v_cache), _p(ctx_out), _p(workspace), workspace.numel(),
@@ -473,9 +490,29 @@ def dllm_commit_positions(order: torch.Tensor, n_commit: torch.Tensor, slot_pos:
     B, m = order.shape
     _need(n_commit, "n_commit", torch.int32, (B,))
     _need(slot_pos, "slot_pos", torch.int32, (B, m))
-    key_pos = torch.empty((B, P), dtype=torch.int32, device=order.device) if key_pos is None else key_pos
+    key_pos = _new((B, P), torch.int32, order.device, stream) if key_pos is None else key_pos
     _need(key_pos, "key_pos", torch.int32, (B, P))
     st = load().dllm_commit_positions(_p(order), _p(n_commit), _p(slot_pos), B, m, P, _p(key_pos),
                                       _stream(stream))
     _check("dllm_commit_positions", st)
     return key_pos
+
+
+def dcu_measure_stream_read(buf: torch.Tensor, grid: int, sink: torch.Tensor, stream=None):
+    """One streaming read of every byte of buf (include/dcu_measure.h)."""
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32)
+    _check("dcu_measure_stream_read",
+           load().dcu_measure_stream_read(_p(buf), buf.numel() * buf.element_size(), int(grid),
+                                          _p(sink), _stream(stream)))
+
+
+def dcu_measure_mfma_loop(grid: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """grid x 4 waves x iters x 8 bf16 MFMAs of 16 x 16 x 32 (include/dcu_measure.h); returns the
+    flop count."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < 256:
+        raise ValueError("sink must hold 256 floats")
+    _check("dcu_measure_mfma_loop",
+           load().dcu_measure_mfma_loop(int(grid), int(iters), _p(sink), _stream(stream)))
+    return int(grid) * 4 * int(iters) * 8 * 16 * 16 * 32 * 2

@@ -3,7 +3,8 @@
     python -m selective_token_cache_amd.build [--jobs N]
 
 Compiles every HIP source under csrc/ for gfx950 and links the shared library next to this file.
-Object files go to <repo>/_build/ (not versioned).
+Object files go to <repo>/_build/ (not versioned). The device assembly of the kernels that drive the
+LDS DMA from inline asm is listed and checked for compiler uses of M0 (see check_m0).
 """
 from __future__ import annotations
 
@@ -11,6 +12,7 @@ import argparse
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -46,12 +48,73 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Kernels that issue the LDS DMA through the inline-asm helper in gemm.h, which writes M0 (the DMA's
+# LDS base) itself. M0 is reserved by the compiler, so it neither saves it nor knows that the asm
+# changed it: these kernels are only correct if the compiler never relies on M0 in them. The build
+# checks that in their gfx950 assembly.
+DMA_SOURCES = ["layer.hip"]
+# instructions that read M0 without naming it
+_IMPLICIT_M0 = re.compile(r"^\s*(s_sendmsg|s_sendmsghalt|s_movrel|v_movrel|ds_gws|v_interp|"
+                          r"ds_append|ds_consume|ds_ordered_count|buffer_load_\w+\s.*\blds\b|"
+                          r"global_load_lds_(?!dwordx4))")
+
+
+def _device_asm(src: str) -> str:
+    out = os.path.join(BUILD, os.path.basename(src) + ".gfx950.s")
+    cmd = [HIPCC, *HIP_FLAGS, "--cuda-device-only", "-S", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"assembly listing failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
+def check_m0(asm: str) -> list[str]:
+    """Problems with M0 in the functions of a gfx950 assembly listing that use the LDS DMA: every
+    write of M0 must be the helper's own `s_mov_b32 m0, sN` directly followed by its
+    global_load_lds_dwordx4, and no instruction may read M0 otherwise (explicitly or implicitly)."""
+    funcs, cur, name = [], [], None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            if name:
+                funcs.append((name, cur))
+            name, cur = m.group(1), []
+        elif name:
+            code = line.split(";", 1)[0].strip()
+            if code and not code.startswith(".") and not code.endswith(":"):
+                cur.append(code)
+    if name:
+        funcs.append((name, cur))
+    bad = []
+    for name, ins in funcs:
+        if not any(i.startswith("global_load_lds_dwordx4") for i in ins):
+            continue
+        for k, i in enumerate(ins):
+            if re.search(r"\bm0\b", i):
+                ok = (re.fullmatch(r"s_mov_b32 m0, s\d+", i) is not None and k + 1 < len(ins)
+                      and ins[k + 1].startswith("global_load_lds_dwordx4"))
+                if not ok:
+                    bad.append(f"{name}: M0 used by the compiler: {i}")
+            elif i.startswith("global_load_lds_dwordx4"):
+                if k == 0 or not re.fullmatch(r"s_mov_b32 m0, s\d+", ins[k - 1]):
+                    bad.append(f"{name}: LDS DMA without its M0 write: {i}")
+            elif _IMPLICIT_M0.match(i):
+                bad.append(f"{name}: instruction reading M0: {i}")
+    return bad
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(8, os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        asm_jobs = [ex.submit(_device_asm, os.path.join(CSRC, f)) for f in DMA_SOURCES]
         objs = list(ex.map(_compile, srcs))
+        listings = [j.result() for j in asm_jobs]
+    for path in listings:
+        problems = check_m0(open(path).read())
+        if problems:
+            raise RuntimeError("M0 check failed in " + path + ":\n  " + "\n  ".join(problems[:20]))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,6 +7,10 @@
 // the lower layer) in IEEE fp64 with a fixed operation order: S summed sequentially in ascending
 // layer order, q_l = (T*s_l)/S, r_l = q_l - floor(q_l). Every step is exactly rounded and done in
 // the same order as a sequential CPU evaluation, so the result is bit-for-bit reproducible.
+// A mean is an average of distances in [0, 2]; a negative entry is read as 0. With every s_l >= 0
+// the floors never sum past T (S is at least (1 - (L-1) 2^-53) times the exact sum and each q_l at
+// most T s_l (1 + 2^-53)^2 / S, so sum_l q_l < T + 1 for T < 2^31, L <= 1024), hence the only
+// correction is +1 on the T - sum floor(q_l) largest remainders.
 // One workgroup per sequence, one thread per layer; latency-bound (L <= 1024 values).
 #include "common.h"
 
@@ -19,7 +23,6 @@ __global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_pre
                                                  int b_layer, int32_t* __restrict__ budget) {
   __shared__ float s_s[1024];
   __shared__ double s_r[1024];
-  __shared__ int s_f[1024];
   __shared__ double s_S;
   __shared__ int s_scan[17];
   const int b = blockIdx.x;
@@ -30,7 +33,10 @@ __global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_pre
     if (l < L) out[l] = b_layer;
     return;
   }
-  if (l < L) s_s[l] = s_prev[int64_t(l) * B + b];  // layer-major [L, B]
+  if (l < L) {
+    const float v = s_prev[int64_t(l) * B + b];  // layer-major [L, B]
+    s_s[l] = v > 0.0f ? v : 0.0f;
+  }
   __syncthreads();
   if (l == 0) {
     double S = 0.0;
@@ -51,26 +57,16 @@ __global__ __launch_bounds__(1024) void k_budget(const float* __restrict__ s_pre
     r = q - fl;
     f = int(fl);
     s_r[l] = r;
-    s_f[l] = f;
   }
   const int sumf = block_sum_int(l < L ? f : 0, s_scan);  // includes a __syncthreads
-  const int R = T - sumf;
+  const int R = T - sumf;                                  // >= 0 (see above)
   if (l < L) {
-    if (R >= 0) {
-      int rank = 0;
-      for (int k = 0; k < L; ++k) {
-        const double rk = s_r[k];
-        rank += (rk > r || (rk == r && k < l)) ? 1 : 0;
-      }
-      if (rank < R) f += 1;
-    } else if (f > 0) {
-      int rank = 0;
-      for (int k = 0; k < L; ++k) {
-        const double rk = s_r[k];
-        rank += (s_f[k] > 0 && (rk < r || (rk == r && k > l))) ? 1 : 0;
-      }
-      if (rank < -R) f -= 1;
+    int rank = 0;
+    for (int k = 0; k < L; ++k) {
+      const double rk = s_r[k];
+      rank += (rk > r || (rk == r && k < l)) ? 1 : 0;
     }
+    if (rank < R) f += 1;
     out[l] = f;
   }
 }

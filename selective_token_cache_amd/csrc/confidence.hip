@@ -7,7 +7,7 @@
 //  * one 512-thread workgroup per row; each thread walks its 16-byte chunks in increasing index
 //    order with 4 chunks in flight, keeping a running (max, sum of exp, argmax) triple;
 //  * a chunk's 8 exponentials are summed in fp32 and added into an fp64 running sum, rescaled only
-//    when the running max grows; exp is the hardware exp2 with a log2(e) pre-scale;
+//    when the running max grows; exp(v - m) is the hardware exp2 of (v - m) * log2(e);
 //  * the argmax keeps the first (lowest) index reaching the max: per thread chunks are visited in
 //    increasing order and only a strictly larger chunk max moves it; across threads equal maxima
 //    resolve to the smaller index;
@@ -59,10 +59,11 @@ __device__ __forceinline__ void absorb(Tri& t, const float (&v)[kElems], int bas
     t.idx = base + first;
   }
   if (t.m == -INFINITY) return;
-  const float mb = t.m * kLog2e;
+  // exp(v - m) as exp2((v - m) log2 e): the difference is taken first, so the maximum's own term
+  // is exactly 1 and no rounding of m log2 e scales every term (a bias growing with |m|)
   float cs = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kElems; ++j) cs += __builtin_amdgcn_exp2f(fmaf(v[j], kLog2e, -mb));
+  for (int j = 0; j < kElems; ++j) cs += __builtin_amdgcn_exp2f((v[j] - t.m) * kLog2e);
   t.s += double(cs);
 }
 

@@ -51,7 +51,8 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 // M0 (the DMA's LDS base) is a register the compiler reserves, hence its -Winline-asm note that a
 // clobbered M0 is not preserved: nothing here needs it preserved. The compiler itself uses M0 only
 // for LDS DMA, GWS, message and indirect register-index instructions, and the kernels that call
-// this function contain none of those (their device assembly shows M0 written only by this asm).
+// this function contain none of those: the build lists their gfx950 assembly and fails unless every
+// M0 write there is this asm's, directly followed by its DMA, and nothing else reads M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {

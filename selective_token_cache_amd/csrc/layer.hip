@@ -228,27 +228,47 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
       if (off[mid] <= r) lo = mid; else hi = mid - 1;
     }
     const int b = lo, j = r - off[b];
-    const int grow = b * N + (sel_idx ? sel_idx[int64_t(b) * N + j] : j);
+    const int pos = sel_idx ? sel_idx[int64_t(b) * N + j] : j;
+    // a listed position outside [0, N) is skipped: its row map entry is -1, its normalised row is
+    // zero, and every later stage leaves the caches and the output alone for it
+    const bool valid = pos >= 0 && pos < N;
+    const int grow = valid ? b * N + pos : -1;
     if (lane == 0) P.rowmap[r] = grow;
     if (P.rope_dh > 0) {  // (cos, sin) of the row's rotation angles, read by the QKV epilogue
-      const float pos = float(grow - b * N);
       for (int i = lane; i < P.rope_dh / 2; i += kWave) {
-        float sn, cs;
-        sincosf(rope_angle(pos, i, P.rope_dh, P.rope_l2t), &sn, &cs);
+        float sn = 0.0f, cs = 1.0f;
+        if (valid) sincosf(rope_angle(float(pos), i, P.rope_dh, P.rope_l2t), &sn, &cs);
         P.rope[int64_t(r) * (P.rope_dh / 2) + i] = make_float2(cs, sn);
       }
     }
-    rms_row<NC, false>(x + int64_t(grow) * d, gain, d, eps, out + int64_t(r) * d, lane);
+    if (valid) {
+      rms_row<NC, false>(x + int64_t(grow) * d, gain, d, eps, out + int64_t(r) * d, lane);
+    } else {
+      for (int g = lane; g < d / 8; g += kWave)
+        reinterpret_cast<uint4*>(out + int64_t(r) * d)[g] = make_uint4(0, 0, 0, 0);
+    }
   }
 }
 
-// RMSNorm of the fp32 rows a -> bf16, one wave per row
+// RMSNorm of the fp32 rows a -> bf16, one wave per row. With rows_done, also the number of rows of
+// each sequence that the layer recomputes (its compacted rows with a valid position; the row map
+// is complete once the gather kernel has run, which precedes this kernel on the stream).
 template <int NC>
 __global__ __launch_bounds__(256) void k_rmsnorm_f32(const float* __restrict__ a,
                                                      const int* __restrict__ hdr,
                                                      const uint16_t* __restrict__ gain, int d,
-                                                     float eps, uint16_t* __restrict__ out) {
+                                                     float eps, uint16_t* __restrict__ out,
+                                                     int32_t* __restrict__ rows_done, int B,
+                                                     const int* __restrict__ seq_off,
+                                                     const int* __restrict__ rowmap) {
   const int M = hdr[kHdrM];
+  if (rows_done) {
+    for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x) {
+      int n = 0;
+      for (int r = seq_off[b]; r < seq_off[b + 1]; ++r) n += rowmap[r] >= 0 ? 1 : 0;
+      rows_done[b] = n;
+    }
+  }
   const int lane = threadIdx.x & (kWave - 1);
   for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4)
     rms_row<NC, true>(a + int64_t(r) * d, gain, d, eps, out + int64_t(r) * d, lane);
@@ -281,6 +301,7 @@ struct GemmArgs {
 __device__ __forceinline__ void store_qkv(const GemmArgs& g, int m, int64_t grow, int n, float w0,
                                           float w1, float w2, float w3) {
   const int part = n / g.d, col = n - part * g.d;
+  if (part != 0 && grow < 0) return;  // a skipped position: the caches keep their rows
   uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
   uint2 st;
   st.x = pack_bf2(w0, w1);
@@ -304,6 +325,7 @@ __device__ __forceinline__ float4 rope_cs(const GemmArgs& g, int m, int n, int w
 __device__ __forceinline__ void store_qkv_rope(const GemmArgs& g, int m, int64_t grow, int n,
                                                float4 x, float4 y, float4 cs0, float4 cs1) {
   const int part = n / g.d, col = n - part * g.d;
+  if (part != 0 && grow < 0) return;  // a skipped position: the caches keep their rows
   uint16_t* dst = part == 0 ? g.q + int64_t(m) * g.d : (part == 1 ? g.kc : g.vc) + grow * g.d;
   uint2 a, b;
   if (part == 2) {
@@ -501,6 +523,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         for (int fn = 0; fn < C::FN; ++fn) {
           const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
           if (n >= g.Nout) continue;
+          if (grow[fm] < 0) continue;  // a skipped position: the output keeps its row
           const gemm::f32x4 v = acc[fm][fn];
           const float4 p = opnd[fm][fn];
           uint2 st;
@@ -524,7 +547,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         if constexpr (EPI == EPI_QKV) {
           store_qkv(g, m, grow, n, v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_RESID) {
-          const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+          // a skipped position has no input row: its (unused) residual is taken as 0
+          const uint2 xr = grow >= 0 ? *reinterpret_cast<const uint2*>(g.x + grow * g.d + n)
+                                     : make_uint2(0u, 0u);
           float4 o;
           o.x = bf_lo(xr.x) + v[0];
           o.y = bf_hi(xr.x) + v[1];
@@ -532,6 +557,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
           o.w = bf_hi(xr.y) + v[3];
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
         } else {  // EPI_VPROJ
+          if (grow < 0) continue;
           uint2 st;
           st.x = pack_bf2(v[0], v[1]);
           st.y = pack_bf2(v[2], v[3]);
@@ -736,15 +762,18 @@ __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) 
           store_qkv_rope(g, m, grow, np, w, v[u][NV - 1], rope_cs(g, m, np, 0),
                          rope_cs(g, m, np, 1));
         } else if constexpr (EPI == EPI_RESID) {
-          const uint2 xr = *reinterpret_cast<const uint2*>(g.x + grow * g.d + n);
+          const uint2 xr = grow >= 0 ? *reinterpret_cast<const uint2*>(g.x + grow * g.d + n)
+                                     : make_uint2(0u, 0u);
           *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) =
               make_float4(bf_lo(xr.x) + w.x, bf_hi(xr.x) + w.y, bf_lo(xr.y) + w.z, bf_hi(xr.y) + w.w);
         } else if constexpr (EPI == EPI_VPROJ) {
+          if (grow < 0) continue;
           uint2 st;
           st.x = pack_bf2(w.x, w.y);
           st.y = pack_bf2(w.z, w.w);
           *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
         } else {  // EPI_DOWN
+          if (grow < 0) continue;  // a skipped position: the output keeps its row
           const float4 ar = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
           uint2 st;
           st.x = pack_bf2(ar.x + w.x, ar.y + w.y);
@@ -822,6 +851,9 @@ constexpr int kAttnMaxUnits = 2 * kAttnWgs * 256;  // 2 * (attention workgroups 
 struct AttnPlan {
   int full, rem, S, kps;
 };
+
+// Most key ranges an item is split into: ranges of at least 128 keys, at most 16
+inline int attn_s_max(int N) { return N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1; }
 
 __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
   const int whole = (N + kKB - 1) / kKB * kKB;
@@ -1207,11 +1239,19 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   L.o = take(2 * M * d);
   L.a = take(4 * M * d);
   L.h = take(2 * M * F);
-  // split tail partials: at most 2 * (resident workgroups) tile segments of 128 x 128 fp32
-  L.part = take(size_t(4) * 2 * (2 * kCUs) * CfgSmall::BM * CfgSmall::BN);
-  // attention split units: [kAttnMaxUnits][kQTile][head_dim] fp32 and [kAttnMaxUnits][kQTile][2]
-  L.opart = take(size_t(4) * kAttnMaxUnits * kQTile * w->head_dim);
-  L.ml = take(size_t(4) * kAttnMaxUnits * kQTile * 2);
+  // split tail partials: at most 2 * (resident workgroups) tile segments of 128 x 128 fp32; with a
+  // row capacity of at most 64 every device row count takes the 64 x 64 tiles, whose weight-streaming
+  // split keeps at most one segment per resident workgroup
+  L.part = L.M_cap <= CfgSkinny::BM
+               ? take(size_t(4) * (2 * kCUs) * CfgSkinny::BM * CfgSkinny::BN)
+               : take(size_t(4) * 2 * (2 * kCUs) * CfgSmall::BM * CfgSmall::BN);
+  // attention split units: [units][kQTile][head_dim] fp32 and [units][kQTile][2]. A split plan
+  // cuts each of at most Tq_max * n_heads items into at most S_max key ranges, and never makes
+  // more than kAttnMaxUnits units
+  const int64_t plan_units = int64_t(L.Tq_max) * w->n_heads * attn_s_max(N);
+  const size_t units = size_t(plan_units < kAttnMaxUnits ? plan_units : kAttnMaxUnits);
+  L.opart = take(size_t(4) * units * kQTile * w->head_dim);
+  L.ml = take(size_t(4) * units * kQTile * 2);
   // rotary (cos, sin) per row and head-dim pair
   L.rope = take(w->weight_layout == DCU_WEIGHTS_BLOCKED_ROPE ? size_t(4) * M * w->head_dim : 0);
   L.total = off;
@@ -1353,8 +1393,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
                                           const int32_t* sel_idx, const int32_t* sel_count,
                                           int32_t B, int32_t N, int32_t max_rows, void* k_cache,
                                           void* v_cache, void* y_out, void* workspace,
-                                          size_t workspace_bytes, void* stream,
-                                          void* const* events, int32_t n_events) {
+                                          size_t workspace_bytes, int32_t* rows_done,
+                                          void* stream, void* const* events, int32_t n_events) {
   using namespace dcu;
   if (events != nullptr && n_events < DCU_LAYER_STAGES + 1) return DCU_EINVAL;
   int st = validate(w, B, N);
@@ -1457,7 +1497,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.N = N;
   aa.H = H;
   aa.d = d;
-  aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;  // key ranges of >= 128 keys
+  aa.S_max = attn_s_max(N);  // key ranges of >= 128 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   st = launch_attention(aa, DH, s);
   if (st != DCU_OK) return st;
@@ -1483,7 +1523,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
     const uint16_t* gf_ = static_cast<const uint16_t*>(w->g_ffn);
 #define DCU_RMS(NC)                                                                        \
   hipLaunchKernelGGL(k_rmsnorm_f32<NC>, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr, gf_, d, \
-                     w->rms_eps, P.xn)
+                     w->rms_eps, P.xn, rows_done, int(B), P.seq_off, P.rowmap)
     switch (rms_nc(d, true)) {
       case 1: DCU_RMS(1); break;
       case 2: DCU_RMS(2); break;
@@ -1669,7 +1709,7 @@ extern "C" int dcu_attention_context(const dcu_layer* w, const void* x_in, int32
   aa.N = N;
   aa.H = w->n_heads;
   aa.d = d;
-  aa.S_max = N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1;
+  aa.S_max = attn_s_max(N);
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   return launch_attention(aa, DH, s);
 }
@@ -1677,7 +1717,9 @@ extern "C" int dcu_attention_context(const dcu_layer* w, const void* x_in, int32
 extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
                                    const int32_t* sel_count, int32_t B, int32_t N,
                                    int32_t max_rows, void* k_cache, void* v_cache, void* y_out,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   void* workspace, size_t workspace_bytes, int32_t* rows_done,
+                                   void* stream) {
   return dcu_selective_layer_staged(w, x_in, sel_idx, sel_count, B, N, max_rows, k_cache, v_cache,
-                                    y_out, workspace, workspace_bytes, stream, nullptr, 0);
+                                    y_out, workspace, workspace_bytes, rows_done, stream, nullptr,
+                                    0);
 }

@@ -10,14 +10,15 @@ import selective_token_cache_amd as stc
 from selective_token_cache_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dcu.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.lib_path()),
                                 reason="libdcu.so not built (run the build first)")
 
 
 def _declared():
-    txt = open(HEADER).read()
+    txt = "\n".join(open(h).read() for h in HEADERS)
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", txt)) -
                   {"if", "sizeof", "defined", "extern"})
@@ -178,7 +179,7 @@ def test_layer_validation():
 
     def call(desc, B=2, N=64, sel=None, cnt=None):
         return L.dcu_selective_layer(ctypes.byref(desc), FAKE, sel, cnt, B, N, 0, FAKE, FAKE, FAKE,
-                                     FAKE, 1 << 40, None)
+                                     FAKE, 1 << 40, None, None)
 
     assert ws(ctypes.byref(_desc()), 2, 64, 0) > 0
     assert ws(ctypes.byref(_desc(layout=0)), 2, 64, 0) == 0
@@ -198,7 +199,7 @@ def test_layer_validation():
     assert call(_desc(), sel=FAKE) == _lib.EINVAL                  # only one of sel_idx / sel_count
     # workspace smaller than the query says
     assert L.dcu_selective_layer(ctypes.byref(_desc()), FAKE, None, None, 2, 64, 0, FAKE, FAKE, FAKE,
-                                 FAKE, 16, None) == _lib.EWORKSPACE
+                                 FAKE, 16, None, None) == _lib.EWORKSPACE
 
 
 def test_attention_context_validation():
@@ -234,3 +235,20 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_m0_check_of_the_dma_kernels():
+    """The build's scan of the DMA kernels' assembly: the built listing passes, and a compiler-style
+    use of M0 (a write not followed by the DMA, an implicit reader) inserted into it is caught."""
+    from selective_token_cache_amd import build as b
+    path = os.path.join(ROOT, "_build", "layer.hip.gfx950.s")
+    if not os.path.exists(path):
+        pytest.skip("assembly listing not built")
+    asm = open(path).read()
+    assert b.check_m0(asm) == []
+    i = asm.index("k_attnILi128E")
+    j = asm.index("s_endpgm", i)
+    bad = asm[:j] + "s_mov_b32 m0, -1\n\tv_movrels_b32 v1, v2\n\t" + asm[j:]
+    problems = b.check_m0(bad)
+    assert any("M0 used by the compiler" in p for p in problems)
+    assert any("reading M0" in p for p in problems)

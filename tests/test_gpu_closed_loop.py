@@ -12,6 +12,7 @@ import selective_token_cache_amd as stc
 from oracle import distance as odist
 from oracle import layer as olayer
 from oracle import select as osel
+from oracle import step as ostep
 from tests.util import assert_rel, dev, dev_bf16, host_bf16, rel_l2
 from workloads import synth
 
@@ -100,3 +101,56 @@ def test_closed_loop_steps_against_the_oracle():
         for b in range(B):
             k = min(int(nh[b]), 2)
             assert kh[b, :k].tolist() == [N - MC + int(oh[b, j]) for j in range(k)]
+
+
+def test_full_budget_closed_loop_step_equals_the_oracle_step():
+    """A closed-loop step in which every row of the first input moves and the budget covers every
+    row: every layer then recomputes all rows (the step equals the dense step), on the GPU chain
+    and in the oracle's own step driver (dcu_step, closed loop, rotary layers) alike, so the two
+    chains are compared layer by layer: selections of all N rows, outputs within rel-L2 1e-2."""
+    g = synth.rng(980, 1)
+    shape = synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=192)
+    L, B, N, bw = 3, 2, 64, 8
+    d = shape.d
+    ws_host = [synth.layer_weights(g, shape, std=0.05, gain_jitter=0.1) for _ in range(L)]
+    layers = []
+    for w in ws_host:
+        t = {k: dev_bf16(v) for k, v in w.items()}
+        layers.append(stc.Layer(d, shape.n_heads, shape.head_dim, shape.ffn, shape.eps, t["w_qkv"],
+                                t["w_o"], t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"],
+                                rope_theta=THETA))
+    x_prev0 = synth.normal_bf16(g, (B, N, d))
+    x1 = synth.f32_to_bf16(synth.bf16_to_f32(x_prev0) +
+                           g.standard_normal((B, N, d), dtype=np.float32) * np.float32(0.1))
+    kc = [torch.zeros((B, N, shape.n_heads, shape.head_dim), dtype=torch.bfloat16, device="cuda")
+          for _ in range(L)]
+    vc = [torch.zeros_like(kc[0]) for _ in range(L)]
+    y = [torch.zeros((B, N, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    xprev = [dev_bf16(x_prev0)] + [torch.zeros((B, N, d), dtype=torch.bfloat16, device="cuda")
+                                   for _ in range(L - 1)]
+    X = xprev[0]
+    for l in range(L):
+        stc.dcu_selective_layer(layers[l], X, None, None, kc[l], vc[l], y[l])
+        if l + 1 < L:
+            xprev[l + 1].copy_(y[l])
+        X = y[l]
+    # the oracle's state: the same cached inputs (the GPU's dense chain), its own dense fill
+    st = ostep.dense_fill(ws_host, shape.n_heads, shape.head_dim, shape.eps,
+                          [host_bf16(t) for t in xprev], THETA)
+    keys = np.array([[20, -1], [40, 41]], np.int32)
+    rec = ostep.dcu_step(st, ws_host, shape.n_heads, shape.head_dim, shape.eps, N, bw, keys,
+                         x0=x1, rope_theta=THETA)
+    budgets = stc.dcu_budget(None, B, L, N)
+    X = dev_bf16(x1)
+    for l in range(L):
+        if l == 0:
+            dist, _ = stc.dcu_distance(X, xprev[0], want_mean=False)
+        else:
+            dist = stc.dcu_distance_rows(y[l - 1], xprev[l], sel, cnt, roll=True)
+        sel, cnt = stc.dcu_select(dist, budgets, l, dev(keys), bw)
+        assert np.all(cnt.cpu().numpy() == N) and np.all(rec[l]["sel_count"] == N)
+        stc.dcu_selective_layer(layers[l], X, sel, cnt, kc[l], vc[l], y[l])
+        e = rel_l2(synth.bf16_to_f32(host_bf16(y[l])), st.y[l])
+        print(f"  layer {l}: rel-L2 against the oracle step {e:.2e}", flush=True)
+        assert e <= 1e-2
+        X = y[l]

@@ -125,6 +125,27 @@ def test_budget_bit_exact():
                           obud.layer_budget(s, 1, 32, 32))
 
 
+def test_budget_negative_and_extreme_means():
+    """Negative means read as 0; means spread over the fp32 exponent range; a total close to 2^31
+    with 1024 layers; equal means in long runs: bit-exact against the oracle, rows summing to T."""
+    _log("budget extremes")
+    g = synth.rng(902, 1)
+    cases = []
+    s = g.uniform(-1e-3, 1e-3, (4, 16)).astype(np.float32)
+    s[3] = -1.0                                                        # all negative: uniform
+    cases.append((s, 7))
+    cases.append(((2.0 ** g.uniform(-126, 100, (3, 1024))).astype(np.float32), (2 ** 31 - 1) // 1024))
+    e = np.full((2, 300), np.float32(0.1))
+    e[1, ::7] = np.float32(1e-45)
+    cases.append((e, 1000))
+    for s, bl in cases:
+        B, L = s.shape
+        got = stc.dcu_budget(dev(s.T.copy()), B, L, bl).cpu().numpy()
+        ref = obud.layer_budget(s, B, L, bl)
+        assert np.array_equal(got, ref), (B, L, bl)
+        assert np.all(got.astype(np.int64).sum(1) == bl * L) and np.all(got >= 0)
+
+
 # ----------------------------------------------------------------------------- select
 def _check_select(d, budgets, layer, keys, bw):
     sel, cnt = stc.dcu_select(dev(d), dev(budgets), layer, dev(keys) if keys is not None else None, bw)
@@ -232,6 +253,27 @@ def test_confidence(R, V, ld, bf16):
     assert np.array_equal(tok.cpu().numpy(), rt)
     assert_rel(c.cpu().numpy(), rc)
     assert np.array_equal(c.cpu().numpy(), c2.cpu().numpy())
+
+
+@pytest.mark.parametrize("peak", [16.0, 300.0, 1000.0, -500.0])
+def test_confidence_large_logits(peak):
+    """Rows whose maximum is far from 0 (a planted peak at +300, +1000, or every logit near -500):
+    the exponentials are taken of z - max z, so the confidence carries no bias that grows with
+    |max z|; 1e-5 relative against the fp64 oracle."""
+    _log(f"confidence peak {peak}")
+    R, V = 24, 126464
+    g = synth.rng(904, 7, int(abs(peak)))
+    z = g.standard_normal((R, V)).astype(np.float32) * np.float32(3.0)
+    if peak > 0:
+        z[np.arange(R), g.integers(0, V, R)] = np.float32(peak) + g.uniform(0, 4, R).astype(np.float32)
+    else:
+        z += np.float32(peak)
+    zb = synth.f32_to_bf16(z)
+    for t, arr in ((dev_bf16(zb), zb), (dev(z), z)):
+        c, tok = stc.dllm_confidence(t, V)
+        rc, rt = oconf.confidence64(arr, V)
+        assert np.array_equal(tok.cpu().numpy(), rt)
+        assert_rel(c.cpu().numpy(), rc)
 
 
 def test_confidence_full_size_sampled():

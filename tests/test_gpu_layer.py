@@ -9,7 +9,7 @@ import torch
 
 import selective_token_cache_amd as stc
 from oracle import layer as olayer
-from tests.util import dev, dev_bf16, host_bf16, rel_l2
+from tests.util import dev, dev_bf16, host_bf16, rel_l2, row_rel_l2
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -41,16 +41,19 @@ class Case:
                          t["w_gate"], t["w_up"], t["w_down"], t["g_attn"], t["g_ffn"],
                          rope_theta=self.theta)
 
-    def run_gpu(self, sel, cnt, max_rows=0, reps=1):
+    def run_gpu(self, sel, cnt, max_rows=0, reps=1, rows_done=None):
         L = self.layer()
         out = []
         for _ in range(reps):
             kc, vc, y = dev_bf16(self.kc), dev_bf16(self.vc), dev_bf16(self.y)
+            rd = torch.full((self.B,), -7, dtype=torch.int32, device="cuda")
             stc.dcu_selective_layer(L, dev_bf16(self.x), None if sel is None else dev(sel),
                                     None if cnt is None else dev(cnt), kc, vc, y,
-                                    max_rows=max_rows)
+                                    max_rows=max_rows, rows_done=rd)
             torch.cuda.synchronize()
             out.append((host_bf16(kc), host_bf16(vc), host_bf16(y)))
+            if rows_done is not None:
+                rows_done.append(rd.cpu().numpy())
         return out
 
     def run_oracle(self, sel, cnt):
@@ -111,8 +114,11 @@ def _compare(case, got, ref, rows):
     ov = np.concatenate([rv[b, r].reshape(len(r), -1) for b, r in allr])
     oy = np.concatenate([ry[b, r] for b, r in allr])
     ek, ev, ey = rel_l2(gk, ok), rel_l2(gv, ov), rel_l2(gy, oy)
-    _log(f"  rel-L2 K {ek:.2e} V {ev:.2e} Y {ey:.2e}")
+    rk_, rv_, ry_ = row_rel_l2(gk, ok).max(), row_rel_l2(gv, ov).max(), row_rel_l2(gy, oy).max()
+    _log(f"  rel-L2 K {ek:.2e} V {ev:.2e} Y {ey:.2e}; worst row K {rk_:.2e} V {rv_:.2e} Y {ry_:.2e}")
     assert ek <= TOL and ev <= TOL and ey <= TOL
+    # the same bar on every recomputed row, so one bad row cannot hide in the pooled value
+    assert rk_ <= TOL and rv_ <= TOL and ry_ <= TOL
 
 
 def _random_selection(g, B, N, counts):
@@ -171,13 +177,88 @@ def test_empty_selection_and_max_rows_clamp():
     shape = synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=128)
     case = Case(shape, 3, 100, seed=8)
     sel, cnt = _random_selection(case.g, 3, 100, [0, 0, 0])
-    (got,) = case.run_gpu(sel, cnt)
+    done = []
+    (got,) = case.run_gpu(sel, cnt, rows_done=done)
     assert np.array_equal(got[0], case.kc) and np.array_equal(got[2], case.y)
-    # counts 40 + 50 + 30 with room for 70 rows: sequence 0 fully, sequence 1 its first 30 rows
+    assert done[0].tolist() == [0, 0, 0]
+    # counts 40 + 50 + 30 with room for 70 rows: sequence 0 fully, sequence 1 its first 30 rows,
+    # which rows_done reports
     sel, cnt = _random_selection(case.g, 3, 100, [40, 50, 30])
-    (got,) = case.run_gpu(sel, cnt, max_rows=70)
+    done = []
+    (got,) = case.run_gpu(sel, cnt, max_rows=70, rows_done=done)
     cl = np.array([40, 30, 0], np.int32)
+    assert done[0].tolist() == cl.tolist()
     _compare(case, got, case.run_oracle(sel, cl), _rows(sel, cl, 3, 100))
+    # counts past N are clamped to N (dense rows of that sequence)
+    sel = np.tile(np.arange(100, dtype=np.int32), (3, 1))
+    done = []
+    (got,) = case.run_gpu(sel, np.array([500, 0, 3], np.int32), rows_done=done)
+    assert done[0].tolist() == [100, 0, 3]
+    _compare(case, got, case.run_oracle(sel, np.array([100, 0, 3], np.int32)),
+             _rows(sel, np.array([100, 0, 3], np.int32), 3, 100))
+
+
+@pytest.mark.parametrize("shape,B,N,theta,max_rows", [
+    (synth.LayerShape(d=128, n_heads=2, head_dim=64, ffn=128), 3, 100, 0.0, 0),
+    (synth.LayerShape(d=256, n_heads=4, head_dim=64, ffn=512), 2, 300, 1e4, 0),
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 2, 90, 5e5, 64),
+])
+def test_positions_outside_the_sequence_are_skipped(shape, B, N, theta, max_rows):
+    """A selection list holding -1, N and other out-of-range entries among its counted positions:
+    nothing is read or written for those entries (caches and output untouched there), every valid
+    position is recomputed as the oracle recomputes the list without them, and rows_done counts
+    the valid positions only."""
+    _log(f"layer skipped positions d={shape.d} B={B} N={N} theta={theta}")
+    case = Case(shape, B, N, seed=shape.d + N + 77, theta=theta)
+    g = case.g
+    sel = np.full((B, N), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    valid = []
+    for b in range(B):
+        k = min(N // 3, 25 if max_rows else N // 3)
+        good = np.sort(g.choice(N, size=k, replace=False)).astype(np.int32)
+        bad = np.array([-1, N, N + 5, -(2 ** 31), 2 ** 31 - 1][: 2 + b], np.int32)
+        lst = np.concatenate([good, bad])
+        g.shuffle(lst)
+        sel[b, :len(lst)] = lst
+        cnt[b] = len(lst)
+        valid.append(good)
+    done = []
+    (got, got2) = case.run_gpu(sel, cnt, max_rows=max_rows, reps=2, rows_done=done)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    assert done[0].tolist() == [len(v) for v in valid]
+    vsel = np.full((B, N), -1, np.int32)
+    vcnt = np.array([len(v) for v in valid], np.int32)
+    for b, v in enumerate(valid):
+        vsel[b, :len(v)] = v
+    _compare(case, got, case.run_oracle(vsel, vcnt), _rows(vsel, vcnt, B, N))
+
+
+def test_layer_on_a_side_stream_keeps_its_workspace():
+    """The binding's own workspace, allocated on the current stream for work enqueued on another
+    stream, is not handed to a later allocation on the current stream while that work runs: a
+    call on a side stream followed at once by allocations filled with garbage on the default
+    stream gives the same bits as the same call on the default stream."""
+    shape = synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048)
+    B, N = 2, 512
+    case = Case(shape, B, N, seed=91)
+    sel, cnt = _random_selection(case.g, B, N, [300, 250])
+    (ref,) = case.run_gpu(sel, cnt)
+    L = case.layer()
+    side = torch.cuda.Stream()
+    x, ds, dc = dev_bf16(case.x), dev(sel), dev(cnt)
+    n_junk = L.workspace_bytes(B, N) // 4
+    for _ in range(3):
+        kc, vc, y = dev_bf16(case.kc), dev_bf16(case.vc), dev_bf16(case.y)
+        torch.cuda.synchronize()
+        stc.dcu_selective_layer(L, x, ds, dc, kc, vc, y, stream=side)
+        junk = [torch.full((n_junk,), float("nan"), device="cuda") for _ in range(4)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bf16(kc), ref[0]) and np.array_equal(host_bf16(vc), ref[1])
+        assert np.array_equal(host_bf16(y), ref[2])
+        del junk
 
 
 def test_full_size_single_sequence_64_rows():

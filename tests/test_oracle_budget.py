@@ -103,3 +103,38 @@ def test_batched_rows_are_independent():
     b = ob.layer_budget(s, 5, 9, 11)
     for i in range(5):
         assert b[i].tolist() == ob.layer_budget_row(s[i], 9, 11).tolist()
+
+
+def test_floors_never_overshoot_on_adversarial_means():
+    """The floors of q_l = (T s_l) / S never sum past T (the module docstring's bound), so the
+    largest-remainder step only ever adds: means spread over the whole fp32 exponent range, long
+    runs of equal means, T close to 2^31 and L up to 1024 keep sum(b) == T with every b_l >= 0."""
+    g = synth.rng(200, 3)
+    for trial in range(200):
+        L = int(g.integers(1, 1025)) if trial % 4 else 1024
+        b_layer = int(g.integers(1, (2 ** 31 - 1) // L + 1)) if trial % 3 == 0 else int(g.integers(0, 300))
+        kind = trial % 5
+        if kind == 0:
+            s = (2.0 ** g.uniform(-126, 100, size=L)).astype(np.float32)
+        elif kind == 1:
+            s = np.full(L, np.float32(g.uniform(1e-6, 1.0)))
+        elif kind == 2:
+            s = g.uniform(0, 2, size=L).astype(np.float32)
+            s[g.integers(0, L, size=max(1, L // 2))] = np.float32(1e-45)   # smallest subnormal
+        elif kind == 3:
+            s = np.nextafter(np.float32(1.0), np.float32(2.0), dtype=np.float32) * np.ones(L, np.float32)
+            s[::3] = np.float32(1.0)
+        else:
+            s = g.uniform(0, 1e-3, size=L).astype(np.float32)
+        b = ob.layer_budget_row(s, L, b_layer)
+        assert int(b.astype(np.int64).sum()) == b_layer * L
+        assert np.all(b >= 0)
+
+
+def test_negative_means_read_as_zero():
+    """Means are averages of distances in [0, 2]; a negative entry counts as 0 (a layer that gets
+    no share), and an all-negative row is the all-zero row (uniform budgets)."""
+    s = np.array([0.5, -0.25, 1.5, -3.0], np.float32)
+    assert ob.layer_budget_row(s, 4, 8).tolist() == ob.layer_budget_row(np.maximum(s, 0), 4, 8).tolist()
+    assert ob.layer_budget_row(s, 4, 8).tolist() == [8, 0, 24, 0]
+    assert ob.layer_budget_row(-np.ones(3, np.float32), 3, 5).tolist() == [5, 5, 5]

@@ -24,6 +24,14 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+def row_rel_l2(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """rel-L2 of every row (last axis flattened per leading index) of got against ref."""
+    got = np.asarray(got, np.float64).reshape(len(got), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    den = np.linalg.norm(ref, axis=1)
+    return np.linalg.norm(got - ref, axis=1) / np.where(den > 0, den, 1.0)
+
+
 def assert_rel(got, ref, rtol=1e-5):
     """|got - ref| <= rtol * |ref| elementwise; exact zero where ref == 0."""
     got = np.asarray(got, np.float64)
