@@ -263,6 +263,26 @@ int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel
                         size_t workspace_bytes, int32_t* rows_done, void* stream);
 
 /*
+ * dcu_selective_layer_noalloc -- dcu_selective_layer for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation (same kernels, same results bit for bit) with its scratch in a device
+ * array the library owns instead of a caller workspace; it calls no allocating routine.
+ * The array holds DCU_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, until the process
+ * ends; its address is looked up on the first call for a device (the device of `stream`).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller. Its contents on entry do not matter.
+ * Arguments, outputs and errors as dcu_selective_layer, plus EWORKSPACE when the scratch these
+ * shapes need (dcu_selective_layer_workspace(w, B, N, max_rows)) exceeds
+ * DCU_NOALLOC_SCRATCH_BYTES: a LLaDA-8B-shaped layer (d 4096, 32 heads of 128, FFN 12288) fits
+ * with max_rows <= 64 (one sequence: budget 32 + window 32) up to N = 8192; pass max_rows.
+ */
+#define DCU_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int dcu_selective_layer_noalloc(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
+                                const int32_t* sel_count, int32_t B, int32_t N, int32_t max_rows,
+                                void* k_cache, void* v_cache, void* y_out, int32_t* rows_done,
+                                void* stream);
+
+/*
  * dcu_attention_context -- the attention context of every row of a layer, for an attention-context
  * distance. (DyLLM, in the pages' listing of related papers, finds its salient tokens by the cosine
  * similarity of attention contexts between adjacent denoising steps; apply dcu_distance to ctx_out

@@ -22,9 +22,12 @@ Closed loop: feed y[l] to layer l+1 and use dcu_distance_rows for the layers aft
 dllm_commit_positions turns the commits into the next step's key positions. Other pieces:
 dllm_commit (factor / threshold / per-position threshold rules), dllm_apd (adaptive parallel
 decoding), dcu_v_features and dcu_attention_context (other distance features).
+dcu_selective_layer_noalloc is the layer call for callers that cannot allocate (its scratch is a
+device array of the library, shared by all calls on a GPU).
 """
 from ._lib import (BF16, F32, DcuError, Layer, dcu_attention_context, dcu_budget,  # noqa: F401
                    dcu_distance, dcu_distance_rows, dcu_pack_gate_up, dcu_pack_qkv,
-                   dcu_pack_weights, dcu_select, dcu_selective_layer, dcu_v_features, dllm_apd,
+                   dcu_pack_weights, dcu_select, dcu_selective_layer,
+                   dcu_selective_layer_noalloc, dcu_v_features, dllm_apd,
                    dllm_commit, dllm_commit_positions, dllm_confidence, frechet_commit, lib_path,
                    load, status_string, version)

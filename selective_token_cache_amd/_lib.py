@@ -59,6 +59,8 @@ EXPORTS = {
                                       [ctypes.POINTER(LayerDesc), _i32, _i32, _i32]),
     "dcu_selective_layer": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32, _i32,
                                            _i32, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]),
+    "dcu_selective_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _vp, _vp, _i32,
+                                                   _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "dcu_v_features": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
     "dcu_attention_context": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _vp, _i32, _i32, _vp, _vp,
@@ -347,6 +349,36 @@ def dcu_selective_layer(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_
                                                workspace.numel(), _p(rows_done), _stream(stream),
                                                arr, len(events))
         _check("dcu_selective_layer_staged", st)
+    return k_cache, v_cache, y_out
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # DCU_NOALLOC_SCRATCH_BYTES
+
+
+def dcu_selective_layer_noalloc(layer: Layer, x_in: torch.Tensor, sel_idx, sel_count, k_cache,
+                                v_cache, y_out, max_rows: int, rows_done: torch.Tensor | None = None,
+                                stream=None):
+    """dcu_selective_layer with the library's own device scratch (no workspace, nothing allocated):
+    for callers that cannot allocate. Calls on one GPU share that scratch and must not overlap."""
+    _need(x_in, "x_in", torch.bfloat16)
+    B, N, d = x_in.shape
+    if d != layer.d:
+        raise ValueError("x_in width does not match the layer")
+    _need(k_cache, "k_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, N, layer.n_heads, layer.head_dim))
+    _need(y_out, "y_out", torch.bfloat16, (B, N, d))
+    if (sel_idx is None) != (sel_count is None):
+        raise ValueError("sel_idx and sel_count go together")
+    if sel_idx is not None:
+        _need(sel_idx, "sel_idx", torch.int32, (B, N))
+        _need(sel_count, "sel_count", torch.int32, (B,))
+    if rows_done is not None:
+        _need(rows_done, "rows_done", torch.int32, (B,))
+    st = load().dcu_selective_layer_noalloc(ctypes.byref(layer.desc), _p(x_in), _p(sel_idx),
+                                            _p(sel_count), B, N, max_rows, _p(k_cache),
+                                            _p(v_cache), _p(y_out), _p(rows_done),
+                                            _stream(stream))
+    _check("dcu_selective_layer_noalloc", st)
     return k_cache, v_cache, y_out
 
 

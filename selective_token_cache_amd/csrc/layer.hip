@@ -26,6 +26,7 @@
 // tile walk) with fused epilogues, on 128x128 tiles (4 waves of 64x64, two workgroups per CU).
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1712,6 +1713,62 @@ extern "C" int dcu_attention_context(const dcu_layer* w, const void* x_in, int32
   aa.S_max = attn_s_max(N);
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   return launch_attention(aa, DH, s);
+}
+
+// ------------------------------------------------------------------------------ allocation-free call
+// The scratch of dcu_selective_layer_noalloc: a library-owned device array (every GPU the library
+// runs on holds its own copy until the process ends). In host code `scratch` names a host-side
+// stand-in, not the device address: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to the kernels.
+static __device__ __align__(256) unsigned char scratch[DCU_NOALLOC_SCRATCH_BYTES];
+
+namespace dcu {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// Device address of the scratch array on the device that runs `stream`, looked up on the first call
+// for that device with the device current.
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return DCU_EHIP;
+  if (stream == nullptr) {
+    dev = cur;
+  } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    return DCU_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DCU_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DCU_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return DCU_EHIP;
+    if (e != hipSuccess || p == nullptr) return DCU_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DCU_OK;
+}
+}  // namespace
+}  // namespace dcu
+
+extern "C" int dcu_selective_layer_noalloc(const dcu_layer* w, const void* x_in,
+                                           const int32_t* sel_idx, const int32_t* sel_count,
+                                           int32_t B, int32_t N, int32_t max_rows, void* k_cache,
+                                           void* v_cache, void* y_out, int32_t* rows_done,
+                                           void* stream) {
+  using namespace dcu;
+  const int st = validate(w, B, N);
+  if (st != DCU_OK) return st;
+  if (make_layout(w, B, N, max_rows).total > size_t(DCU_NOALLOC_SCRATCH_BYTES)) return DCU_EWORKSPACE;
+  void* ws = nullptr;
+  const int sst = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (sst != DCU_OK) return sst;
+  return dcu_selective_layer_staged(w, x_in, sel_idx, sel_count, B, N, max_rows, k_cache, v_cache,
+                                    y_out, ws, size_t(DCU_NOALLOC_SCRATCH_BYTES), rows_done, stream,
+                                    nullptr, 0);
 }
 
 extern "C" int dcu_selective_layer(const dcu_layer* w, const void* x_in, const int32_t* sel_idx,
