@@ -31,3 +31,4 @@ from ._lib import (BF16, F32, DcuError, Layer, dcu_attention_context, dcu_budget
                    dcu_selective_layer_noalloc, dcu_v_features, dllm_apd,
                    dllm_commit, dllm_commit_positions, dllm_confidence, frechet_commit, lib_path,
                    load, status_string, version)
+from ._lib import dcu_measure_mfma_loop, dcu_measure_stream_read  # noqa: F401
