@@ -112,6 +112,7 @@ PROFILED_KERNELS = [
     ("k_gemm_fixup<5>", "qkv_fixup", 1), ("k_attn<", "attention", 1),
     ("k_attn_combine", "attention_combine", 1), ("k_gemm<1>", "o_proj_residual", 1),
     ("k_gemm_fixup<1>", "o_proj_fixup", 1), ("k_rmsnorm_f32<", "rmsnorm", 1),
+    ("k_resid_rmsnorm<", "rmsnorm", 1),
     ("k_gemm<2>", "gate_up_swiglu", 1), ("k_gemm_fixup<2>", "gate_up_fixup", 1),
     ("k_gemm<3>", "down_residual_scatter", 1), ("k_gemm_fixup<3>", "down_fixup", 1),
     ("k_confidence<", "confidence", 0), ("k_frechet", "commit", 0),
@@ -888,11 +889,11 @@ def measure_peaks(stc, torch, dev):
     del buf
     fs = torch.zeros((256,), dtype=torch.float32, device=dev)
     best_f = 0.0
-    for grid in (512, 1024):
+    for grid in (1024, 2048):
         flops = [0]
 
         def run():
-            flops[0] = stc.dcu_measure_mfma_loop(grid, 2048, fs)
+            flops[0] = stc.dcu_measure_mfma_loop(grid, 1024, fs)
         ms = _event_time_ms(torch, run, 3)
         best_f = max(best_f, flops[0] / (ms * 1e-3) / 1e12)
     return {"stream_read_GBps": round(best, 1), "hbm_nominal_GBps": HBM_PEAK_GBS,
@@ -901,7 +902,7 @@ def measure_peaks(stc, torch, dev):
             "mfma_loop_frac_of_nominal": round(best_f / MFMA_BF16_PEAK_TFLOPS, 3),
             "kernels": "dcu_measure_stream_read (2 GiB, 16-byte non-temporal loads, best of grids "
                        "1024/2048/4096 x 256 threads); dcu_measure_mfma_loop (8 independent "
-                       "v_mfma_f32_16x16x32_bf16 chains per wave, best of 512/1024 workgroups)"}
+                       "v_mfma_f32_32x32x16_bf16 chains per wave, best of 1024/2048 workgroups)"}
 
 
 def batch1_layer(stc, torch, wd, layer, N, dev):

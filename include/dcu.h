@@ -110,8 +110,11 @@ int dcu_distance(const void* x_cur, const void* x_prev, int32_t dtype, int64_t G
  * roll     non-zero: afterwards each listed row of x_cur is copied into x_prev (the cache roll of
  *          the rows that changed; the others are already equal).
  * The layer mean is then available from dcu_select (mean argument), which reads every distance.
+ * One launch: each workgroup marks its sequence's listed positions in an LDS bitmap and writes
+ * 0 for the unlisted positions it covers.
  * Errors: EINVAL on NULL pointers, B, N, d <= 0 or a bad dtype; EUNSUPPORTED if d is not a
- *         multiple of 8 (bf16) or 4 (fp32), a pointer is not 16-byte aligned, or B > 65535.
+ *         multiple of 8 (bf16) or 4 (fp32), a pointer is not 16-byte aligned, B > 65535 or
+ *         N > 65536.
  */
 int dcu_distance_rows(const void* x_cur, void* x_prev, int32_t dtype, int64_t B, int64_t N,
                       int64_t d, const int32_t* sel_idx, const int32_t* sel_count, float* dist,
@@ -319,7 +322,8 @@ int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, int32_t N, v
  * the first kernel and events[i] after stage i on `stream`, for the DCU_LAYER_STAGES stages
  *   1 row offsets and map + gather + RMSNorm, 2 QKV projection + K/V scatter,
  *   3 its split-tail fixup, 4 attention (+ split combine), 5 output projection + residual,
- *   6 its fixup, 7 RMSNorm, 8 gate/up projection + SwiGLU, 9 its fixup,
+ *   6 its fixup (empty for rows of up to 4096 values: the split tiles are then finished inside
+ *   stage 7), 7 RMSNorm, 8 gate/up projection + SwiGLU, 9 its fixup,
  *   10 down projection + residual + scatter, 11 its fixup.
  * (A fixup kernel finishes the tiles whose K range was split over idle workgroups; it exits at
  * once when the projection did not split.)

@@ -28,8 +28,8 @@ int dcu_measure_stream_read(const void* buf, int64_t bytes, int32_t grid, uint32
 
 /*
  * dcu_measure_mfma_loop -- `grid` workgroups of 4 waves, each wave issuing iters x 8 independent
- * v_mfma_f32_16x16x32_bf16 (16 x 16 x 32 multiply-adds, 16384 flops each) on register operands:
- * the matrix-core rate is grid * 4 * iters * 8 * 16384 / kernel time.
+ * v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 multiply-adds, 32768 flops each) on register operands:
+ * the matrix-core rate is grid * 4 * iters * 8 * 32768 / kernel time.
  * sink  256 floats the kernel may write (so the work is kept); values meaningless.
  * Errors: EINVAL on a NULL sink, grid <= 0 or iters <= 0.
  */

@@ -540,11 +540,11 @@ def dcu_measure_stream_read(buf: torch.Tensor, grid: int, sink: torch.Tensor, st
 
 
 def dcu_measure_mfma_loop(grid: int, iters: int, sink: torch.Tensor, stream=None) -> int:
-    """grid x 4 waves x iters x 8 bf16 MFMAs of 16 x 16 x 32 (include/dcu_measure.h); returns the
+    """grid x 4 waves x iters x 8 bf16 MFMAs of 32 x 32 x 16 (include/dcu_measure.h); returns the
     flop count."""
     _need(sink, "sink", torch.float32)
     if sink.numel() < 256:
         raise ValueError("sink must hold 256 floats")
     _check("dcu_measure_mfma_loop",
            load().dcu_measure_mfma_loop(int(grid), int(iters), _p(sink), _stream(stream)))
-    return int(grid) * 4 * int(iters) * 8 * 16 * 16 * 32 * 2
+    return int(grid) * 4 * int(iters) * 8 * 32 * 32 * 16 * 2

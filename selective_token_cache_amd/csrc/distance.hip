@@ -50,6 +50,27 @@ __device__ __forceinline__ void acc_f32_pair(Acc& s, uint32_t wa0, uint32_t wa1,
   s.nb1 = fma(b1, b1, s.nb1);
 }
 
+// the distance from a wave's per-lane sums (butterfly over the wave, then 1 - cos in fp64);
+// every lane returns the same value
+__device__ __forceinline__ double finish_distance(const Acc& s) {
+  const double dot = wave_sum(s.dot0 + s.dot1);
+  const double na = wave_sum(s.na0 + s.na1);
+  const double nb = wave_sum(s.nb0 + s.nb1);
+  const uint32_t diff = wave_or(s.diff);
+  double d;
+  if (diff == 0u) {
+    d = 0.0;
+  } else if (na == 0.0 && nb == 0.0) {
+    d = 0.0;
+  } else if (na == 0.0 || nb == 0.0) {
+    d = 1.0;
+  } else {
+    d = 1.0 - dot / sqrt(na * nb);
+    d = d < 0.0 ? 0.0 : (d > 2.0 ? 2.0 : d);
+  }
+  return d;
+}
+
 // distance of one row pair by one wave: fp64 sums of the products, XOR flag for identical rows;
 // every lane returns the same value
 template <bool kBf16>
@@ -82,22 +103,7 @@ __device__ __forceinline__ double row_distance(const uint4* __restrict__ a,
       }
     }
   }
-  double dot = wave_sum(s.dot0 + s.dot1);
-  double na = wave_sum(s.na0 + s.na1);
-  double nb = wave_sum(s.nb0 + s.nb1);
-  uint32_t diff = wave_or(s.diff);
-  double d;
-  if (diff == 0u) {
-    d = 0.0;
-  } else if (na == 0.0 && nb == 0.0) {
-    d = 0.0;
-  } else if (na == 0.0 || nb == 0.0) {
-    d = 1.0;
-  } else {
-    d = 1.0 - dot / sqrt(na * nb);
-    d = d < 0.0 ? 0.0 : (d > 2.0 ? 2.0 : d);
-  }
-  return d;
+  return finish_distance(s);
 }
 
 template <bool kBf16>
@@ -112,12 +118,28 @@ __global__ __launch_bounds__(256) void k_distance(const uint4* __restrict__ xc,
 }
 
 // Listed rows only (closed-loop chaining: the previous layer scattered exactly these rows, every
-// other row of x_cur equals x_prev bit for bit and has distance 0): one wave per list slot j of
-// sequence b; with roll, the row of x_cur is then copied into x_prev (the cache roll of that row).
-__global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * blockDim.x)
-    p[i] = 0.0f;
+// other row of x_cur equals x_prev bit for bit and has distance 0). Workgroup (blk, b) first marks
+// the listed positions of sequence b in an LDS bitmap (the list is a few hundred words), then wave w
+// writes 0 for position 4 blk + w if it is not listed, and computes the distance of list slot
+// 4 blk + w if that slot is counted; with roll, that row of x_cur is then copied into x_prev (the
+// cache roll of the row). Every position's distance is written by exactly one wave.
+// Latency: the count, the wave's own slot and the first kListPre entries of the list are loaded
+// together (all in bounds whatever the count), and a row that fits in one round of loads is rolled
+// from the registers it was read into.
+constexpr int kMaxRowsBitmap = 65536;  // positions per sequence (LDS bitmap of 8 KB)
+constexpr int kListPre = 4;            // list entries per thread loaded before the count is known
+
+template <bool kBf16>
+__device__ __forceinline__ void acc_chunk(Acc& s, const uint4& a, const uint4& b) {
+  if constexpr (kBf16) {
+    acc_bf16_word(s, a.x, b.x);
+    acc_bf16_word(s, a.y, b.y);
+    acc_bf16_word(s, a.z, b.z);
+    acc_bf16_word(s, a.w, b.w);
+  } else {
+    acc_f32_pair(s, a.x, a.y, b.x, b.y);
+    acc_f32_pair(s, a.z, a.w, b.z, b.w);
+  }
 }
 
 template <bool kBf16>
@@ -126,18 +148,62 @@ __global__ __launch_bounds__(256) void k_distance_rows(const uint4* __restrict__
                                                        const int32_t* __restrict__ sel_idx,
                                                        const int32_t* __restrict__ sel_count,
                                                        int roll, float* __restrict__ dist) {
+  __shared__ uint32_t listed[kMaxRowsBitmap / 32];
   const int lane = threadIdx.x & (kWave - 1);
   const int b = blockIdx.y;
   const int j = blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
-  // the slot's position is loaded with the count (j < N: in bounds either way), one round trip
-  const int pos = j < N ? sel_idx[int64_t(b) * N + j] : -1;
+  const int32_t* lst = sel_idx + int64_t(b) * N;
   int cnt = sel_count[b];
+  const int pos = j < N ? lst[j] : -1;
+  int pre[kListPre];
+#pragma unroll
+  for (int k = 0; k < kListPre; ++k) {
+    const int i = threadIdx.x + k * 256;
+    pre[k] = i < N ? lst[i] : -1;
+  }
+  const int words = (N + 31) / 32;
+  for (int i = threadIdx.x; i < words; i += blockDim.x) listed[i] = 0u;
   cnt = cnt < 0 ? 0 : (cnt > N ? N : cnt);
-  if (j >= cnt) return;
-  if (pos < 0 || pos >= N) return;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kListPre; ++k) {
+    const int i = threadIdx.x + k * 256, p = pre[k];
+    if (i < cnt && p >= 0 && p < N) atomicOr(&listed[p >> 5], 1u << (p & 31));
+  }
+  for (int i = threadIdx.x + kListPre * 256; i < cnt; i += blockDim.x) {
+    const int p = lst[i];
+    if (p >= 0 && p < N) atomicOr(&listed[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  if (j < N && lane == 0 && ((listed[j >> 5] >> (j & 31)) & 1u) == 0u)
+    dist[int64_t(b) * N + j] = 0.0f;
+  if (j >= cnt || pos < 0 || pos >= N) return;
   const int64_t row = int64_t(b) * N + pos;
   const uint4* a = xc + row * chunks;
   uint4* p = xp + row * chunks;
+  if (chunks <= kWave * kUnroll) {
+    // the whole row in one round of loads: distance, then the roll from the same registers
+    uint4 ra[kUnroll], rb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = u * kWave + lane;
+      ra[u] = c < chunks ? load_nt(a + c) : make_uint4(0, 0, 0, 0);
+      rb[u] = c < chunks ? load_nt(p + c) : make_uint4(0, 0, 0, 0);
+    }
+    Acc sacc;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc_chunk<kBf16>(sacc, ra[u], rb[u]);
+    const double d = finish_distance(sacc);
+    if (lane == 0) dist[row] = float(d);
+    if (roll) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = u * kWave + lane;
+        if (c < chunks) p[c] = ra[u];
+      }
+    }
+    return;
+  }
   const double d = row_distance<kBf16>(a, p, chunks, lane);
   if (lane == 0) dist[row] = float(d);
   if (roll)
@@ -203,15 +269,10 @@ extern "C" int dcu_distance_rows(const void* x_cur, void* x_prev, int32_t dtype,
   const int64_t per_chunk = dtype == DCU_BF16 ? 8 : 4;
   if (d % per_chunk != 0) return DCU_EUNSUPPORTED;
   if (!dcu_aligned16(x_cur) || !dcu_aligned16(x_prev)) return DCU_EUNSUPPORTED;
-  if (B > 65535 || N > (int64_t(1) << 30)) return DCU_EUNSUPPORTED;
+  if (B > 65535 || N > dcu::kMaxRowsBitmap) return DCU_EUNSUPPORTED;
   const int64_t chunks = d / per_chunk;
   if (chunks > (int64_t(1) << 30)) return DCU_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t n = B * N;
-  const int64_t zb = (n + 255) / 256;
-  hipLaunchKernelGGL(dcu::k_zero_f32, dim3(unsigned(zb < 4096 ? zb : 4096)), dim3(256), 0, s, dist,
-                     n);
-  DCU_LAUNCH_CHECK();
   const dim3 grid(unsigned((N + dcu::kRowsPerBlock - 1) / dcu::kRowsPerBlock), unsigned(B));
   const uint4* xc = static_cast<const uint4*>(x_cur);
   uint4* xp = static_cast<uint4*>(x_prev);

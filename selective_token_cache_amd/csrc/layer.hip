@@ -18,7 +18,9 @@
 //  4. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
 //                     when there are too few tiles to fill the chip) + k_attn_combine;
 //  5. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
-//  6. k_rmsnorm_f32   RMSNorm of a -> an (bf16);
+//  6. k_resid_rmsnorm the split tiles of a finished (fixed-order sums of the pieces + residual)
+//                     and RMSNorm of a -> an (bf16) in one pass (k_gemm_fixup + k_rmsnorm_f32 for
+//                     rows wider than 4096 or a row capacity of at most 64);
 //  7. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
 //  8. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
 //
@@ -425,6 +427,16 @@ using CfgSmall = gemm::Cfg<128, 128, 64, 64, 2, 4>;
 // three stages keeps twice the weight bytes in flight per CU (two K-tiles per workgroup, two
 // workgroups per CU) for the same LDS budget.
 using CfgSkinny = gemm::Cfg<64, 64, 32, 32, 4, 4>;
+// When the caller's row bound is at most 64 (one sequence: budget plus window) the host launches a
+// kernel of its own for the weight stream: 64 x 128 tiles (twice the weight rows per activation
+// row fetched), four stages, one workgroup per CU with 96 KB of LDS. Measured on the batch-1
+// shapes with cold weights: QKV 25.5 -> 22.6 us, output 10.8 -> 9.7, gate/up 45.3 -> 38.7, down
+// 23.9 -> 21.7 against the 64 x 64 tiles at two workgroups per CU.
+using CfgStream = gemm::Cfg<64, 128, 32, 64, 4, 4>;
+constexpr int kStreamSlots = 256;  // one workgroup per CU
+static_assert(CfgStream::BM * CfgStream::BN * kStreamSlots <=
+                  CfgSkinny::BM * CfgSkinny::BN * 2 * 256,
+              "partial tiles of the streaming kernel fit the 64-row workspace");
 constexpr int kGemmLdsChunks = CfgSmall::STAGES * CfgSmall::CHUNKS > CfgSkinny::STAGES * CfgSkinny::CHUNKS
                                    ? CfgSmall::STAGES * CfgSmall::CHUNKS
                                    : CfgSkinny::STAGES * CfgSkinny::CHUNKS;
@@ -444,7 +456,7 @@ constexpr bool early_refill() {
 }
 template <int EPI, class C>
 constexpr int split_mode() {
-  return std::is_same<C, CfgSkinny>::value ? kSplitStreaming
+  return (std::is_same<C, CfgSkinny>::value || std::is_same<C, CfgStream>::value) ? kSplitStreaming
                                            : (early_refill<EPI, C>() ? kSplitFewTiles : kSplitTail);
 }
 
@@ -657,6 +669,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
     gemm_body<EPI, CfgSmall>(g, M, smem);
 }
 
+// The weight-streaming projection for a row capacity of at most 64 (the device row count is then
+// at most 64 as well), one workgroup per CU
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_stream(GemmArgs g) {
+  __shared__ u32x4 smem[CfgStream::STAGES * CfgStream::CHUNKS];
+  const int M = g.hdr[kHdrM];
+  if (M <= 0) return;
+  gemm_body<EPI, CfgStream>(g, M, smem);
+}
+
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
 // thread and item, kFixupU items per thread and round, with kFixupChunk partials of those items
 // loaded before any is added (memory-level parallelism). Exits at once when the GEMM did not split.
@@ -790,10 +812,111 @@ template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   const int M = g.hdr[kHdrM];
   if (M <= 0) return;
-  if (use_skinny(M))
+  if (slots == kStreamSlots)
+    fixup_body<EPI, CfgStream>(g, M, slots);
+  else if (use_skinny(M))
     fixup_body<EPI, CfgSkinny>(g, M, slots);
   else
     fixup_body<EPI, CfgSmall>(g, M, slots);
+}
+
+// The output projection's split tiles finished together with the RMSNorm before the FFN: one wave
+// per row r takes each of its lane's 8-column groups either from a (a whole tile, stored by the
+// GEMM's epilogue) or as the fixed-order sum of the tile's fp32 pieces plus the residual x (a split
+// tile; the same order and residual as k_gemm_fixup's), stores that to a (the down projection's
+// residual), then normalises the row held in registers -> an (bf16). This replaces the output
+// projection's fixup launch. With rows_done, also the per-sequence count of recomputed rows.
+template <int NC, class C>
+__device__ __forceinline__ void resid_rms_rows(const GemmArgs& g, int M, int slots,
+                                               const uint16_t* __restrict__ gain, float eps,
+                                               uint16_t* __restrict__ out) {
+  const int d = g.d, groups = d / 8;
+  const int MT = (M + C::BM - 1) / C::BM;
+  const int NT = (g.Nout + C::BN - 1) / C::BN;
+  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode<EPI_RESID, C>());
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
+    const int m_t = r / C::BM, rl = r - m_t * C::BM;
+    const int64_t grow = int64_t(g.rowmap[r]);
+    float* arow = g.a + int64_t(r) * d;
+    float v[NC][8];
+    uint4 gg[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int gi = lane + c * kWave;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[c][k] = 0.0f;
+      if (gi >= groups) continue;
+      gg[c] = reinterpret_cast<const uint4*>(gain)[gi];
+      const int col = gi * 8, n_t = col / C::BN, cl = col - n_t * C::BN;
+      const int tile = n_t * MT + m_t;
+      float4 lo, hi;
+      if (tile < sp.full) {
+        lo = *reinterpret_cast<const float4*>(arow + col);
+        hi = *reinterpret_cast<const float4*>(arow + col + 4);
+      } else {
+        const float* pt = g.part + int64_t(tile - sp.full) * sp.S * (C::BM * C::BN) + rl * C::BN + cl;
+        lo = *reinterpret_cast<const float4*>(pt);
+        hi = *reinterpret_cast<const float4*>(pt + 4);
+        for (int sg = 1; sg < sp.S; ++sg) {
+          const float* q = pt + int64_t(sg) * (C::BM * C::BN);
+          const float4 a0 = *reinterpret_cast<const float4*>(q);
+          const float4 a1 = *reinterpret_cast<const float4*>(q + 4);
+          lo.x += a0.x; lo.y += a0.y; lo.z += a0.z; lo.w += a0.w;
+          hi.x += a1.x; hi.y += a1.y; hi.z += a1.z; hi.w += a1.w;
+        }
+        const uint4 xr = grow >= 0 ? *reinterpret_cast<const uint4*>(g.x + grow * d + col)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+        lo = make_float4(bf_lo(xr.x) + lo.x, bf_hi(xr.x) + lo.y, bf_lo(xr.y) + lo.z, bf_hi(xr.y) + lo.w);
+        hi = make_float4(bf_lo(xr.z) + hi.x, bf_hi(xr.z) + hi.y, bf_lo(xr.w) + hi.z, bf_hi(xr.w) + hi.w);
+        *reinterpret_cast<float4*>(arow + col) = lo;
+        *reinterpret_cast<float4*>(arow + col + 4) = hi;
+      }
+      v[c][0] = lo.x; v[c][1] = lo.y; v[c][2] = lo.z; v[c][3] = lo.w;
+      v[c][4] = hi.x; v[c][5] = hi.y; v[c][6] = hi.z; v[c][7] = hi.w;
+    }
+    // the RMSNorm of rms_row, same per-lane order
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) ss += v[c][k] * v[c][k] + v[c][k + 1] * v[c][k + 1];
+    ss = wave_sum(ss);
+    const float scale = 1.0f / sqrtf(ss / float(d) + eps);
+    uint16_t* orow = out + int64_t(r) * d;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int gi = lane + c * kWave;
+      if (gi >= groups) continue;
+      uint4 o;
+      o.x = pack_bf2(v[c][0] * scale * bf_lo(gg[c].x), v[c][1] * scale * bf_hi(gg[c].x));
+      o.y = pack_bf2(v[c][2] * scale * bf_lo(gg[c].y), v[c][3] * scale * bf_hi(gg[c].y));
+      o.z = pack_bf2(v[c][4] * scale * bf_lo(gg[c].z), v[c][5] * scale * bf_hi(gg[c].z));
+      o.w = pack_bf2(v[c][6] * scale * bf_lo(gg[c].w), v[c][7] * scale * bf_hi(gg[c].w));
+      reinterpret_cast<uint4*>(orow)[gi] = o;
+    }
+  }
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void k_resid_rmsnorm(GemmArgs g, int slots,
+                                                       const uint16_t* __restrict__ gain, float eps,
+                                                       uint16_t* __restrict__ out,
+                                                       int32_t* __restrict__ rows_done, int B,
+                                                       const int* __restrict__ seq_off) {
+  const int M = g.hdr[kHdrM];
+  if (rows_done) {
+    for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < B; b += gridDim.x * blockDim.x) {
+      int n = 0;
+      for (int r = seq_off[b]; r < seq_off[b + 1]; ++r) n += g.rowmap[r] >= 0 ? 1 : 0;
+      rows_done[b] = n;
+    }
+  }
+  if (M <= 0) return;
+  if (use_skinny(M))
+    resid_rms_rows<NC, CfgSkinny>(g, M, slots, gain, eps, out);
+  else
+    resid_rms_rows<NC, CfgSmall>(g, M, slots, gain, eps, out);
 }
 
 // ------------------------------------------------------------------------------ 4. attention
@@ -853,8 +976,9 @@ struct AttnPlan {
   int full, rem, S, kps;
 };
 
-// Most key ranges an item is split into: ranges of at least 128 keys, at most 16
-inline int attn_s_max(int N) { return N / 128 > 1 ? (N / 128 < 16 ? N / 128 : 16) : 1; }
+// Most key ranges an item is split into: ranges of at least 64 keys (two 32-key blocks, so a
+// unit's blocks are nearly all in flight at once), at most 16
+inline int attn_s_max(int N) { return N / kKB > 1 ? (N / kKB < 16 ? N / kKB : 16) : 1; }
 
 __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
   const int whole = (N + kKB - 1) / kKB * kKB;
@@ -1289,22 +1413,29 @@ int gemm_slots() {
   return 2 * kCUs;  // two workgroups per CU (64-72 KB of LDS each)
 }
 
+// A row capacity of at most 64 takes the weight-streaming kernel (its grid is one workgroup per
+// CU); otherwise the persistent two-per-CU kernel, which picks its tile shape on the device.
 template <int EPI>
-void launch_gemm(const GemmArgs& ga, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm<EPI>), dim3(gemm_slots()), dim3(256), 0, s, ga);
+void launch_gemm(const GemmArgs& ga, hipStream_t s, int M_cap) {
+  if (M_cap <= CfgStream::BM)
+    hipLaunchKernelGGL((k_gemm_stream<EPI>), dim3(kStreamSlots), dim3(256), 0, s, ga);
+  else
+    hipLaunchKernelGGL((k_gemm<EPI>), dim3(gemm_slots()), dim3(256), 0, s, ga);
 }
 
 // The fixup is launched unless the host can tell that the projection will not split: with a row
-// capacity of at most 64, every device row count takes the 64 x 64 tiles with one row tile, so the
-// split plan is the same for all of them.
+// capacity of at most 64, every device row count takes the streaming kernel's 64 x 128 tiles with
+// one row tile, so the split plan is the same for all of them.
 template <int EPI>
 void launch_fixup(const GemmArgs& ga, hipStream_t s, int M_cap) {
-  if (M_cap <= CfgSkinny::BM) {
-    const int NT = EPI == EPI_SWIGLU ? ga.Nout / (CfgSkinny::BN / 2)
-                                     : (ga.Nout + CfgSkinny::BN - 1) / CfgSkinny::BN;
-    const SplitPlan sp = plan_split(NT, gemm_slots(), ga.K / CfgSkinny::BK,
-                                    split_mode<EPI, CfgSkinny>());
+  if (M_cap <= CfgStream::BM) {
+    const int NT = EPI == EPI_SWIGLU ? ga.Nout / (CfgStream::BN / 2)
+                                     : (ga.Nout + CfgStream::BN - 1) / CfgStream::BN;
+    const SplitPlan sp = plan_split(NT, kStreamSlots, ga.K / CfgStream::BK,
+                                    split_mode<EPI, CfgStream>());
     if (sp.rem == 0) return;
+    hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, kStreamSlots);
+    return;
   }
   hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, gemm_slots());
 }
@@ -1471,9 +1602,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.rope_dh = P.rope_dh;
   ga.rope = P.rope;
   if (P.rope_dh > 0)
-    launch_gemm<EPI_QKV_ROPE>(ga, s);
+    launch_gemm<EPI_QKV_ROPE>(ga, s, L.M_cap);
   else
-    launch_gemm<EPI_QKV>(ga, s);
+    launch_gemm<EPI_QKV>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   if (P.rope_dh > 0)
@@ -1512,26 +1643,43 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.x = x;
   ga.a = P.a;
 
-  launch_gemm<EPI_RESID>(ga, s);
+  launch_gemm<EPI_RESID>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  launch_fixup<EPI_RESID>(ga, s, L.M_cap);
+  // RMSNorm before the FFN -> an (reuses the xn buffer). Rows of up to 4096 values with a row
+  // capacity above 64: the output projection's split tiles are finished inside the RMSNorm kernel
+  // (no fixup launch; stage 6 is then empty). At most 64 rows (every tile split in up to 16
+  // pieces, one wave per row would walk 16 dependent piece loads per column group; measured 28 us
+  // against 10 us for the two launches) and wider rows take the fixup and the plain RMSNorm.
+  const uint16_t* gf_ = static_cast<const uint16_t*>(w->g_ffn);
+  const int rnc = L.M_cap <= CfgStream::BM ? 0 : rms_nc(d, true);
+  const int o_slots = gemm_slots();
+  if (rnc == 0) launch_fixup<EPI_RESID>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-
-  // RMSNorm before the FFN -> an (reuses the xn buffer)
   {
-    const uint16_t* gf_ = static_cast<const uint16_t*>(w->g_ffn);
 #define DCU_RMS(NC)                                                                        \
   hipLaunchKernelGGL(k_rmsnorm_f32<NC>, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr, gf_, d, \
                      w->rms_eps, P.xn, rows_done, int(B), P.seq_off, P.rowmap)
-    switch (rms_nc(d, true)) {
-      case 1: DCU_RMS(1); break;
-      case 2: DCU_RMS(2); break;
-      case 4: DCU_RMS(4); break;
-      case 8: DCU_RMS(8); break;
-      default: DCU_RMS(0); break;
+#define DCU_RESID_RMS(NC)                                                                  \
+  hipLaunchKernelGGL(k_resid_rmsnorm<NC>, dim3(norm_blocks), dim3(256), 0, s, ga, o_slots, gf_, \
+                     w->rms_eps, P.xn, rows_done, int(B), P.seq_off)
+    switch (rnc) {
+      case 1: DCU_RESID_RMS(1); break;
+      case 2: DCU_RESID_RMS(2); break;
+      case 4: DCU_RESID_RMS(4); break;
+      case 8: DCU_RESID_RMS(8); break;
+      default:
+        switch (rms_nc(d, true)) {
+          case 1: DCU_RMS(1); break;
+          case 2: DCU_RMS(2); break;
+          case 4: DCU_RMS(4); break;
+          case 8: DCU_RMS(8); break;
+          default: DCU_RMS(0); break;
+        }
+        break;
     }
+#undef DCU_RESID_RMS
 #undef DCU_RMS
   }
   DCU_LAUNCH_CHECK();
@@ -1543,7 +1691,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = d;
   ga.Nout = F;
   ga.h = P.h;
-  launch_gemm<EPI_SWIGLU>(ga, s);
+  launch_gemm<EPI_SWIGLU>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_SWIGLU>(ga, s, L.M_cap);
@@ -1556,7 +1704,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.K = F;
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(y_out);
-  launch_gemm<EPI_DOWN>(ga, s);
+  launch_gemm<EPI_DOWN>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
   launch_fixup<EPI_DOWN>(ga, s, L.M_cap);
@@ -1615,7 +1763,7 @@ extern "C" int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, i
   ga.K = d;
   ga.Nout = d;
   ga.y = static_cast<uint16_t*>(v_out);
-  launch_gemm<EPI_VPROJ>(ga, s);
+  launch_gemm<EPI_VPROJ>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   launch_fixup<EPI_VPROJ>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
@@ -1685,11 +1833,11 @@ extern "C" int dcu_attention_context(const dcu_layer* w, const void* x_in, int32
   ga.rope_dh = P.rope_dh;
   ga.rope = P.rope;
   if (P.rope_dh > 0) {
-    launch_gemm<EPI_QKV_ROPE>(ga, s);
+    launch_gemm<EPI_QKV_ROPE>(ga, s, L.M_cap);
     DCU_LAUNCH_CHECK();
     launch_fixup<EPI_QKV_ROPE>(ga, s, L.M_cap);
   } else {
-    launch_gemm<EPI_QKV>(ga, s);
+    launch_gemm<EPI_QKV>(ga, s, L.M_cap);
     DCU_LAUNCH_CHECK();
     launch_fixup<EPI_QKV>(ga, s, L.M_cap);
   }

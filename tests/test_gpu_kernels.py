@@ -479,6 +479,37 @@ def test_distance_rows_equals_full_distance_and_rolls(bf16):
     assert np.array_equal(got.cpu().numpy().view(np.uint32), full.cpu().numpy().view(np.uint32))
     assert torch.equal(xp2.view(torch.uint8) if bf16 else xp2, xc.view(torch.uint8) if bf16 else xc)
     assert float(got[1].abs().sum()) == 0.0
+    # every position is written (an output full of NaN beforehand), also with the lists shuffled
+    # and out-of-range entries among the counted ones
+    sel2 = sel.copy()
+    cnt2 = cnt.copy()
+    for b in range(B):
+        lst = np.concatenate([sel[b, :cnt[b]], np.array([-1, N, 7 * N], np.int32)[: min(3, N - cnt[b])]])
+        g.shuffle(lst)
+        sel2[b, :len(lst)] = lst
+        cnt2[b] = len(lst)
+    out = torch.full((B, N), float("nan"), dtype=torch.float32, device="cuda")
+    xp3 = xp.clone()
+    got2 = stc.dcu_distance_rows(xc, xp3, dev(sel2), dev(cnt2), dist=out, roll=True)
+    assert np.array_equal(got2.cpu().numpy().view(np.uint32), full.cpu().numpy().view(np.uint32))
+    assert torch.equal(xp3.view(torch.uint8) if bf16 else xp3, xc.view(torch.uint8) if bf16 else xc)
+
+
+def test_distance_rows_longest_sequence():
+    """N = 65536 (the bitmap's limit): 200 listed rows spread over the sequence, the rest exact 0."""
+    g = synth.rng(970, 7)
+    N, d = 65536, 64
+    prev = synth.normal_bf16(g, (1, N, d))
+    cur = prev.copy()
+    rows = np.sort(g.choice(N, 200, replace=False))
+    cur[0, rows] = synth.f32_to_bf16(synth.bf16_to_f32(prev[0, rows]) + np.float32(0.1))
+    sel = np.full((1, N), -1, np.int32)
+    sel[0, :200] = rows
+    xc, xp = dev_bf16(cur), dev_bf16(prev)
+    full, _ = stc.dcu_distance(xc, xp, want_mean=False)
+    out = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+    got = stc.dcu_distance_rows(xc, xp.clone(), dev(sel), dev(np.array([200], np.int32)), dist=out)
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), full.cpu().numpy().view(np.uint32))
 
 
 def test_commit_positions():
