@@ -202,6 +202,10 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
                                                         Ptrs P) {
   __shared__ int off[kMaxSeqs + 1];
   __shared__ int scan_lds[17];
+  // one sequence: this wave's first row r is slot r of the list, so its position is loaded with
+  // the count instead of after it (r < M_cap <= N keeps the load in bounds)
+  const int r_first = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int pos_first = (B == 1 && sel_idx && r_first < N) ? sel_idx[r_first] : 0;
   row_offsets(sel_count, B, N, M_cap, off, scan_lds);
   const int M = off[B];
   if (blockIdx.x == 0) {
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
       if (off[mid] <= r) lo = mid; else hi = mid - 1;
     }
     const int b = lo, j = r - off[b];
-    const int pos = sel_idx ? sel_idx[int64_t(b) * N + j] : j;
+    const int pos = !sel_idx ? j : (B == 1 && r == r_first ? pos_first : sel_idx[int64_t(b) * N + j]);
     // a listed position outside [0, N) is skipped: its row map entry is -1, its normalised row is
     // zero, and every later stage leaves the caches and the output alone for it
     const bool valid = pos >= 0 && pos < N;
@@ -1211,7 +1215,25 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
       issue(std::integral_constant<int, NXT>{}, j + ST - 1);
       compute(cur, j);
     };
-    if (nblk > 0) {
+    if (nblk > 0 && nblk <= ST) {
+      // a short unit (split ranges of few blocks): all its blocks are issued at once, one buffer
+      // each, and consumed in order without refills (one DMA latency instead of one per block)
+      issue(I0{}, 0);
+      if (nblk > 1) issue(I1{}, 1);
+      if constexpr (ST == 3) { if (nblk > 2) issue(I2{}, 2); }
+      auto consume = [&](auto cur, int j) {
+        // blocks j+1 .. nblk-1 may still be in flight
+        if (nblk - 1 - j >= 2) gemm::wait_vm_lgkm0<2 * 2 * NQ>();
+        else if (nblk - 1 - j == 1) gemm::wait_vm_lgkm0<2 * NQ>();
+        else gemm::wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        compute(cur, j);
+      };
+      consume(I0{}, 0);
+      if (nblk > 1) consume(I1{}, 1);
+      if constexpr (ST == 3) { if (nblk > 2) consume(I2{}, 2); }
+      __builtin_amdgcn_s_barrier();  // every wave is done with the buffers before the next unit
+    } else if (nblk > 0) {
       issue(I0{}, 0);
       if constexpr (ST == 3) issue(I1{}, 1);
       for (int j = 0; j < nblk; j += ST) {
@@ -1346,7 +1368,8 @@ Layout make_layout(const dcu_layer* w, int B, int N, int max_rows) {
   Layout L{};
   const int64_t BN = int64_t(B) * N;
   L.M_cap = int(max_rows <= 0 || max_rows > BN ? BN : max_rows);
-  L.Tq_max = (L.M_cap + kQTile - 1) / kQTile + B;
+  // query tiles: sum over sequences of ceil(rows_b / kQTile) <= ceil(M / kQTile) + B - 1
+  L.Tq_max = (L.M_cap + kQTile - 1) / kQTile + B - 1;
   const size_t d = size_t(w->d), F = size_t(w->ffn), M = size_t(L.M_cap);
   size_t off = 0;
   auto take = [&](size_t bytes) {
