@@ -432,11 +432,15 @@ using CfgSmall = gemm::Cfg<128, 128, 64, 64, 2, 4>;
 // workgroups per CU) for the same LDS budget.
 using CfgSkinny = gemm::Cfg<64, 64, 32, 32, 4, 4>;
 // When the caller's row bound is at most 64 (one sequence: budget plus window) the host launches a
-// kernel of its own for the weight stream: 64 x 128 tiles (twice the weight rows per activation
-// row fetched), four stages, one workgroup per CU with 96 KB of LDS. Measured on the batch-1
-// shapes with cold weights: QKV 25.5 -> 22.6 us, output 10.8 -> 9.7, gate/up 45.3 -> 38.7, down
-// 23.9 -> 21.7 against the 64 x 64 tiles at two workgroups per CU.
+// kernel of its own for the weight stream, one workgroup per CU with four stages: gate/up on
+// 64 x 128 tiles (twice the weight rows per activation row fetched, 96 KB of LDS), the others on
+// 64 x 64 tiles. Measured on the batch-1 shapes with cold weights, GEMM + split fixup, against the
+// 64 x 64 tiles at two workgroups per CU: gate/up 48.9 -> 41.8 us (64 x 128), QKV 28.0 -> 26.5 (64 x
+// 64, no K split, so no fixup), output 15.4 -> 11.7, down 28.1 -> 24.8; 64 x 128 tiles for the
+// other three were slower (25.2, 14.1 and 26.2).
 using CfgStream = gemm::Cfg<64, 128, 32, 64, 4, 4>;
+template <int EPI>
+using StreamCfg = typename std::conditional<EPI == EPI_SWIGLU, CfgStream, CfgSkinny>::type;
 constexpr int kStreamSlots = 256;  // one workgroup per CU
 static_assert(CfgStream::BM * CfgStream::BN * kStreamSlots <=
                   CfgSkinny::BM * CfgSkinny::BN * 2 * 256,
@@ -677,10 +681,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs g) {
 // at most 64 as well), one workgroup per CU
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_stream(GemmArgs g) {
-  __shared__ u32x4 smem[CfgStream::STAGES * CfgStream::CHUNKS];
+  __shared__ u32x4 smem[StreamCfg<EPI>::STAGES * StreamCfg<EPI>::CHUNKS];
   const int M = g.hdr[kHdrM];
   if (M <= 0) return;
-  gemm_body<EPI, CfgStream>(g, M, smem);
+  gemm_body<EPI, StreamCfg<EPI>>(g, M, smem);
 }
 
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
@@ -817,7 +821,7 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
   const int M = g.hdr[kHdrM];
   if (M <= 0) return;
   if (slots == kStreamSlots)
-    fixup_body<EPI, CfgStream>(g, M, slots);
+    fixup_body<EPI, StreamCfg<EPI>>(g, M, slots);
   else if (use_skinny(M))
     fixup_body<EPI, CfgSkinny>(g, M, slots);
   else
@@ -1452,10 +1456,9 @@ void launch_gemm(const GemmArgs& ga, hipStream_t s, int M_cap) {
 template <int EPI>
 void launch_fixup(const GemmArgs& ga, hipStream_t s, int M_cap) {
   if (M_cap <= CfgStream::BM) {
-    const int NT = EPI == EPI_SWIGLU ? ga.Nout / (CfgStream::BN / 2)
-                                     : (ga.Nout + CfgStream::BN - 1) / CfgStream::BN;
-    const SplitPlan sp = plan_split(NT, kStreamSlots, ga.K / CfgStream::BK,
-                                    split_mode<EPI, CfgStream>());
+    using C = StreamCfg<EPI>;
+    const int NT = EPI == EPI_SWIGLU ? ga.Nout / (C::BN / 2) : (ga.Nout + C::BN - 1) / C::BN;
+    const SplitPlan sp = plan_split(NT, kStreamSlots, ga.K / C::BK, split_mode<EPI, C>());
     if (sp.rem == 0) return;
     hipLaunchKernelGGL((k_gemm_fixup<EPI>), dim3(2048), dim3(256), 0, s, ga, kStreamSlots);
     return;
