@@ -286,6 +286,55 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, mfma_dir, bench_json, s
     print(out2)
 
 
+def summarize_trace(ktrace_dir, bench_json, steps, cmd, out_name, title):
+    """Kernel-trace summary of one workload (durations only). Every step starts with the budget
+    kernel, so the timed region runs from the start of the last `steps` budget launches to the end
+    of the trace (a --profile run stops after the timed steps); per kernel of the library, its
+    launches per step and average duration inside that window."""
+    import csv
+    import glob
+    import re
+
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(ktrace_dir, "*_kernel_trace.csv"))[0])))
+    rows = [r for r in rows if "dcu::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    bj = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    budgets = [r for r in rows if "::k_budget" in r["Kernel_Name"]]
+    t0 = int(budgets[-steps]["Start_Timestamp"])
+    window = [r for r in rows if int(r["Start_Timestamp"]) >= t0]
+    t1 = max(int(r["End_Timestamp"]) for r in window)
+    by = {}
+    for r in window:
+        m = re.search(r"::(k_\w+(<[^>]*>)?)", r["Kernel_Name"])
+        name = m.group(1) if m else r["Kernel_Name"][:40]
+        by.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    order = []
+    for r in window:
+        m = re.search(r"::(k_\w+(<[^>]*>)?)", r["Kernel_Name"])
+        name = m.group(1) if m else r["Kernel_Name"][:40]
+        if name not in order:
+            order.append(name)
+    lines = [f"# {title}", "", "Kernel trace command (run from the repository root):", "", "    " + cmd, "",
+             f"The last {steps} steps of the run (from their first budget launch to the end of the "
+             f"trace: {(t1 - t0) / 1e3 / steps:.1f} us per step). Bench line of the traced run: "
+             f"{bj['value']} {bj['unit']}, {bj['ms_per_step']} ms per step, rows per layer "
+             f"{bj['rows_per_layer_min_max']}.", "",
+             "| kernel | launches per step | avg us | us per step |", "|---|---|---|---|"]
+    total = 0.0
+    for name in order:
+        d = by[name]
+        per = len(d) / steps
+        avg = sum(d) / len(d)
+        lines.append(f"| `{name}` | {per:g} | {avg:.2f} | {avg * per:.1f} |")
+        total += avg * per
+    lines += ["", f"Sum of kernel durations per step: {total:.1f} us; the rest of the step time is the "
+                  "gaps between dependent launches.", ""]
+    out = os.path.join(ROOT, "profiles", out_name)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def torch_dense_layer(w, x, eps):
     """PyTorch reference of the dense layer (every row recomputed), a cross-check outside the
     library: vendor GEMMs (torch.nn.functional.linear on 2-D operands) and attention as two
@@ -323,6 +372,11 @@ def torch_dense_layer(w, x, eps):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        # ktrace_dir bench_json steps cmd out_name title
+        a = sys.argv[2:]
+        summarize_trace(a[0], a[1], int(a[2]), a[3], a[4], a[5])
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # ktrace_dir fetch_dir write_dir mfma_dir bench_json steps cmd_trace cmd_fetch cmd_write cmd_mfma
         a = sys.argv[2:]
