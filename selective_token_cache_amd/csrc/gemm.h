@@ -28,6 +28,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -68,6 +69,22 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N - 1>{}), in order
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Wait for every memory access the compiler tracks (the previous tile's epilogue loads and stores)
+// before a main loop starts. The DMAs are asm the compiler does not count; if a tracked access were
+// still pending at the loop head, the compiler's own wait for it (vmcnt 0, which also drains the
+// DMAs in flight) would land inside the K loop and serialise the stages.
+__device__ __forceinline__ void wait_tracked_memory() { wait_vm_lgkm0<0>(); }
+
 // chunk c of activation row r in a stage buffer (8 16-byte chunks per row)
 __device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
 
@@ -87,7 +104,7 @@ struct Cfg {
   static_assert(ROWS % (ROWS_PER_DMA * NW) == 0, "rows per stage");
   static_assert(BM % (ROWS_PER_DMA * NW) == 0, "activation / weight DMA split by instruction");
   static_assert(BN % 16 == 0 && WN % 16 == 0, "whole 16-row weight blocks");
-  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(STAGES >= 2 && STAGES <= 8, "stages");
   static_assert((STAGES - 2) * NQ < 64, "vmcnt range");
   using acc_t = f32x4;
 };
@@ -133,12 +150,13 @@ struct GateUpBlocks {
   __device__ __forceinline__ int tiles() const { return F / (BN / 2); }
 };
 
-// Per-lane global sources of a wave's NQ DMA instructions for K-tile 0 of the range; instruction i
+// Per-lane global sources of a wave's NQ DMA instructions for K-tile kt0 of the range; instruction i
 // advances by dma_step<C>(i) elements per K-tile. Instructions i < NQA load 8 activation rows
-// (row-major, swizzled chunks); the others load half a weight block (1 KB, linear).
-template <class C, class WB>
-__device__ __forceinline__ void dma_sources(const uint16_t* (&src)[C::NQ], const uint16_t* A, int M,
-                                            int K, int m0, int n_t, const WB& wb, int kt0) {
+// (row-major, swizzled chunks; arow(r) is the first element of tile row r); the others load half a
+// weight block (1 KB, linear).
+template <class C, class WB, class AR>
+__device__ __forceinline__ void dma_sources_rows(const uint16_t* (&src)[C::NQ], const AR& arow,
+                                                 int n_t, const WB& wb, int kt0) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < C::NQ; ++i) {
@@ -146,15 +164,26 @@ __device__ __forceinline__ void dma_sources(const uint16_t* (&src)[C::NQ], const
     if (i < C::NQA) {
       const int row = q * C::ROWS_PER_DMA + lane / C::RC;
       const int c = (lane % C::RC) ^ (row & 7);
-      int ar = m0 + row;
-      ar = ar < M ? ar : M - 1;
-      src[i] = A + int64_t(ar) * K + c * 8 + kt0 * C::BK;
+      src[i] = arow(row) + c * 8 + kt0 * C::BK;
     } else {
       const int qb = q - C::BM / C::ROWS_PER_DMA;  // weight half-block: block qb / 2, half qb % 2
       src[i] = wb.template block<C::BN>(n_t, qb >> 1) + int64_t(kt0) * kBlockElems +
                (qb & 1) * (kBlockElems / 2) + lane * 8;
     }
   }
+}
+
+// The same for a row-major A of M rows from row m0 (rows past M clamped to row M-1)
+template <class C, class WB>
+__device__ __forceinline__ void dma_sources(const uint16_t* (&src)[C::NQ], const uint16_t* A, int M,
+                                            int K, int m0, int n_t, const WB& wb, int kt0) {
+  dma_sources_rows<C>(
+      src,
+      [&](int row) {
+        const int ar = m0 + row < M ? m0 + row : M - 1;
+        return A + int64_t(ar) * K;
+      },
+      n_t, wb, kt0);
 }
 
 template <class C>
@@ -184,6 +213,7 @@ __device__ __forceinline__ void tile_mainloop(f32x4 (&acc)[C::FM][C::FN], const 
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
+  wait_tracked_memory();
 
   // the wave index as a scalar, so every DMA's LDS base (M0) is computed without readfirstlane
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
@@ -247,6 +277,81 @@ __device__ __forceinline__ void tile_mainloop(f32x4 (&acc)[C::FM][C::FN], const 
   __builtin_amdgcn_s_barrier();
 }
 
+// Hook applied to every activation fragment after its LDS read (none by default): ap(f, k, frag)
+// gets fragment f (0 <= f < FM) of the lane's row, whose 8 elements are columns k .. k+7 of A.
+struct NoAProc {
+  __device__ __forceinline__ void operator()(int, int, u32x4&) const {}
+};
+
+// The same main loop for any stage count (2..8): the STAGES buffers sit at compile-time offsets of
+// one LDS array; the DMA sources come from dma_sources / dma_sources_rows for K-tile kt0. Used by
+// the weight stream of a few rows (one workgroup per CU).
+template <class C, class AP>
+__device__ __forceinline__ void tile_mainloop_deep(f32x4 (&acc)[C::FM][C::FN],
+                                                   const uint16_t* const (&src0)[C::NQ],
+                                                   u32x4* smem, int kt0, int kt1, AP& ap) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+  const int KT = kt1 - kt0;
+  const uint16_t* src[C::NQ];
+#pragma unroll
+  for (int i = 0; i < C::NQ; ++i) src[i] = src0[i];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
+  wait_tracked_memory();
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  auto issue = [&](auto sidx, int kt) {
+    u32x4* buf = smem + decltype(sidx)::value * C::CHUNKS;
+    const int kc = kt < KT ? kt : KT - 1;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      const int q = i * C::NW + wid_s;
+      dma16(static_cast<const void*>(src[i] + int64_t(kc) * dma_step<C>(i)),
+            uint32_t(reinterpret_cast<uintptr_t>(DCU_LDS_PTR(buf + q * 64))));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](auto sidx, int kt) {
+    const u32x4* buf = smem + decltype(sidx)::value * C::CHUNKS;
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 32; ++ks) {
+      const int c = ks * 4 + (lane >> 4);
+      u32x4 fw[C::FN], fx[C::FM];
+#pragma unroll
+      for (int f = 0; f < C::FN; ++f) fw[f] = buf[wfrag<C>(wn, f, ks, lane)];
+#pragma unroll
+      for (int f = 0; f < C::FM; ++f) fx[f] = buf[swz(wm * C::WM + f * 16 + (lane & 15), c)];
+#pragma unroll
+      for (int f = 0; f < C::FM; ++f) ap(f, (kt0 + kt) * C::BK + c * 8, fx[f]);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma(fw[j], fx[i], acc[i][j]);
+    }
+  };
+  // prologue: K-tiles 0 .. STAGES-2
+  static_for<C::STAGES - 1>([&](auto s) { issue(s, decltype(s)::value); });
+  for (int kt = 0; kt < KT; kt += C::STAGES) {
+    bool live = true;
+    static_for<C::STAGES>([&](auto cur) {
+      constexpr int S = decltype(cur)::value;
+      if (!live || kt + S >= KT) {
+        live = false;
+        return;
+      }
+      wait_vm_lgkm0<(C::STAGES - 2) * C::NQ>();
+      __builtin_amdgcn_s_barrier();
+      issue(std::integral_constant<int, (S + C::STAGES - 1) % C::STAGES>{}, kt + S + C::STAGES - 1);
+      compute(cur, kt + S);
+    });
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
 // Two-buffer main loop with early refill. A K-tile's fragments are all read into registers right
 // after the barrier that makes the tile visible; a second barrier (after lgkmcnt(0)) then frees its
 // buffer, which is refilled at once with K-tile kt+2 while the MFMAs run. Each DMA thus has two
@@ -267,6 +372,7 @@ __device__ __forceinline__ void tile_mainloop_er(f32x4 (&acc)[C::FM][C::FN], con
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{};
+  wait_tracked_memory();
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   auto issue = [&](auto sidx, int kt) {
     constexpr int S = decltype(sidx)::value;

@@ -105,6 +105,43 @@ __device__ void row_offsets(const int32_t* __restrict__ sel_count, int B, int N,
   __syncthreads();
 }
 
+// The row count, per-sequence row offsets and attention query-tile tables (tiles of 64 query rows
+// per sequence) from the LDS offsets off[0..B], written by one workgroup for the later kernels
+__device__ void publish_plan(const int* off, int B, const Ptrs& P) {
+  const int M = off[B];
+  int toff = 0;
+  for (int b = 0; b < B; ++b) {  // uniform loop
+    const int nt = (off[b + 1] - off[b] + kQTile - 1) / kQTile;
+    for (int j = threadIdx.x; j < nt; j += blockDim.x) P.tile_seq[toff + j] = b;
+    if (threadIdx.x == 0) {
+      P.seq_off[b] = off[b];
+      P.tile_off[b] = toff;
+    }
+    toff += nt;
+  }
+  if (threadIdx.x == 0) {
+    P.seq_off[B] = M;
+    P.tile_off[B] = toff;
+    P.hdr[kHdrM] = M;
+    P.hdr[kHdrTq] = toff;
+  }
+}
+
+// Global cache row of compacted row r (-1 for a listed position outside [0, N)) and its position
+__device__ __forceinline__ int row_of(const int* off, int B, int N, const int32_t* sel_idx, int r,
+                                      int* pos_out) {
+  int lo = 0, hi = B - 1;  // sequence of row r: the last b with off[b] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo, j = r - off[b];
+  const int pos = !sel_idx ? j : sel_idx[int64_t(b) * N + j];
+  const bool valid = pos >= 0 && pos < N;
+  *pos_out = valid ? pos : -1;
+  return valid ? b * N + pos : -1;
+}
+
 // RMSNorm of one row by one wave: out = x * (1 / sqrt(mean(x^2) + eps)) * gain, fp32 arithmetic,
 // bf16 out. NC > 0: the lane's NC 8-element groups (lane, lane + 64, ...) are loaded at once and kept
 // in registers, so the row costs a single round trip to memory; NC == 0: two passes over the row.
@@ -208,24 +245,7 @@ __global__ __launch_bounds__(256) void k_gather_rmsnorm(const uint16_t* __restri
   const int pos_first = (B == 1 && sel_idx && r_first < N) ? sel_idx[r_first] : 0;
   row_offsets(sel_count, B, N, M_cap, off, scan_lds);
   const int M = off[B];
-  if (blockIdx.x == 0) {
-    int toff = 0;
-    for (int b = 0; b < B; ++b) {  // uniform loop; tiles of 64 query rows per sequence
-      const int nt = (off[b + 1] - off[b] + kQTile - 1) / kQTile;
-      for (int j = threadIdx.x; j < nt; j += blockDim.x) P.tile_seq[toff + j] = b;
-      if (threadIdx.x == 0) {
-        P.seq_off[b] = off[b];
-        P.tile_off[b] = toff;
-      }
-      toff += nt;
-    }
-    if (threadIdx.x == 0) {
-      P.seq_off[B] = M;
-      P.tile_off[B] = toff;
-      P.hdr[kHdrM] = M;
-      P.hdr[kHdrTq] = toff;
-    }
-  }
+  if (blockIdx.x == 0) publish_plan(off, B, P);
   const int lane = threadIdx.x & (kWave - 1);
   for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
     // sequence of row r: the last b with off[b] <= r
@@ -494,33 +514,43 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         *reinterpret_cast<uint2*>(g.h + int64_t(m) * g.Nout + j) = st;
       }
     }
-  } else if constexpr (EPI == EPI_QKV_ROPE || EPI == EPI_DOWN) {
-    // Every load of these epilogues (row map, rotary table, fp32 a) is issued before the first
-    // store: loads and stores share one memory counter, so a load issued after a store also waits
-    // for the store. (Measured faster for these two; the others keep their loads next to the
-    // stores.)
-    int64_t grow[C::FM];
+  } else {
+    // Every load of the epilogue (the row map, then the rotary table, the fp32 a or the residual
+    // rows that depend on it) is issued before the first store, unconditionally, at addresses
+    // clamped into the buffers (row M-1 for rows past M, the last column group for columns past
+    // Nout, row 0 of x for a skipped position): loads and stores share one memory counter, so a load
+    // issued after a store also waits for the store, and a load under a branch is waited for inside
+    // that branch (a chain of round trips). Values read for rows or columns that are not stored are
+    // never used.
+    int grow[C::FM];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
-      grow[fm] = m < M ? int64_t(g.rowmap[m]) : 0;
+      grow[fm] = g.rowmap[m < M ? m : M - 1];
     }
-    // EPI_QKV_ROPE: (cos, sin) of the pairs of fragment pair fn/2 (two float4 each);
-    // EPI_DOWN: fp32 a of each fragment
-    float4 opnd[C::FM][C::FN];
+    constexpr bool kF4 = EPI == EPI_QKV_ROPE || EPI == EPI_DOWN;
+    float4 opnd[kF4 ? C::FM : 1][kF4 ? C::FN : 1];
+    uint2 xres[EPI == EPI_RESID ? C::FM : 1][EPI == EPI_RESID ? C::FN : 1];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
+      const int mc = m < M ? m : M - 1;
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
-        opnd[fm][fn] = make_float4(0.f, 0.f, 0.f, 0.f);
         if constexpr (EPI == EPI_QKV_ROPE) {
+          // (cos, sin) of the pairs of fragment pair fn/2 (two float4 each); every column index
+          // maps into the row's table
           const int n = n_t * C::BN + wn * C::WN + (fn & ~1) * 16 + cg;
-          if (m < M && n < g.Nout) opnd[fm][fn] = rope_cs(g, m, n, fn & 1);
-        } else {
-          const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
-          if (m < M && n < g.Nout)
-            opnd[fm][fn] = *reinterpret_cast<const float4*>(g.a + int64_t(m) * g.d + n);
+          opnd[fm][fn] = rope_cs(g, mc, n, fn & 1);
+        } else if constexpr (EPI == EPI_DOWN) {
+          int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+          n = n < g.Nout ? n : g.Nout - 4;
+          opnd[fm][fn] = *reinterpret_cast<const float4*>(g.a + int64_t(mc) * g.d + n);
+        } else if constexpr (EPI == EPI_RESID) {
+          int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
+          n = n < g.Nout ? n : g.Nout - 4;
+          const int64_t xr = grow[fm] >= 0 ? int64_t(grow[fm]) : 0;
+          xres[fm][fn] = *reinterpret_cast<const uint2*>(g.x + xr * g.d + n);
         }
       }
     }
@@ -529,6 +559,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
     for (int fm = 0; fm < C::FM; ++fm) {
       const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
       if (m >= M) continue;
+      const int64_t gr = int64_t(grow[fm]);
       if constexpr (EPI == EPI_QKV_ROPE) {
         static_assert(C::FN % 2 == 0, "fragment pairs");
 #pragma unroll
@@ -536,7 +567,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
           const int n = n_t * C::BN + wn * C::WN + fp * 16 + cg;
           if (n >= g.Nout) continue;
           const gemm::f32x4 x = acc[fm][fp], y = acc[fm][fp + 1];
-          store_qkv_rope(g, m, grow[fm], n, make_float4(x[0], x[1], x[2], x[3]),
+          store_qkv_rope(g, m, gr, n, make_float4(x[0], x[1], x[2], x[3]),
                          make_float4(y[0], y[1], y[2], y[3]), opnd[fm][fp], opnd[fm][fp + 1]);
         }
       } else {
@@ -544,45 +575,32 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, gemm::f32x4 (&a
         for (int fn = 0; fn < C::FN; ++fn) {
           const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
           if (n >= g.Nout) continue;
-          if (grow[fm] < 0) continue;  // a skipped position: the output keeps its row
           const gemm::f32x4 v = acc[fm][fn];
-          const float4 p = opnd[fm][fn];
-          uint2 st;
-          st.x = pack_bf2(p.x + v[0], p.y + v[1]);
-          st.y = pack_bf2(p.z + v[2], p.w + v[3]);
-          *reinterpret_cast<uint2*>(g.y + grow[fm] * g.d + n) = st;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-      const int m = m0 + wm * C::WM + fm * 16 + (lane & 15);
-      if (m >= M) continue;
-      const int64_t grow = int64_t(g.rowmap[m]);
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) {
-        const int n = n_t * C::BN + wn * C::WN + fn * 16 + cg;
-        if (n >= g.Nout) continue;
-        const gemm::f32x4 v = acc[fm][fn];
-        if constexpr (EPI == EPI_QKV) {
-          store_qkv(g, m, grow, n, v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_RESID) {
-          // a skipped position has no input row: its (unused) residual is taken as 0
-          const uint2 xr = grow >= 0 ? *reinterpret_cast<const uint2*>(g.x + grow * g.d + n)
-                                     : make_uint2(0u, 0u);
-          float4 o;
-          o.x = bf_lo(xr.x) + v[0];
-          o.y = bf_hi(xr.x) + v[1];
-          o.z = bf_lo(xr.y) + v[2];
-          o.w = bf_hi(xr.y) + v[3];
-          *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
-        } else {  // EPI_VPROJ
-          if (grow < 0) continue;
-          uint2 st;
-          st.x = pack_bf2(v[0], v[1]);
-          st.y = pack_bf2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(g.y + grow * g.d + n) = st;
+          if constexpr (EPI == EPI_QKV) {
+            store_qkv(g, m, gr, n, v[0], v[1], v[2], v[3]);
+          } else if constexpr (EPI == EPI_DOWN) {
+            if (gr < 0) continue;  // a skipped position: the output keeps its row
+            const float4 p = opnd[fm][fn];
+            uint2 st;
+            st.x = pack_bf2(p.x + v[0], p.y + v[1]);
+            st.y = pack_bf2(p.z + v[2], p.w + v[3]);
+            *reinterpret_cast<uint2*>(g.y + gr * g.d + n) = st;
+          } else if constexpr (EPI == EPI_RESID) {
+            // a skipped position has no input row: its (unused) residual is taken as 0
+            const uint2 xr = gr >= 0 ? xres[fm][fn] : make_uint2(0u, 0u);
+            float4 o;
+            o.x = bf_lo(xr.x) + v[0];
+            o.y = bf_hi(xr.x) + v[1];
+            o.z = bf_lo(xr.y) + v[2];
+            o.w = bf_hi(xr.y) + v[3];
+            *reinterpret_cast<float4*>(g.a + int64_t(m) * g.d + n) = o;
+          } else {  // EPI_VPROJ
+            if (gr < 0) continue;
+            uint2 st;
+            st.x = pack_bf2(v[0], v[1]);
+            st.y = pack_bf2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(g.y + gr * g.d + n) = st;
+          }
         }
       }
     }
@@ -685,6 +703,234 @@ __global__ __launch_bounds__(256, 1) void k_gemm_stream(GemmArgs g) {
   const int M = g.hdr[kHdrM];
   if (M <= 0) return;
   gemm_body<EPI, StreamCfg<EPI>>(g, M, smem);
+}
+
+// ------------------------------------------------------------------------------ 1+3 fused (few rows)
+// For a row capacity of at most 64 the gather and the RMSNorm run inside the QKV weight stream.
+// Every workgroup evaluates the row offsets and the row map of the <= 64 selected rows itself
+// (workgroup 0 publishes them with the attention tables for the later kernels), its DMA sources
+// are the selected rows of x themselves, and every activation fragment is multiplied by the
+// RMSNorm gains right after its LDS read while the squares of the raw values are summed; the
+// finished tile row is then scaled by the row's 1/sqrt(mean(x^2) + eps):
+//   RMSNorm(x; g) W^T = s * ((x * g) W^T),  s = 1 / sqrt(mean(x^2) + eps) per row
+// (x * g rounded to bf16 for the MFMA, where the two-launch form rounds x * s * g). The rotary
+// (cos, sin) table of the workgroup's rows is built in LDS. Tiles run whole (no K split), one
+// workgroup per CU. This removes the gather launch and the normalised rows' round trip through
+// memory.
+constexpr int kFusedMaxD = 8192;      // model width whose gains fit the LDS copy
+constexpr int kFusedMaxRopeDh = 128;  // rotary head_dim whose (cos, sin) table fits LDS
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_qkv_fused(GemmArgs g, Ptrs P,
+                                                      const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ sel_idx,
+                                                      const int32_t* __restrict__ sel_count,
+                                                      int B, int N, int M_cap,
+                                                      const uint16_t* __restrict__ gain,
+                                                      float eps) {
+  using C = CfgSkinny;
+  static_assert(C::BM == 64 && C::BK == 64, "one row tile of 64");
+  __shared__ u32x4 smem[C::STAGES * C::CHUNKS];
+  __shared__ int off[kMaxSeqs + 1];
+  __shared__ int scan_lds[17];
+  __shared__ int s_row[C::BM], s_pos[C::BM];
+  __shared__ u32x4 s_gain[kFusedMaxD / 8];
+  __shared__ float2 s_rope[EPI == EPI_QKV_ROPE ? C::BM * (kFusedMaxRopeDh / 2) : 1];
+  const int d = g.d;
+  // the gains first: their loads overlap the plan below
+  for (int i = threadIdx.x; i < d / 8; i += blockDim.x)
+    s_gain[i] = reinterpret_cast<const u32x4*>(gain)[i];
+  row_offsets(sel_count, B, N, M_cap, off, scan_lds);
+  const int M = off[B];
+  if (blockIdx.x == 0) publish_plan(off, B, P);
+  if (M <= 0) return;
+  if (int(threadIdx.x) < M) {
+    int pos;
+    const int grow = row_of(off, B, N, sel_idx, threadIdx.x, &pos);
+    s_row[threadIdx.x] = grow;
+    s_pos[threadIdx.x] = pos;
+    if (blockIdx.x == 0) P.rowmap[threadIdx.x] = grow;
+  }
+  __syncthreads();
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    const int hp = g.rope_dh / 2;
+    for (int e = threadIdx.x; e < M * hp; e += blockDim.x) {
+      const int r = e / hp, i = e - r * hp;
+      const int pos = s_pos[r];
+      float sn = 0.0f, cs = 1.0f;
+      if (pos >= 0) sincosf(rope_angle(float(pos), i, g.rope_dh, P.rope_l2t), &sn, &cs);
+      s_rope[e] = make_float2(cs, sn);
+    }
+  }
+  __syncthreads();
+  GemmArgs lg = g;
+  lg.rowmap = s_row;
+  lg.rope = s_rope;
+  const gemm::PlainBlocks wr{g.W, g.Nout, g.K / C::BK};
+  const int NT = wr.template tiles<C::BN>();
+  for (int n_t = blockIdx.x; n_t < NT; n_t += gridDim.x) {
+    const uint16_t* src[C::NQ];
+    gemm::dma_sources_rows<C>(
+        src,
+        [&](int row) {
+          const int grow = s_row[row < M ? row : M - 1];
+          return x + int64_t(grow >= 0 ? grow : 0) * d;  // a skipped position reads row 0 (unused)
+        },
+        n_t, wr, 0);
+    float ss[C::FM];
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) ss[f] = 0.0f;
+    // x * g for the MFMA, sum of x^2 of the lane's row (columns k .. k+7)
+    auto gain_sumsq = [&](int f, int k, u32x4& fx) {
+      const u32x4 gg = s_gain[k >> 3];
+      const uint32_t xw[4] = {fx.x, fx.y, fx.z, fx.w};
+      const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
+      uint32_t o[4];
+      float sq = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = bf_lo(xw[j]), b = bf_hi(xw[j]);
+        sq = fmaf(a, a, sq);
+        sq = fmaf(b, b, sq);
+        o[j] = pack_bf2(a * bf_lo(gw[j]), b * bf_hi(gw[j]));
+      }
+      ss[f] += sq;
+      fx = u32x4{o[0], o[1], o[2], o[3]};
+    };
+    gemm::f32x4 acc[C::FM][C::FN];
+    gemm::tile_mainloop_deep<C>(acc, src, smem, 0, g.K / C::BK, gain_sumsq);
+    // the four lanes of a row (lane >> 4) hold its four column chunks of every K-tile
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) {
+      float t = ss[f];
+      t += __shfl_xor(t, 16, kWave);
+      t += __shfl_xor(t, 32, kWave);
+      const float scale = 1.0f / sqrtf(t / float(d) + eps);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) acc[f][j] *= scale;
+    }
+    gemm_epilogue<EPI, C>(lg, acc, M, 0, n_t);
+  }
+}
+
+// The output projection's split tiles finished together with the RMSNorm before the FFN for a row
+// capacity of at most 64: one workgroup per row, each thread holding PER 8-column groups. A group
+// comes from a (a whole tile) or is the residual plus the fixed-order sum of its tile's fp32 pieces
+// (k_gemm_fixup's order); the pieces of all the thread's groups are loaded in rounds of four, the
+// first round together with the residual and the gains. The sum of squares is reduced over the
+// workgroup in a fixed order. With rows_done, also the per-sequence count of recomputed rows.
+template <int PER>
+__global__ __launch_bounds__(256) void k_resid_rmsnorm_row(GemmArgs g,
+                                                           const uint16_t* __restrict__ gain,
+                                                           float eps, uint16_t* __restrict__ out,
+                                                           int32_t* __restrict__ rows_done, int B,
+                                                           const int* __restrict__ seq_off) {
+  using C = StreamCfg<EPI_RESID>;
+  const int M = g.hdr[kHdrM];
+  if (rows_done && blockIdx.x == 0) {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      int n = 0;
+      for (int r = seq_off[b]; r < seq_off[b + 1]; ++r) n += g.rowmap[r] >= 0 ? 1 : 0;
+      rows_done[b] = n;
+    }
+  }
+  if (M <= 0) return;
+  const int d = g.d, groups = d / 8;
+  const int MT = (M + C::BM - 1) / C::BM;
+  const int NT = (g.Nout + C::BN - 1) / C::BN;
+  const SplitPlan sp = plan_split(MT * NT, kStreamSlots, g.K / C::BK, split_mode<EPI_RESID, C>());
+  constexpr int kTile = C::BM * C::BN;
+  constexpr int kRound = 4;
+  __shared__ float red[4];
+  const int t = threadIdx.x, wid = t / kWave;
+  for (int r = blockIdx.x; r < M; r += gridDim.x) {
+    const int m_t = r / C::BM, rl = r - m_t * C::BM;
+    const int64_t grow = int64_t(g.rowmap[r]);
+    float* arow = g.a + int64_t(r) * d;
+    float4 lo[PER], hi[PER];
+    uint4 xr[PER], gg[PER];
+    bool split[PER];
+    const float* p0[PER];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int gi = t + c * 256;
+      split[c] = false;
+      p0[c] = nullptr;
+      lo[c] = hi[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      xr[c] = gg[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (gi >= groups) continue;
+      const int col = gi * 8, n_t = col / C::BN;
+      gg[c] = reinterpret_cast<const uint4*>(gain)[gi];
+      if (n_t * MT + m_t < sp.full) {
+        lo[c] = *reinterpret_cast<const float4*>(arow + col);
+        hi[c] = *reinterpret_cast<const float4*>(arow + col + 4);
+      } else {
+        split[c] = true;
+        p0[c] = g.part + int64_t(n_t * MT + m_t - sp.full) * sp.S * kTile + rl * C::BN +
+                (col - n_t * C::BN);
+        if (grow >= 0) xr[c] = *reinterpret_cast<const uint4*>(g.x + grow * d + col);
+      }
+    }
+    for (int s0 = 0; s0 < sp.S; s0 += kRound) {
+      float4 q0[PER][kRound], q1[PER][kRound];
+#pragma unroll
+      for (int c = 0; c < PER; ++c)
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+          if (split[c] && s0 + j < sp.S) {
+            const float* q = p0[c] + int64_t(s0 + j) * kTile;
+            q0[c][j] = *reinterpret_cast<const float4*>(q);
+            q1[c][j] = *reinterpret_cast<const float4*>(q + 4);
+          }
+#pragma unroll
+      for (int c = 0; c < PER; ++c)
+#pragma unroll
+        for (int j = 0; j < kRound; ++j)
+          if (split[c] && s0 + j < sp.S) {
+            if (s0 + j == 0) {
+              lo[c] = q0[c][j];
+              hi[c] = q1[c][j];
+            } else {
+              lo[c].x += q0[c][j].x; lo[c].y += q0[c][j].y; lo[c].z += q0[c][j].z; lo[c].w += q0[c][j].w;
+              hi[c].x += q1[c][j].x; hi[c].y += q1[c][j].y; hi[c].z += q1[c][j].z; hi[c].w += q1[c][j].w;
+            }
+          }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      if (split[c]) {
+        const int col = (t + c * 256) * 8;
+        lo[c] = make_float4(bf_lo(xr[c].x) + lo[c].x, bf_hi(xr[c].x) + lo[c].y,
+                            bf_lo(xr[c].y) + lo[c].z, bf_hi(xr[c].y) + lo[c].w);
+        hi[c] = make_float4(bf_lo(xr[c].z) + hi[c].x, bf_hi(xr[c].z) + hi[c].y,
+                            bf_lo(xr[c].w) + hi[c].z, bf_hi(xr[c].w) + hi[c].w);
+        *reinterpret_cast<float4*>(arow + col) = lo[c];
+        *reinterpret_cast<float4*>(arow + col + 4) = hi[c];
+      }
+      const float v[8] = {lo[c].x, lo[c].y, lo[c].z, lo[c].w, hi[c].x, hi[c].y, hi[c].z, hi[c].w};
+#pragma unroll
+      for (int k = 0; k < 8; k += 2) ss += v[k] * v[k] + v[k + 1] * v[k + 1];
+    }
+    ss = wave_sum(ss);
+    if ((t & (kWave - 1)) == 0) red[wid] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float scale = 1.0f / sqrtf(tot / float(d) + eps);
+    uint16_t* orow = out + int64_t(r) * d;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int gi = t + c * 256;
+      if (gi >= groups) continue;
+      uint4 o;
+      o.x = pack_bf2(lo[c].x * scale * bf_lo(gg[c].x), lo[c].y * scale * bf_hi(gg[c].x));
+      o.y = pack_bf2(lo[c].z * scale * bf_lo(gg[c].y), lo[c].w * scale * bf_hi(gg[c].y));
+      o.z = pack_bf2(hi[c].x * scale * bf_lo(gg[c].z), hi[c].y * scale * bf_hi(gg[c].z));
+      o.w = pack_bf2(hi[c].z * scale * bf_lo(gg[c].w), hi[c].w * scale * bf_hi(gg[c].w));
+      reinterpret_cast<uint4*>(orow)[gi] = o;
+    }
+    __syncthreads();  // red is reused by the next row
+  }
 }
 
 // Sum of a split tail tile's partials in segment order, then the tile's epilogue; 4 columns per
@@ -1626,8 +1872,12 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   if (!mark()) return DCU_EHIP;
 
   const int norm_blocks = (L.M_cap + 3) / 4 < 2048 ? (L.M_cap + 3) / 4 : 2048;
-  {
-    const uint16_t* ga_ = static_cast<const uint16_t*>(w->g_attn);
+  const uint16_t* ga_ = static_cast<const uint16_t*>(w->g_attn);
+  // A row capacity of at most 64: the gather and the RMSNorm run inside the QKV weight stream
+  // (stage 1 and the QKV fixup stage are then empty)
+  const bool fused_qkv = L.M_cap <= CfgSkinny::BM && d <= kFusedMaxD &&
+                         (P.rope_dh == 0 || P.rope_dh <= kFusedMaxRopeDh);
+  if (!fused_qkv) {
 #define DCU_GATHER(NC)                                                                        \
   hipLaunchKernelGGL(k_gather_rmsnorm<NC>, dim3(norm_blocks), dim3(256), 0, s, x, sel_idx,    \
                      sel_count, int(B), int(N), L.M_cap, ga_, d, w->rms_eps, P.xn, P)
@@ -1640,8 +1890,8 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
       default: DCU_GATHER(0); break;
     }
 #undef DCU_GATHER
+    DCU_LAUNCH_CHECK();
   }
-  DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
 
   GemmArgs ga{};
@@ -1659,17 +1909,29 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   ga.vc = static_cast<uint16_t*>(v_cache);
   ga.rope_dh = P.rope_dh;
   ga.rope = P.rope;
-  if (P.rope_dh > 0)
+  if (fused_qkv) {
+    const int qkv_tiles = (3 * d + CfgSkinny::BN - 1) / CfgSkinny::BN;
+    const dim3 grid(unsigned(qkv_tiles < kStreamSlots ? qkv_tiles : kStreamSlots));
+    if (P.rope_dh > 0)
+      hipLaunchKernelGGL(k_qkv_fused<EPI_QKV_ROPE>, grid, dim3(256), 0, s, ga, P, x, sel_idx,
+                         sel_count, int(B), int(N), L.M_cap, ga_, w->rms_eps);
+    else
+      hipLaunchKernelGGL(k_qkv_fused<EPI_QKV>, grid, dim3(256), 0, s, ga, P, x, sel_idx,
+                         sel_count, int(B), int(N), L.M_cap, ga_, w->rms_eps);
+  } else if (P.rope_dh > 0) {
     launch_gemm<EPI_QKV_ROPE>(ga, s, L.M_cap);
-  else
+  } else {
     launch_gemm<EPI_QKV>(ga, s, L.M_cap);
+  }
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  if (P.rope_dh > 0)
-    launch_fixup<EPI_QKV_ROPE>(ga, s, L.M_cap);
-  else
-    launch_fixup<EPI_QKV>(ga, s, L.M_cap);
-  DCU_LAUNCH_CHECK();
+  if (!fused_qkv) {
+    if (P.rope_dh > 0)
+      launch_fixup<EPI_QKV_ROPE>(ga, s, L.M_cap);
+    else
+      launch_fixup<EPI_QKV>(ga, s, L.M_cap);
+    DCU_LAUNCH_CHECK();
+  }
   if (!mark()) return DCU_EHIP;
 
   // attention over the updated caches
@@ -1710,12 +1972,27 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   // rows, each group summing all its tiles' pieces: 17.2 us against 7.1 + 7.7 us for the fixup's
   // 2048 workgroups and the plain RMSNorm at batch 1) and wider rows take the two launches.
   const uint16_t* gf_ = static_cast<const uint16_t*>(w->g_ffn);
+  // at most 64 rows and rows of up to 8192 values: a workgroup per row finishes the split tiles and
+  // normalises (stage 6 empty)
+  const int row_per = L.M_cap <= CfgStream::BM ? (d / 8 + 255) / 256 : 0;
+  const bool row_rms = row_per >= 1 && row_per <= 4;
   const int rnc = L.M_cap <= CfgStream::BM ? 0 : rms_nc(d, true);
   const int o_slots = gemm_slots();
-  if (rnc == 0) launch_fixup<EPI_RESID>(ga, s, L.M_cap);
+  if (rnc == 0 && !row_rms) launch_fixup<EPI_RESID>(ga, s, L.M_cap);
   DCU_LAUNCH_CHECK();
   if (!mark()) return DCU_EHIP;
-  {
+  if (row_rms) {
+#define DCU_ROW_RMS(PER)                                                                      \
+  hipLaunchKernelGGL(k_resid_rmsnorm_row<PER>, dim3(unsigned(L.M_cap)), dim3(256), 0, s, ga, gf_, \
+                     w->rms_eps, P.xn, rows_done, int(B), P.seq_off)
+    switch (row_per) {
+      case 1: DCU_ROW_RMS(1); break;
+      case 2: DCU_ROW_RMS(2); break;
+      case 3: DCU_ROW_RMS(3); break;
+      default: DCU_ROW_RMS(4); break;
+    }
+#undef DCU_ROW_RMS
+  } else {
 #define DCU_RMS(NC)                                                                        \
   hipLaunchKernelGGL(k_rmsnorm_f32<NC>, dim3(norm_blocks), dim3(256), 0, s, P.a, P.hdr, gf_, d, \
                      w->rms_eps, P.xn, rows_done, int(B), P.seq_off, P.rowmap)

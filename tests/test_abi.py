@@ -252,3 +252,19 @@ def test_m0_check_of_the_dma_kernels():
     problems = b.check_m0(bad)
     assert any("M0 used by the compiler" in p for p in problems)
     assert any("reading M0" in p for p in problems)
+
+
+def test_stage_wait_check_of_the_dma_kernels():
+    """The build's scan for full memory waits inside the staged DMA loops: the built listing has
+    none, and one inserted after a stage barrier of the QKV projection is caught."""
+    from selective_token_cache_amd import build as b
+    path = os.path.join(ROOT, "_build", "layer.hip.gfx950.s")
+    if not os.path.exists(path):
+        pytest.skip("assembly listing not built")
+    asm = open(path).read()
+    assert b.check_stage_waits(asm) == []
+    i = asm.index("k_gemmILi5E")
+    j = asm.index("s_barrier", i) + len("s_barrier")
+    bad = asm[:j] + "\n\ts_waitcnt vmcnt(0)" + asm[j:]
+    problems = b.check_stage_waits(bad)
+    assert len(problems) == 1 and "k_gemmILi5E" in problems[0]
