@@ -38,6 +38,7 @@ namespace dcu {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -737,19 +738,27 @@ __global__ __launch_bounds__(256, 1) void k_qkv_fused(GemmArgs g, Ptrs P,
   __shared__ u32x4 s_gain[kFusedMaxD / 8];
   __shared__ float2 s_rope[EPI == EPI_QKV_ROPE ? C::BM * (kFusedMaxRopeDh / 2) : 1];
   const int d = g.d;
-  // the gains first: their loads overlap the plan below
-  for (int i = threadIdx.x; i < d / 8; i += blockDim.x)
-    s_gain[i] = reinterpret_cast<const u32x4*>(gain)[i];
+  // one sequence: thread r's list entry is loaded together with the count (r < M_cap <= N)
+  const int t = threadIdx.x;
+  const int pre = (B == 1 && sel_idx && t < M_cap && t < N) ? sel_idx[t] : 0;
+  // the gains next: their loads overlap the plan below
+  for (int i = t; i < d / 8; i += blockDim.x) s_gain[i] = reinterpret_cast<const u32x4*>(gain)[i];
   row_offsets(sel_count, B, N, M_cap, off, scan_lds);
   const int M = off[B];
   if (blockIdx.x == 0) publish_plan(off, B, P);
   if (M <= 0) return;
-  if (int(threadIdx.x) < M) {
-    int pos;
-    const int grow = row_of(off, B, N, sel_idx, threadIdx.x, &pos);
-    s_row[threadIdx.x] = grow;
-    s_pos[threadIdx.x] = pos;
-    if (blockIdx.x == 0) P.rowmap[threadIdx.x] = grow;
+  if (t < M) {
+    int pos, grow;
+    if (B == 1) {
+      pos = sel_idx ? pre : t;
+      pos = pos >= 0 && pos < N ? pos : -1;
+      grow = pos;
+    } else {
+      grow = row_of(off, B, N, sel_idx, t, &pos);
+    }
+    s_row[t] = grow;
+    s_pos[t] = pos;
+    if (blockIdx.x == 0) P.rowmap[t] = grow;
   }
   __syncthreads();
   if constexpr (EPI == EPI_QKV_ROPE) {
@@ -786,15 +795,14 @@ __global__ __launch_bounds__(256, 1) void k_qkv_fused(GemmArgs g, Ptrs P,
       const uint32_t xw[4] = {fx.x, fx.y, fx.z, fx.w};
       const uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
       uint32_t o[4];
-      float sq = 0.0f;
+      float sq = ss[f];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = bf_lo(xw[j]), b = bf_hi(xw[j]);
-        sq = fmaf(a, a, sq);
-        sq = fmaf(b, b, sq);
-        o[j] = pack_bf2(a * bf_lo(gw[j]), b * bf_hi(gw[j]));
+        const bf16x2 xp = __builtin_bit_cast(bf16x2, xw[j]);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(xp, xp, sq, false);  // + x0^2 + x1^2
+        o[j] = pack_bf2(bf_lo(xw[j]) * bf_lo(gw[j]), bf_hi(xw[j]) * bf_hi(gw[j]));
       }
-      ss[f] += sq;
+      ss[f] = sq;
       fx = u32x4{o[0], o[1], o[2], o[3]};
     };
     gemm::f32x4 acc[C::FM][C::FN];
