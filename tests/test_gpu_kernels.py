@@ -199,6 +199,29 @@ def test_select_candidate_fractions(N, frac):
         _check_select(d, budgets, 1, keys, bw)
 
 
+@pytest.mark.parametrize("N", [64, 3000])
+def test_select_threshold_paths(N):
+    """The radix search's exits: the threshold bin taken whole at the first pass (every key of the
+    top exponent byte), a run of equal keys cut by the budget (the position-order tie ranks after
+    the last pass), no budget, and a budget of every candidate; 256- and 1024-thread workgroups."""
+    _log(f"select threshold paths N={N}")
+    g = synth.rng(907, N)
+    d = np.zeros((4, N), np.float32)
+    for b in range(4):
+        hi = g.choice(N, 10, replace=False)
+        rest = np.setdiff1d(np.arange(N), hi)
+        lo = g.choice(rest, 20, replace=False)
+        d[b, hi] = np.float32(2.0)     # exponent byte 0x40
+        d[b, lo] = np.float32(0.5)     # exponent byte 0x3f
+    # budgets: 10 (the 2.0 keys: their first-pass bin whole), 5 (part of a tie run), 0, 30 (all)
+    budgets = np.array([[10], [5], [0], [30]], np.int32)
+    keys = np.zeros((4, 0), np.int32)
+    sel, cnt = stc.dcu_select(dev(d), dev(budgets), 0, None, 0)
+    rs, rc = osel.select(d, budgets, 0, keys, 0)
+    assert rc.tolist() == [10, 5, 0, 30]
+    assert np.array_equal(cnt.cpu().numpy(), rc) and np.array_equal(sel.cpu().numpy(), rs)
+
+
 def test_select_identical_inputs_give_only_windows():
     d = np.zeros((2, 1024), np.float32)
     budgets = np.full((2, 32), 32, np.int32)
