@@ -277,15 +277,11 @@ __device__ __forceinline__ void tile_mainloop(f32x4 (&acc)[C::FM][C::FN], const 
   __builtin_amdgcn_s_barrier();
 }
 
-// Hook applied to every activation fragment after its LDS read (none by default): ap(f, k, frag)
-// gets fragment f (0 <= f < FM) of the lane's row, whose 8 elements are columns k .. k+7 of A.
-struct NoAProc {
-  __device__ __forceinline__ void operator()(int, int, u32x4&) const {}
-};
-
 // The same main loop for any stage count (2..8): the STAGES buffers sit at compile-time offsets of
 // one LDS array; the DMA sources come from dma_sources / dma_sources_rows for K-tile kt0. Used by
-// the weight stream of a few rows (one workgroup per CU).
+// the weight stream of a few rows (one workgroup per CU). ap(f, k, frag) is applied to every
+// activation fragment after its LDS read: fragment f (0 <= f < FM) of the lane's row, whose 8
+// elements are columns k .. k+7 of A.
 template <class C, class AP>
 __device__ __forceinline__ void tile_mainloop_deep(f32x4 (&acc)[C::FM][C::FN],
                                                    const uint16_t* const (&src0)[C::NQ],

@@ -166,6 +166,24 @@ def test_selective_layer_at_most_64_rows(shape, B, N, counts, max_rows):
     _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
 
 
+@pytest.mark.parametrize("shape,B,N,counts,max_rows,theta", [
+    # rows of 6144 and 8192 values under a row bound of 64: the fused QKV stream (gains of up to
+    # 8192 values in LDS) and the workgroup-per-row fixup + RMSNorm with 3 and 4 groups per thread
+    (synth.LayerShape(d=6144, n_heads=48, head_dim=128, ffn=256), 2, 40, [17, 30], 64, 5e5),
+    (synth.LayerShape(d=8192, n_heads=64, head_dim=128, ffn=256), 1, 48, [33], 48, 0.0),
+    # 8256 values: past both limits, so the gather kernel, the split fixup and the plain RMSNorm run
+    (synth.LayerShape(d=8256, n_heads=129, head_dim=64, ffn=192), 1, 40, [21], 32, 1e4),
+])
+def test_wide_rows_at_most_64_rows(shape, B, N, counts, max_rows, theta):
+    _log(f"layer wide rows d={shape.d} B={B} N={N} max_rows={max_rows}")
+    case = Case(shape, B, N, seed=shape.d + N + 9, theta=theta)
+    sel, cnt = _random_selection(case.g, B, N, counts)
+    (got, got2) = case.run_gpu(sel, cnt, max_rows=max_rows, reps=2)
+    for a, b in zip(got, got2):
+        assert np.array_equal(a, b)
+    _compare(case, got, case.run_oracle(sel, cnt), _rows(sel, cnt, B, N))
+
+
 def test_dense_mode_small():
     shape = synth.LayerShape(d=256, n_heads=2, head_dim=128, ffn=320)
     case = Case(shape, 2, 150, seed=7)
