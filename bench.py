@@ -516,15 +516,18 @@ def main():
             stc.dllm_commit_positions(order, n_commit, slot_pos, N_KEYS, key_pos=keys)
             x_cur[0], x_prev[0] = x_prev[0], x_cur[0]
 
-    def make_events(full):
+    def make_events(full, sample=None):
         """Events of one step: every stage boundary (full), or only the two around the roofline
-        kernel (each recorded event costs device time, so the timed steps carry only those)."""
+        kernel of layer `sample` (each recorded event costs ~4.5 us of device time, so a timed step
+        carries just those two; the sampled layer rotates over the timed steps)."""
         def ev():
             return torch.cuda.Event(enable_timing=True)
         per = []
-        for _ in range(L_):
+        for l in range(L_):
             if full:
                 per.append([ev() for _ in range(n_ev_layer)])
+            elif l != sample:
+                per.append([None] * (n_ev_layer if wl["layers"] else 3))
             elif wl["layers"]:
                 g = [None] * n_ev_layer
                 gi = 2 + stages.index("gate_up_swiglu")
@@ -553,7 +556,7 @@ def main():
     # K steps with only the roofline kernel's events, then a few instrumented steps with an event
     # at every stage boundary for the per-stage table
     K = args.steps
-    evs = [make_events(False) for _ in range(K)]
+    evs = [make_events(False, sample=it % L_) for it in range(K)]
     torch.cuda.synchronize()
     log(f"timing {K} steps")
     t0 = time.perf_counter()
@@ -563,15 +566,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / K * 1e3
-    roof_ms = [0.0] * L_           # roofline kernel time per layer, summed over the timed steps
+    # roofline kernel: one sampled launch per timed step (layer it mod L), its duration from events
+    roof = []                      # (layer, ms) of every sampled launch
     for it in range(K):
-        for l in range(L_):
-            e = evs[it][l]
-            if wl["layers"]:
-                gi = 2 + stages.index("gate_up_swiglu")
-                roof_ms[l] += e[gi].elapsed_time(e[gi + 1])
-            else:
-                roof_ms[l] += e[0].elapsed_time(e[1])
+        l = it % L_
+        e = evs[it][l]
+        if wl["layers"]:
+            gi = 2 + stages.index("gate_up_swiglu")
+            roof.append((l, e[gi].elapsed_time(e[gi + 1])))
+        else:
+            roof.append((l, e[0].elapsed_time(e[1])))
 
     KI = 0 if args.profile else min(K, 5)
     ievs = [make_events(True) for _ in range(KI)]
@@ -723,10 +727,11 @@ def main():
         del zprev
 
     # roofline of the dominant kernel, timed with HIP events on the library's stream
+    n_roof = len(roof)
     if wl["layers"]:
-        gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l in range(L_)) * K
-        gu_time = sum(roof_ms) * 1e-3
-        gu_bytes = (2.0 * F * D * 2) * L_ * K
+        gu_flops = sum(2.0 * int(M_l[l]) * 2 * F * D for l, _ in roof)
+        gu_time = sum(ms for _, ms in roof) * 1e-3
+        gu_bytes = (2.0 * F * D * 2) * n_roof
         if float(M_l.mean()) >= 312:
             # MFMA-bound at these row counts: gate/up projection with the SwiGLU epilogue
             achieved = gu_flops / gu_time / 1e12
@@ -741,24 +746,26 @@ def main():
             roofline = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU)", "bound": "mfma",
                         "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "traffic": traffic, "algorithmic_flops_per_launch": int(gu_flops / (K * L_)),
-                        "avg_launch_us": round(gu_time / (K * L_) * 1e6, 2)}
+                        "traffic": traffic, "algorithmic_flops_per_launch": int(gu_flops / n_roof),
+                        "avg_launch_us": round(gu_time / n_roof * 1e6, 2),
+                        "launches_timed": n_roof}
         else:
             # few rows: the projection streams its weights once per layer-step (HBM-bound)
             achieved = gu_bytes / gu_time / 1e9
             roofline = {"kernel": "k_gemm<EPI_SWIGLU> (gate/up projection + SwiGLU)", "bound": "hbm",
                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                        "algorithmic_bytes_per_launch": int(gu_bytes / (K * L_)),
-                        "avg_launch_us": round(gu_time / (K * L_) * 1e6, 2)}
+                        "algorithmic_bytes_per_launch": int(gu_bytes / n_roof),
+                        "avg_launch_us": round(gu_time / n_roof * 1e6, 2),
+                        "launches_timed": n_roof}
     else:
-        d_ms = sum(roof_ms) / (K * L_)
+        d_ms = sum(ms for _, ms in roof) / n_roof
         d_bytes = 2.0 * B * N * D * 2 + B * N * 4
         roofline = {"kernel": "k_distance (cosine distance)", "bound": "hbm",
                     "achieved": round(d_bytes / (d_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "traffic": None, "algorithmic_bytes_per_launch": int(d_bytes),
-                    "avg_launch_us": round(d_ms * 1e3, 2)}
+                    "avg_launch_us": round(d_ms * 1e3, 2), "launches_timed": n_roof}
 
     # ------------------------------------------------------------------ dense recompute, same shape
     dense = None
