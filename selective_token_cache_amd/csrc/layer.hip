@@ -13,19 +13,23 @@
 //                     counts, the compacted row map (selected row -> global cache row), attention
 //                     query-tile tables, the gather of the selected input rows + RMSNorm -> xn,
 //                     and (rotary layout) each row's (cos, sin) table;
-//  3. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches
-//                     (k_gemm<QKV_ROPE>: the same with the rotation of q and k);
-//  4. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
+//  2. k_gemm<QKV>     xn W_qkv^T; epilogue writes q and scatters k, v straight into the caches
+//                     (k_gemm<QKV_ROPE>: the same with the rotation of q and k); for a row
+//                     capacity of at most 64, k_qkv_fused does 1 and 2 in one weight stream;
+//  3. k_attn<DH>      flash-style attention of each 64-query tile over the cache (split over keys
 //                     when there are too few tiles to fill the chip) + k_attn_combine;
-//  5. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
-//  6. k_resid_rmsnorm the split tiles of a finished (fixed-order sums of the pieces + residual)
-//                     and RMSNorm of a -> an (bf16) in one pass (k_gemm_fixup + k_rmsnorm_f32 for
-//                     rows wider than 4096 or a row capacity of at most 64);
-//  7. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
-//  8. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
+//  4. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
+//  5. k_resid_rmsnorm the split tiles of a finished (fixed-order sums of the pieces + residual)
+//                     and RMSNorm of a -> an (bf16) in one pass (k_resid_rmsnorm_row, a workgroup
+//                     per row, for a row capacity of at most 64; k_gemm_fixup + k_rmsnorm_f32 for
+//                     wider rows);
+//  6. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
+//  7. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
+// Split-K projections are finished by k_gemm_fixup (fixed-order sums of the pieces + epilogue).
 //
 // GEMM design (gfx950): the persistent MFMA core in gemm.h (global->LDS DMA, swizzled LDS, XCD-aware
-// tile walk) with fused epilogues, on 128x128 tiles (4 waves of 64x64, two workgroups per CU).
+// tile walk) with fused epilogues, on 128x128 tiles (4 waves of 64x64, two workgroups per CU); for a
+// row capacity of at most 64, a weight-streaming form (64-row tiles, one workgroup per CU).
 #include <math.h>
 
 #include <mutex>
