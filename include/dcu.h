@@ -322,9 +322,11 @@ int dcu_v_features(const dcu_layer* w, const void* x_in, int32_t B, int32_t N, v
  * the first kernel and events[i] after stage i on `stream`, for the DCU_LAYER_STAGES stages
  *   1 row offsets and map + gather + RMSNorm, 2 QKV projection + K/V scatter,
  *   3 its split-tail fixup, 4 attention (+ split combine), 5 output projection + residual,
- *   6 its fixup (empty for rows of up to 4096 values: the split tiles are then finished inside
- *   stage 7), 7 RMSNorm, 8 gate/up projection + SwiGLU, 9 its fixup,
- *   10 down projection + residual + scatter, 11 its fixup.
+ *   6 its fixup (empty when the split tiles are finished inside stage 7: rows of up to 4096
+ *   values, or of up to 8192 under a row bound of at most 64), 7 RMSNorm, 8 gate/up projection +
+ *   SwiGLU, 9 its fixup, 10 down projection + residual + scatter, 11 its fixup.
+ *   Under a row bound (max_rows) of at most 64 with rows of up to 8192 values (rotary head_dim up
+ *   to 128), stage 2 also does the work of stage 1, which is then empty, and stage 3 is empty.
  * (A fixup kernel finishes the tiles whose K range was split over idle workgroups; it exits at
  * once when the projection did not split.)
  * events may be NULL (then this is dcu_selective_layer); otherwise n_events must be at least
