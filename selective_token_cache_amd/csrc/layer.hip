@@ -426,10 +426,17 @@ __host__ __device__ inline SplitPlan plan_split(int T, int G, int KT, int mode =
     return p;
   }
   if (T < G) {
-    // every tile: pick S minimising rounds / S with at most 2 rounds of units
+    // every tile: the S in [2, min(16, KT / 8, 2G / T)] minimising rounds / S (at most 2 rounds
+    // of units), ties to the smaller S. rounds / S is 1 / S up to G / T and 2 / S above, so the
+    // minimum is at the largest one-round S or at the largest S: two candidates in ascending order
+    // (every workgroup of the GEMM and its fixup evaluates this at its start, so no loop)
+    int smax = KT / 8 < kMaxSplitK ? KT / 8 : kMaxSplitK;
+    smax = smax < 2 * G / T ? smax : 2 * G / T;
+    const int Sa = smax < G / T ? smax : G / T;
     float best = 1.0f;
-    for (int S = 2; S <= kMaxSplitK; ++S) {
-      if (KT / S < 8 || T * S > 2 * G) break;
+    for (int c = 0; c < 2; ++c) {
+      const int S = c == 0 ? Sa : smax;
+      if (S < 2 || (c == 1 && S == Sa)) continue;
       const float cost = float((T * S + G - 1) / G) / float(S);
       if (cost < best - 1e-6f) {
         best = cost;
@@ -1260,14 +1267,16 @@ constexpr int kAttnStages = DCU_ATTN_STAGES; // LDS stages of (K, V) blocks
 constexpr int kAttnWgs = DCU_ATTN_WGS;       // workgroups per CU the registers are budgeted for
 static_assert(kAttnKB == 32 || kAttnKB == 64, "key block");
 
-// Work plan of the attention grid (G persistent workgroups, two per CU) for the device-side
-// query-tile count. Items are (query tile, head) pairs. When there are fewer items than CUs
-// (items < G / 2, e.g. one sequence or few selected rows) every item is split along the keys into
-// S ranges so that the units fill the chip; otherwise every item runs whole. (Splitting only the
+// Work plan of the attention grid (G persistent workgroups, kAttnWgs per CU) for the device-side
+// query-tile count. Items are (query tile, head) pairs. When there are fewer items than half the
+// workgroups (e.g. one sequence or few selected rows) every item is split along the keys into S
+// ranges so that the units use the idle workgroups; otherwise every item runs whole. (Splitting only the
 // items of a partial last round was measured slower at batch 8: 65.6 vs 57.6 us per layer, since
 // the short units and the merge cost more than the half-empty round, whose workgroups run alone
 // on their CUs.) A split unit writes its unnormalised fp32 output and (max, sum) to a unit-indexed
 // slot; k_attn_combine merges an item's S units in split order. Split units: items * S < G + items.
+// (Closed-loop step, ~60 rows per sequence, 384 items: S = 2 in one round of units against S = 3
+// with a partial second round.)
 constexpr int kAttnMaxUnits = 2 * kAttnWgs * 256;  // 2 * (attention workgroups per CU * 256 CUs)
 
 struct AttnPlan {
@@ -1283,14 +1292,29 @@ __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
   AttnPlan p{items, 0, 1, whole};
   if (items <= 0) return p;
   if (2 * items >= G) return p;
-  const int rem = items;
-  int S = (G + items - 1) / items;
-  S = S < S_max ? S : S_max;
-  if (S <= 1) return p;
-  const int kps = ((N + S - 1) / S + kKB - 1) / kKB * kKB;
-  const int S_eff = (N + kps - 1) / kps;  // every range starts below N
-  if (S_eff <= 1) return p;
-  return AttnPlan{items - rem, rem, S_eff, kps};
+  // Two candidates for S (both <= S_max): floor(G / items), whose units fit one round, and
+  // ceil(G / items), which fills every workgroup but may need a partial second round (units
+  // < G + items). The one that gives the busiest workgroup the fewest 64-key steps, rounds x steps
+  // per unit, wins (ties to the smaller S: fewer partial rows to merge); a partial extra round of
+  // units costs a whole unit's time. (Closed form, int32: every workgroup evaluates it.)
+  int S_lo = G / items, S_hi = (G + items - 1) / items;
+  S_lo = S_lo < S_max ? S_lo : S_max;
+  S_hi = S_hi < S_max ? S_hi : S_max;
+  int best_S = 1, best_kps = whole, best_cost = whole / kKB;
+  for (int c = 0; c < 2; ++c) {
+    const int S = c == 0 ? S_lo : S_hi;
+    if (S <= 1 || (c == 1 && S == S_lo)) continue;
+    const int kps = ((N + S - 1) / S + kKB - 1) / kKB * kKB;
+    const int S_eff = (N + kps - 1) / kps;  // every range starts below N
+    const int cost = (items * S_eff + G - 1) / G * (kps / kKB);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_S = S_eff;
+      best_kps = kps;
+    }
+  }
+  if (best_S <= 1) return p;
+  return AttnPlan{0, items, best_S, best_kps};
 }
 
 // Chunk swizzle of a key row: 8 consecutive keys land on distinct 16-byte bank groups (the K
