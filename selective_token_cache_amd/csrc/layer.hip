@@ -1405,7 +1405,11 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
     const int kbeg = split * ap.kps;
     const int kend = w < ap.full ? g.N : min(g.N, kbeg + ap.kps);
     const int nblk = (kend - kbeg + KB - 1) / KB;
-    // this wave's 16 queries; lane column `col` is its query
+    // this wave's 16 queries; lane column `col` is its query. A wave whose 16 rows all lie past
+    // the sequence's last row (the ragged last tile) still issues its share of every block's DMA
+    // and takes part in the barriers, but skips the scores, softmax and products: its SIMD issue
+    // slots go to the co-resident workgroups
+    const bool wave_live = r0 + wid_s * 16 < rend;
     int qr = r0 + wid * 16 + col;
     const bool qvalid = qr < rend;
     qr = qvalid ? qr : rend - 1;
@@ -1453,6 +1457,7 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
 
     auto compute = [&](auto sidx, int j) {
       constexpr int S = decltype(sidx)::value;
+      if (!wave_live) return;
       const u32x4* kb = S == 0 ? k0 : (S == 1 ? k1 : k2);
       const uint16_t* vh = reinterpret_cast<const uint16_t*>(S == 0 ? v0 : (S == 1 ? v1 : v2));
       const int kb0 = kbeg + j * KB;
