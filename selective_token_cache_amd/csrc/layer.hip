@@ -484,10 +484,13 @@ static_assert(kGemmLdsChunks * 16 <= 80 * 1024, "two workgroups per CU");
 static_assert(CfgSkinny::BM * CfgSkinny::BN <= CfgSmall::BM * CfgSmall::BN, "partial tile slots");
 // the tile shape follows the device-side row count; kernel and fixup take the same decision
 __device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
-// Main loop per projection. Gate/up (~3.4 rounds of 512 tiles at ~1.1k rows) keeps two busy
-// workgroups per CU and runs the plain loop. QKV, output and down (1-1.7 rounds) run the
+// Main loop per projection. QKV, output and down (1-1.7 rounds of 512 tiles at ~1.1k rows) run the
 // early-refill loop, whose DMAs have two K-tiles of latency, with their tiles whole: measured at
 // batch 8, N = 1024, output 58.0 + 17.8 (split fixup) -> 60.4 + 6.8 us, down and QKV even.
+// Gate/up runs it too up to four rounds of tiles (the selective row counts), whole tiles with the
+// CU-paired tail: closed loop (~500 rows, 1.5 rounds) 108.1 + 11.5 (split fixup) -> 105.9 + 6.7 us,
+// ~1.1k and ~2.2k rows even; above four rounds (the dense M = B N) the plain two-stage loop, which
+// the early refill trails by 13% at M = 8192.
 template <int EPI, class C>
 constexpr bool early_refill() {
   return (EPI == EPI_QKV || EPI == EPI_QKV_ROPE || EPI == EPI_RESID || EPI == EPI_DOWN ||
@@ -495,9 +498,16 @@ constexpr bool early_refill() {
          std::is_same<C, CfgSmall>::value;
 }
 template <int EPI, class C>
+constexpr bool early_refill_few_rounds() {
+  return EPI == EPI_SWIGLU && std::is_same<C, CfgSmall>::value;
+}
+constexpr int kEarlyRefillMaxRounds = 4;
+template <int EPI, class C>
 constexpr int split_mode() {
-  return (std::is_same<C, CfgSkinny>::value || std::is_same<C, CfgStream>::value) ? kSplitStreaming
-                                           : (early_refill<EPI, C>() ? kSplitFewTiles : kSplitTail);
+  return (std::is_same<C, CfgSkinny>::value || std::is_same<C, CfgStream>::value)
+             ? kSplitStreaming
+             : (early_refill<EPI, C>() || early_refill_few_rounds<EPI, C>() ? kSplitFewTiles
+                                                                            : kSplitTail);
 }
 
 template <int EPI, class C>
@@ -670,10 +680,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
     }
     const int m_t = tile % MT, n_t = tile / MT;  // consecutive tiles share the weight tile
     gemm::f32x4 acc[C::FM][C::FN];
-    if constexpr (early_refill<EPI, C>())
+    if constexpr (early_refill<EPI, C>()) {
       gemm::tile_mainloop_er<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, kt0, kt1);
-    else
+    } else if constexpr (early_refill_few_rounds<EPI, C>()) {
+      if (MT * NT <= kEarlyRefillMaxRounds * int(gridDim.x))
+        gemm::tile_mainloop_er<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, kt0, kt1);
+      else
+        gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
+    } else {
       gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
+    }
     if (lin < sp.full) {
       gemm_epilogue<EPI, C>(g, acc, M, m_t * C::BM, n_t);
     } else {
