@@ -487,10 +487,12 @@ __device__ inline bool use_skinny(int M) { return M <= CfgSkinny::BM; }
 // Main loop per projection. QKV, output and down (1-1.7 rounds of 512 tiles at ~1.1k rows) run the
 // early-refill loop, whose DMAs have two K-tiles of latency, with their tiles whole: measured at
 // batch 8, N = 1024, output 58.0 + 17.8 (split fixup) -> 60.4 + 6.8 us, down and QKV even.
-// Gate/up runs it too up to four rounds of tiles (the selective row counts), whole tiles with the
-// CU-paired tail: closed loop (~500 rows, 1.5 rounds) 108.1 + 11.5 (split fixup) -> 105.9 + 6.7 us,
-// ~1.1k and ~2.2k rows even; above four rounds (the dense M = B N) the plain two-stage loop, which
-// the early refill trails by 13% at M = 8192.
+// Gate/up runs it too up to two rounds of tiles, whole tiles with the CU-paired tail: closed loop
+// (~500 rows, 1.5 rounds) 108.1 + 11.5 (split fixup) -> 105.9 + 6.7 us. At ~1.1k rows (3.4 rounds)
+// it was even in time but fetched 754 instead of 584 MB per launch from beyond the L2 (the
+// workgroups of an XCD drift further apart with two K-tiles in flight and share fewer activation
+// and weight lines), and at M = 8192 it trails the two-stage loop by 13%; above two rounds gate/up
+// keeps the two-stage loop and the tail split.
 template <int EPI, class C>
 constexpr bool early_refill() {
   return (EPI == EPI_QKV || EPI == EPI_QKV_ROPE || EPI == EPI_RESID || EPI == EPI_DOWN ||
@@ -501,13 +503,21 @@ template <int EPI, class C>
 constexpr bool early_refill_few_rounds() {
   return EPI == EPI_SWIGLU && std::is_same<C, CfgSmall>::value;
 }
-constexpr int kEarlyRefillMaxRounds = 4;
+constexpr int kEarlyRefillMaxRounds = 2;
 template <int EPI, class C>
 constexpr int split_mode() {
-  return (std::is_same<C, CfgSkinny>::value || std::is_same<C, CfgStream>::value)
-             ? kSplitStreaming
-             : (early_refill<EPI, C>() || early_refill_few_rounds<EPI, C>() ? kSplitFewTiles
-                                                                            : kSplitTail);
+  return (std::is_same<C, CfgSkinny>::value || std::is_same<C, CfgStream>::value) ? kSplitStreaming
+                                           : (early_refill<EPI, C>() ? kSplitFewTiles : kSplitTail);
+}
+// Gate/up: the early-refill loop (whole tiles, CU-paired tail) for T tiles on G workgroups up to
+// two rounds, the two-stage loop with the tail split above. The GEMM and its fixup both decide here.
+template <int EPI, class C>
+__host__ __device__ constexpr bool gate_up_early_refill(int T, int G) {
+  return early_refill_few_rounds<EPI, C>() && T <= kEarlyRefillMaxRounds * G;
+}
+template <int EPI, class C>
+__host__ __device__ constexpr int split_mode_for(int T, int G) {
+  return gate_up_early_refill<EPI, C>(T, G) ? kSplitFewTiles : split_mode<EPI, C>();
 }
 
 template <int EPI, class C>
@@ -646,7 +656,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = wr.template tiles<C::BN>();
   const int KT = g.K / C::BK;
-  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, split_mode<EPI, C>());
+  const SplitPlan sp = plan_split(MT * NT, gridDim.x, KT, split_mode_for<EPI, C>(MT * NT, gridDim.x));
   const int units = sp.full + sp.rem * sp.S;
   int lin, zero;
   for (int round = 0;; ++round) {
@@ -683,7 +693,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int M, u32x4* smem)
     if constexpr (early_refill<EPI, C>()) {
       gemm::tile_mainloop_er<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, kt0, kt1);
     } else if constexpr (early_refill_few_rounds<EPI, C>()) {
-      if (MT * NT <= kEarlyRefillMaxRounds * int(gridDim.x))
+      if (gate_up_early_refill<EPI, C>(MT * NT, gridDim.x))
         gemm::tile_mainloop_er<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, kt0, kt1);
       else
         gemm::tile_mainloop<C>(acc, g.A, M, g.K, m_t * C::BM, n_t, wr, b0, b1, b2, b3, kt0, kt1);
@@ -978,7 +988,7 @@ template <int EPI, class C>
 __device__ __forceinline__ void fixup_body(const GemmArgs& g, int M, int slots) {
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = EPI == EPI_SWIGLU ? g.Nout / (C::BN / 2) : (g.Nout + C::BN - 1) / C::BN;
-  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode<EPI, C>());
+  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode_for<EPI, C>(MT * NT, slots));
   if (sp.rem == 0) return;
   // SwiGLU: an item is an output column group from its gate and up columns; rotary QKV: an item is
   // a column group of a 32-column group's first half together with its partner 16 columns on
