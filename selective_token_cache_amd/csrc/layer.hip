@@ -864,29 +864,23 @@ __global__ __launch_bounds__(256, 1) void k_qkv_fused(GemmArgs g, Ptrs P,
 // (k_gemm_fixup's order); the pieces of all the thread's groups are loaded in rounds of four, the
 // first round together with the residual and the gains. The sum of squares is reduced over the
 // workgroup in a fixed order. With rows_done, also the per-sequence count of recomputed rows.
-template <int PER>
-__global__ __launch_bounds__(256) void k_resid_rmsnorm_row(GemmArgs g,
-                                                           const uint16_t* __restrict__ gain,
-                                                           float eps, uint16_t* __restrict__ out,
-                                                           int32_t* __restrict__ rows_done, int B,
-                                                           const int* __restrict__ seq_off) {
-  using C = StreamCfg<EPI_RESID>;
-  const int M = g.hdr[kHdrM];
-  if (rows_done && blockIdx.x == 0) {
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-      int n = 0;
-      for (int r = seq_off[b]; r < seq_off[b + 1]; ++r) n += g.rowmap[r] >= 0 ? 1 : 0;
-      rows_done[b] = n;
-    }
-  }
-  if (M <= 0) return;
-  const int d = g.d, groups = d / 8;
+// the output projection's split plan for M rows on `slots` workgroups (as k_gemm made it)
+template <class C>
+__device__ __forceinline__ SplitPlan oproj_plan(const GemmArgs& g, int M, int slots) {
   const int MT = (M + C::BM - 1) / C::BM;
   const int NT = (g.Nout + C::BN - 1) / C::BN;
-  const SplitPlan sp = plan_split(MT * NT, kStreamSlots, g.K / C::BK, split_mode<EPI_RESID, C>());
+  return plan_split(MT * NT, slots, g.K / C::BK, split_mode_for<EPI_RESID, C>(MT * NT, slots));
+}
+
+template <int PER, class C>
+__device__ __forceinline__ void resid_rmsnorm_row_body(const GemmArgs& g, int M,
+                                                       const SplitPlan& sp,
+                                                       const uint16_t* __restrict__ gain, float eps,
+                                                       uint16_t* __restrict__ out, float* red) {
+  const int d = g.d, groups = d / 8;
+  const int MT = (M + C::BM - 1) / C::BM;
   constexpr int kTile = C::BM * C::BN;
   constexpr int kRound = 4;
-  __shared__ float red[4];
   const int t = threadIdx.x, wid = t / kWave;
   for (int r = blockIdx.x; r < M; r += gridDim.x) {
     const int m_t = r / C::BM, rl = r - m_t * C::BM;
@@ -975,6 +969,36 @@ __global__ __launch_bounds__(256) void k_resid_rmsnorm_row(GemmArgs g,
       reinterpret_cast<uint4*>(orow)[gi] = o;
     }
     __syncthreads();  // red is reused by the next row
+  }
+}
+
+// slots: the output projection's grid (kStreamSlots for the weight-streaming kernel, else the
+// persistent grid, whose tile shape follows the device row count as in k_gemm)
+template <int PER>
+__global__ __launch_bounds__(256) void k_resid_rmsnorm_row(GemmArgs g, int slots,
+                                                           const uint16_t* __restrict__ gain,
+                                                           float eps, uint16_t* __restrict__ out,
+                                                           int32_t* __restrict__ rows_done, int B,
+                                                           const int* __restrict__ seq_off) {
+  __shared__ float red[4];
+  const int M = g.hdr[kHdrM];
+  if (rows_done && blockIdx.x == 0) {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      int n = 0;
+      for (int r = seq_off[b]; r < seq_off[b + 1]; ++r) n += g.rowmap[r] >= 0 ? 1 : 0;
+      rows_done[b] = n;
+    }
+  }
+  if (M <= 0) return;
+  if (slots == kStreamSlots) {
+    using C = StreamCfg<EPI_RESID>;
+    resid_rmsnorm_row_body<PER, C>(g, M, oproj_plan<C>(g, M, slots), gain, eps, out, red);
+  } else if (use_skinny(M)) {
+    resid_rmsnorm_row_body<PER, CfgSkinny>(g, M, oproj_plan<CfgSkinny>(g, M, slots), gain, eps,
+                                           out, red);
+  } else {
+    resid_rmsnorm_row_body<PER, CfgSmall>(g, M, oproj_plan<CfgSmall>(g, M, slots), gain, eps, out,
+                                          red);
   }
 }
 
@@ -1126,13 +1150,11 @@ __global__ __launch_bounds__(256) void k_gemm_fixup(GemmArgs g, int slots) {
 // residual), then normalises the row held in registers -> an (bf16). This replaces the output
 // projection's fixup launch. With rows_done, also the per-sequence count of recomputed rows.
 template <int NC, class C>
-__device__ __forceinline__ void resid_rms_rows(const GemmArgs& g, int M, int slots,
+__device__ __forceinline__ void resid_rms_rows(const GemmArgs& g, int M, const SplitPlan& sp,
                                                const uint16_t* __restrict__ gain, float eps,
                                                uint16_t* __restrict__ out) {
   const int d = g.d, groups = d / 8;
   const int MT = (M + C::BM - 1) / C::BM;
-  const int NT = (g.Nout + C::BN - 1) / C::BN;
-  const SplitPlan sp = plan_split(MT * NT, slots, g.K / C::BK, split_mode<EPI_RESID, C>());
   const int lane = threadIdx.x & (kWave - 1);
   constexpr int kTile = C::BM * C::BN;
   for (int r = blockIdx.x * 4 + threadIdx.x / kWave; r < M; r += gridDim.x * 4) {
@@ -1244,10 +1266,26 @@ __global__ __launch_bounds__(256) void k_resid_rmsnorm(GemmArgs g, int slots,
     }
   }
   if (M <= 0) return;
-  if (use_skinny(M))
-    resid_rms_rows<NC, CfgSkinny>(g, M, slots, gain, eps, out);
-  else
-    resid_rms_rows<NC, CfgSmall>(g, M, slots, gain, eps, out);
+  // When the output projection split every tile (fewer tiles than workgroup slots: each group of a
+  // row is a sum of pieces), a workgroup per row (grid-stride over the rows) keeps four times more
+  // pieces in flight than a wave per row: closed-loop step (~500 rows, 4 pieces) 21.6 -> 15.9 us
+  // per layer. With whole tiles (a plain read of a) the wave per row stays faster (~1.1k rows:
+  // 15.1 against 17.7 us; ~2.2k rows: 16.5 against 25.1).
+  constexpr int PER = NC >= 4 ? NC / 4 : 1;
+  __shared__ float red[4];
+  if (use_skinny(M)) {
+    const SplitPlan sp = oproj_plan<CfgSkinny>(g, M, slots);
+    if (sp.full == 0 && sp.rem > 0)
+      resid_rmsnorm_row_body<PER, CfgSkinny>(g, M, sp, gain, eps, out, red);
+    else
+      resid_rms_rows<NC, CfgSkinny>(g, M, sp, gain, eps, out);
+  } else {
+    const SplitPlan sp = oproj_plan<CfgSmall>(g, M, slots);
+    if (sp.full == 0 && sp.rem > 0)
+      resid_rmsnorm_row_body<PER, CfgSmall>(g, M, sp, gain, eps, out, red);
+    else
+      resid_rms_rows<NC, CfgSmall>(g, M, sp, gain, eps, out);
+  }
 }
 
 // ------------------------------------------------------------------------------ 4. attention
@@ -2050,8 +2088,9 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   if (!mark()) return DCU_EHIP;
   if (row_rms) {
 #define DCU_ROW_RMS(PER)                                                                      \
-  hipLaunchKernelGGL(k_resid_rmsnorm_row<PER>, dim3(unsigned(L.M_cap)), dim3(256), 0, s, ga, gf_, \
-                     w->rms_eps, P.xn, rows_done, int(B), P.seq_off)
+  hipLaunchKernelGGL(k_resid_rmsnorm_row<PER>, dim3(unsigned(L.M_cap)), dim3(256), 0, s, ga,      \
+                     L.M_cap <= CfgStream::BM ? kStreamSlots : o_slots, gf_, w->rms_eps, P.xn,   \
+                     rows_done, int(B), P.seq_off)
     switch (row_per) {
       case 1: DCU_ROW_RMS(1); break;
       case 2: DCU_ROW_RMS(2); break;
