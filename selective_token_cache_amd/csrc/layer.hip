@@ -2054,7 +2054,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.N = N;
   aa.H = H;
   aa.d = d;
-  aa.S_max = attn_s_max(N);  // key ranges of >= 128 keys
+  aa.S_max = attn_s_max(N);  // at most 16 key ranges of >= 64 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   st = launch_attention(aa, DH, s);
   if (st != DCU_OK) return st;
