@@ -20,15 +20,16 @@
 //                     when there are too few tiles to fill the chip) + k_attn_combine;
 //  4. k_gemm<RESID>   o W_o^T plus the residual gathered from x -> a (fp32);
 //  5. k_resid_rmsnorm the split tiles of a finished (fixed-order sums of the pieces + residual)
-//                     and RMSNorm of a -> an (bf16) in one pass (k_resid_rmsnorm_row, a workgroup
-//                     per row, for a row capacity of at most 64; k_gemm_fixup + k_rmsnorm_f32 for
-//                     wider rows);
+//                     and RMSNorm of a -> an (bf16) in one pass, a wave per row, or a workgroup per
+//                     row when every tile was split (k_resid_rmsnorm_row, the same body, for a row
+//                     capacity of at most 64; k_gemm_fixup + k_rmsnorm_f32 for wider rows);
 //  6. k_gemm<SWIGLU>  gate and up tiles computed together; epilogue silu(g)*u -> h (bf16);
 //  7. k_gemm<DOWN>    h W_down^T plus a; epilogue scatters y back into y_out.
 // Split-K projections are finished by k_gemm_fixup (fixed-order sums of the pieces + epilogue).
 //
 // GEMM design (gfx950): the persistent MFMA core in gemm.h (global->LDS DMA, swizzled LDS, XCD-aware
-// tile walk) with fused epilogues, on 128x128 tiles (4 waves of 64x64, two workgroups per CU); for a
+// tile walk) with fused epilogues, on 128x128 tiles (4 waves of 64x64, two workgroups per CU; the
+// early-refill loop for QKV, output and down, and for gate/up up to two rounds of tiles); for a
 // row capacity of at most 64, a weight-streaming form (64-row tiles, one workgroup per CU).
 #include <math.h>
 
