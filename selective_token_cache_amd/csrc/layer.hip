@@ -1350,7 +1350,10 @@ struct AttnPlan {
 
 // Most key ranges an item is split into: ranges of at least 64 keys (two 32-key blocks, so a
 // unit's blocks are nearly all in flight at once), at most 16
-inline int attn_s_max(int N) { return N / kKB > 1 ? (N / kKB < 16 ? N / kKB : 16) : 1; }
+constexpr int kAttnMaxSplit = 16;  // key ranges per item at most
+inline int attn_s_max(int N) {
+  return N / kKB > 1 ? (N / kKB < kAttnMaxSplit ? N / kKB : kAttnMaxSplit) : 1;
+}
 
 __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
   const int whole = (N + kKB - 1) / kKB * kKB;
@@ -1664,58 +1667,53 @@ __global__ __launch_bounds__(256, kAttnWgs) void k_attn(AttnArgs g) {
   }
 }
 
-// merge the S units of every split item, one wave per (item, query row), in split order; exits at
-// once when the plan split nothing. Every (max, sum) pair and partial row of the item is loaded
-// before the merge (lane s holds unit s's pair; the partial rows are read in groups of 4 units).
+// merge the S (<= kAttnMaxSplit) units of every split item, one wave per (item, query row), in
+// split order; exits at once when the plan split nothing. The (max, sum) pairs (lane s holds unit
+// s's) and all S partial rows are loaded together, before the row's sequence lookup, which only
+// gates the store: their slots follow from the unit index alone (a row past its sequence's end
+// has slots that were never written; they are loaded and merged but not stored).
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs g, int DH, int attn_grid) {
   const AttnPlan ap = attn_plan(g.hdr[kHdrTq] * g.H, attn_grid, g.N, g.S_max);
   if (ap.rem == 0) return;
   const int lane = threadIdx.x & 63;
+  const int S = ap.S;
   const int64_t pairs = int64_t(ap.rem) * kQTile;
   for (int64_t p = int64_t(blockIdx.x) * 4 + threadIdx.x / 64; p < pairs;
        p += int64_t(gridDim.x) * 4) {
     const int k = int(p / kQTile), j = int(p % kQTile);
     const int item = ap.full + k;
     const int h = item % g.H, tile = item / g.H;
-    const int b = g.tile_seq[tile];
-    const int r = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile + j;
-    if (r >= g.seq_off[b + 1]) continue;
-    const int64_t slot0 = int64_t(k) * ap.S * kQTile + j;  // unit s of this row: slot0 + s * kQTile
-    // every (max, sum) pair (lane s holds unit s's) and the first four partial rows are loaded
-    // together: the weights need the maximum first, but the loads do not
+    const int64_t slot0 = int64_t(k) * S * kQTile + j;  // unit s of this row: slot0 + s * kQTile
     float m_s = -INFINITY, l_s = 0.0f;
-    if (lane < ap.S) {
+    if (lane < S) {
       const float2 v = *reinterpret_cast<const float2*>(g.ml + (slot0 + int64_t(lane) * kQTile) * 2);
       m_s = v.x;
       l_s = v.y;
     }
-    float o0[4], o1[4];
-    auto load_rows = [&](int s0) {
+    float o0[kAttnMaxSplit], o1[kAttnMaxSplit];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s2 = s0 + u < ap.S ? s0 + u : s0;
-        const float* op = g.opart + (slot0 + int64_t(s2) * kQTile) * DH;
-        o0[u] = lane < DH ? op[lane] : 0.0f;
-        o1[u] = lane + 64 < DH ? op[lane + 64] : 0.0f;
-      }
-    };
-    load_rows(0);
-    const float mx = wave_max(m_s);
-    float l = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
-    for (int s0 = 0; s0 < ap.S; s0 += 4) {
-      if (s0 > 0) load_rows(s0);
-      float f[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) f[u] = __shfl(m_s, s0 + u < ap.S ? s0 + u : s0, kWave);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (s0 + u >= ap.S) break;
-        const float w = __builtin_amdgcn_exp2f(f[u] - mx);
-        l += __shfl(l_s, s0 + u, kWave) * w;
-        acc0 += o0[u] * w;
-        acc1 += o1[u] * w;
+    for (int u = 0; u < kAttnMaxSplit; ++u) {
+      o0[u] = o1[u] = 0.0f;
+      if (u < S) {
+        const float* op = g.opart + (slot0 + int64_t(u) * kQTile) * DH;
+        if (lane < DH) o0[u] = op[lane];
+        if (lane + 64 < DH) o1[u] = op[lane + 64];
       }
     }
+    const int b = g.tile_seq[tile];
+    const int r = g.seq_off[b] + (tile - g.tile_off[b]) * kQTile + j;
+    const int rend = g.seq_off[b + 1];
+    const float mx = wave_max(m_s);
+    float l = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kAttnMaxSplit; ++u) {
+      if (u >= S) break;
+      const float w = __builtin_amdgcn_exp2f(__shfl(m_s, u, kWave) - mx);
+      l += __shfl(l_s, u, kWave) * w;
+      acc0 += o0[u] * w;
+      acc1 += o1[u] * w;
+    }
+    if (r >= rend) continue;
     const float inv = 1.0f / l;
     uint16_t* dst = g.o + int64_t(r) * g.d + h * DH;
     if (lane < DH) dst[lane] = uint16_t(f_to_bf_bits(acc0 * inv));
