@@ -29,9 +29,10 @@
  *    to 16 bytes, unless stated otherwise. bf16 tensors are raw 16-bit patterns.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work and return;
  *    outputs are valid once the stream reaches that point; inputs must stay alive until then.
- *  - The library never allocates device memory, keeps no pointer past a call and has no mutable
- *    global state: calls are reentrant and thread-safe. Outputs must not alias inputs except for
- *    the documented in/out buffers.
+ *  - The library never allocates device memory and keeps no pointer past a call. Its one piece of
+ *    mutable global state is the scratch of dcu_selective_layer_noalloc (a device array per GPU,
+ *    see there); every other call is reentrant and thread-safe. Outputs must not alias inputs
+ *    except for the documented in/out buffers.
  *  - All argument checks happen on the host before any launch: a non-zero status means nothing
  *    was enqueued, except DCU_EHIP, which reports a failed launch.
  *  - NaN or Inf inputs are a caller error; the results are then unspecified.
