@@ -1350,9 +1350,14 @@ struct AttnPlan {
 
 // Most key ranges an item is split into: ranges of at least 64 keys (two 32-key blocks, so a
 // unit's blocks are nearly all in flight at once), at most 16
-constexpr int kAttnMaxSplit = 16;  // key ranges per item at most
+constexpr int kAttnMaxSplit = 16;    // key ranges per item at most
+constexpr int kAttnMinRange = 128;   // keys per range at least
+// Ranges shorter than 128 keys cost more in the merge (one partial row per range) than they save:
+// batch 1, N = 1024 (32 items), attention + merge 19.5 us with 16 ranges of 64 keys, 16.3-16.7 with
+// 8 of 128, 17.4 with 4 of 256.
 inline int attn_s_max(int N) {
-  return N / kKB > 1 ? (N / kKB < kAttnMaxSplit ? N / kKB : kAttnMaxSplit) : 1;
+  const int r = N / kAttnMinRange;
+  return r > 1 ? (r < kAttnMaxSplit ? r : kAttnMaxSplit) : 1;
 }
 
 __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
@@ -2053,7 +2058,7 @@ extern "C" int dcu_selective_layer_staged(const dcu_layer* w, const void* x_in,
   aa.N = N;
   aa.H = H;
   aa.d = d;
-  aa.S_max = attn_s_max(N);  // at most 16 key ranges of >= 64 keys
+  aa.S_max = attn_s_max(N);  // at most 16 key ranges of >= 128 keys
   aa.scale_log2 = float(1.4426950408889634 / sqrt(double(DH)));
   st = launch_attention(aa, DH, s);
   if (st != DCU_OK) return st;
