@@ -136,6 +136,10 @@ def _random_selection(g, B, N, counts):
     (synth.LayerShape(d=128, n_heads=4, head_dim=32, ffn=192), 4, 77, [77, 5, 33, 64]),
     # K long enough for the split-K path of the output (K = 1024) and down (K = 2048) projections
     (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=2048), 2, 256, [100, 37]),
+    # 700 rows: gate/up has 6 x 64 = 384 tiles for 512 workgroups (at most two rounds), so it runs
+    # the early-refill loop with the CU-paired tail (128 tiles cut in 2 K-segments, fixup); the
+    # output projection's 48 tiles are all split, so the RMSNorm finishes them a workgroup per row
+    (synth.LayerShape(d=1024, n_heads=8, head_dim=128, ffn=4096), 2, 512, [400, 300]),
 ])
 def test_selective_layer_small_shapes(shape, B, N, counts):
     _log(f"layer d={shape.d} H={shape.n_heads} dh={shape.head_dim} F={shape.ffn} B={B} N={N}")
