@@ -292,6 +292,47 @@ def summarize_profiles(ktrace_dir, fetch_dir, write_dir, mfma_dir, bench_json, s
     print(out2)
 
 
+def summarize_counters(pmc_dir, cmd, out_name, title, notes):
+    """Per-kernel averages of every counter or derived metric of one rocprofv3 --pmc run (all
+    launches of each library kernel the run collected), as a table with the command that made it."""
+    import collections
+    import csv
+    import glob
+    import re
+
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(pmc_dir, "*_counter_collection.csv"))[0])))
+    agg = collections.OrderedDict()
+    launches = collections.defaultdict(set)
+    for r in rows:
+        if "dcu::" not in r["Kernel_Name"]:
+            continue
+        m = re.search(r"dcu::(?:\(anonymous namespace\)::)?(\w+(?:<[^>]*>)?)", r["Kernel_Name"])
+        k = m.group(1) if m else r["Kernel_Name"]
+        agg.setdefault(k, collections.OrderedDict()).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+        launches[k].add(r["Dispatch_Id"])
+    names = []
+    for d in agg.values():
+        for c in d:
+            if c not in names:
+                names.append(c)
+    out = [f"# {title}", "", "Command (run from the repository root):", "", "    " + cmd, "",
+           "Average over every launch of each kernel in the run.", ""]
+    out += notes + [""] if notes else []
+    out.append("| kernel | launches | " + " | ".join(names) + " |")
+    out.append("|---|---|" + "---|" * len(names))
+    for k, d in agg.items():
+        cells = []
+        for c in names:
+            v = d.get(c)
+            cells.append("-" if not v else f"{sum(v) / len(v):.4g}")
+        out.append(f"| `{k}` | {len(launches[k])} | " + " | ".join(cells) + " |")
+    path = os.path.join(ROOT, "profiles", out_name)
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+
+
 def summarize_trace(ktrace_dir, bench_json, steps, cmd, out_name, title):
     """Kernel-trace summary of one workload (durations only). Every step starts with the budget
     kernel, so the timed region runs from the start of the last `steps` budget launches to the end
@@ -382,6 +423,11 @@ def main():
         # ktrace_dir bench_json steps cmd out_name title
         a = sys.argv[2:]
         summarize_trace(a[0], a[1], int(a[2]), a[3], a[4], a[5])
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # pmc_dir cmd out_name title [note lines...]
+        a = sys.argv[2:]
+        summarize_counters(a[0], a[1], a[2], a[3], a[4:])
         return
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-profiles":
         # ktrace_dir fetch_dir write_dir mfma_dir bench_json steps cmd_trace cmd_fetch cmd_write cmd_mfma
