@@ -1391,11 +1391,16 @@ __device__ inline AttnPlan attn_plan(int items, int G, int N, int S_max) {
 }
 
 // Chunk swizzle of a key row: 8 consecutive keys land on distinct 16-byte bank groups (the K
-// fragment reads), and keys 4G..4G+3 x two adjacent chunks land on distinct 8-byte bank pairs
-// (the transposing V reads).
+// fragment reads), and the 8 keys x two adjacent chunks that 32 lanes of a transposing V read
+// address land on distinct 8-byte bank pairs: with 16 chunks per row (head_dim 128), keys 0..7
+// of a group XOR their chunk index with 0, 2, .., 14, so each key's chunk pair is its own
+// (rocprofv3 LdsBankConflict 1.0 -> 0 conflict cycles per access cycle for the attention kernel
+// against 0, 2, 4, 6, 1, 3, 5, 7, which gave keys k and k + 4 the same pair). Narrower rows keep
+// the 8-key spread of the K reads.
 template <int CH>
 __device__ __forceinline__ int kvsw(int key) {
-  return ((((key & 3) << 1) | ((key >> 2) & 1))) & (CH - 1);
+  return CH >= 16 ? (((key & 3) << 1) | (((key >> 2) & 1) << 3))
+                  : ((((key & 3) << 1) | ((key >> 2) & 1))) & (CH - 1);
 }
 template <int CH>
 __device__ __forceinline__ int kswz(int key, int c) { return key * CH + (c ^ kvsw<CH>(key)); }
