@@ -319,13 +319,23 @@ def summarize_counters(pmc_dir, cmd, out_name, title, notes):
     out = [f"# {title}", "", "Command (run from the repository root):", "", "    " + cmd, "",
            "Average over every launch of each kernel in the run.", ""]
     out += notes + [""] if notes else []
-    out.append("| kernel | launches | " + " | ".join(names) + " |")
-    out.append("|---|---|" + "---|" * len(names))
+    # with SQ_WAVE_CYCLES in the run, the other SQ wave-cycle counters (same quad-cycle units) are
+    # shown as fractions of it
+    frac = "SQ_WAVE_CYCLES" in names
+    shown = [c for c in names if not (frac and c == "SQ_WAVE_CYCLES")]
+    heads = [f"{c} / SQ_WAVE_CYCLES" if frac and c.startswith("SQ_") else c for c in shown]
+    out.append("| kernel | launches | " + " | ".join(heads) + " |")
+    out.append("|---|---|" + "---|" * len(heads))
     for k, d in agg.items():
         cells = []
-        for c in names:
+        for c in shown:
             v = d.get(c)
-            cells.append("-" if not v else f"{sum(v) / len(v):.4g}")
+            if not v:
+                cells.append("-")
+            elif frac and c.startswith("SQ_"):
+                cells.append(f"{sum(v) / max(sum(d['SQ_WAVE_CYCLES']), 1.0):.2f}")
+            else:
+                cells.append(f"{sum(v) / len(v):.4g}")
         out.append(f"| `{k}` | {len(launches[k])} | " + " | ".join(cells) + " |")
     path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w") as f:
